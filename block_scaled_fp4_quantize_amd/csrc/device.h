@@ -1,0 +1,97 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 conversion, block-scale
+// decode and the round-to-nearest-even e2m1 / e4m3 encoders.
+//
+// Formats: "vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A Complete Technical
+// Guide", §6.1 (NVFP4: e2m1 elements with max 6.0, e4m3 scale per 16 along K) and
+// §6.4 (MXFP4: 32-element blocks, exponent-only e8m0 scale).  E4M3 is the OCP
+// e4m3fn variant (bias 7, max 448) that gfx950 also uses natively.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Magnitude code (0..7) of the e2m1 value nearest to y >= 0, ties to the even code,
+// values above 6 saturating to code 7.  The thresholds are the midpoints between
+// neighbouring e2m1 values {0, .5, 1, 1.5, 2, 3, 4, 6}; a midpoint goes to the
+// neighbour whose mantissa bit is 0 (strict '>' where that is the lower one,
+// '>=' where it is the upper one).
+__device__ __forceinline__ uint32_t e2m1_mag_code(float y) {
+  return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
+         (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
+         (uint32_t)(y > 5.0f);
+}
+
+// e4m3fn code of sf >= 0 (finite or +inf): round to nearest even, saturating at 448
+// (code 0x7E).  Normal range: keep 3 mantissa bits of the fp32 pattern with
+// round-half-even at bit 20 and rebias the exponent (127 -> 7).  Below 2^-6 the
+// grid is m * 2^-9: scale exactly by 2^9 and round half-even to an integer (8 is
+// the smallest normal, code 0x08, so the carry works out).
+__device__ __forceinline__ uint32_t e4m3_code_pos(float sf) {
+  if (!(sf < 448.0f)) return 0x7Eu;
+  if (sf < 0.015625f) return (uint32_t)__builtin_rintf(sf * 512.0f);
+  uint32_t u = __float_as_uint(sf);
+  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  uint32_t code = (r >> 20) - (120u << 3);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Value of a non-negative e4m3fn code (0..0x7E).
+__device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Value 2^(c-127) of an e8m0 code (c = 0 gives the fp32 subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t c) {
+  return c == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((c & 0xFFu) << 23);
+}
+
+// Two e2m1 codes in byte `sel` of `packed` -> two bf16 values times `scale` (low
+// nibble first).  gfx950's scaled conversion multiplies in fp32; every product of
+// an e2m1 value and an e4m3 or e8m0 scale fits bf16 exactly.
+template <int SEL>
+__device__ __forceinline__ bf16x2 fp4x2_to_bf16(uint32_t packed, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, SEL);
+}
+
+// 8 e2m1 codes (one dword) -> bf16x8 operand, elements in k order.
+__device__ __forceinline__ bf16x8 decode8(uint32_t packed, float scale) {
+  bf16x2 p0 = fp4x2_to_bf16<0>(packed, scale);
+  bf16x2 p1 = fp4x2_to_bf16<1>(packed, scale);
+  bf16x2 p2 = fp4x2_to_bf16<2>(packed, scale);
+  bf16x2 p3 = fp4x2_to_bf16<3>(packed, scale);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 bits_to_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+}  // namespace fp4

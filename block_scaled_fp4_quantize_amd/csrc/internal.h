@@ -1,0 +1,109 @@
+// Internal launcher interface between the C-ABI layer (api.cpp) and the kernels.
+// Not installed; the public interface is include/fp4.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+enum Fmt : int { kNV = 0, kMX = 1 };
+
+// ---- activation / weight quantization --------------------------------------------
+struct QuantParams {
+  const void* x;            // bf16 bits or fp32, [rows of the source, ldx]
+  int in_f32;               // 0: bf16 input, 1: fp32 input
+  int64_t M, K, ldx;
+  float g;                  // NVFP4 quantize multiplier 1/input_scale (scalar)
+  const int32_t* row_src;   // optional: source row of output row r
+  const int32_t* row_grp;   // optional: group of output row r, selects grp_g
+  const float* grp_g;       // per-group multiplier (device)
+  uint8_t* codes;           // [M, K/2]
+  uint8_t* scales;          // [M, K/G]
+};
+hipError_t launch_quant(int fmt, const QuantParams& p, hipStream_t s, const char** name);
+
+// ---- block-scaled matmul ----------------------------------------------------------
+struct GemmParams {
+  int64_t M, N, K;
+  // activations: fp4 codes/scales, or bf16 bits with row stride lda
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint16_t* a_bf16;
+  int64_t lda;
+  const int32_t* a_gather;  // optional: source row of virtual row p
+  // weights, one [N, K] matrix per group at these strides
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  int64_t w_estride_codes, w_estride_scales;
+  // grouping: dense when mblk_expert == nullptr
+  const int32_t* mblk_expert;     // [n_mblocks] group of each row block (-1 = none)
+  const int32_t* mblk_row0;       // [n_mblocks] first virtual row of each row block
+  const int32_t* group_end;       // [groups]: one past the last virtual row of each group
+  int64_t n_mblocks;
+  int bm;                          // rows per row block the table was built for
+  const float* alpha_g;           // optional per-group alpha (device)
+  float alpha;
+  void* out;
+  int64_t ldo;
+  int out_f32;
+};
+enum AKind : int { kA_FP4 = 0, kA_BF16 = 1 };
+// Row-block height the launcher will use for a problem of this shape.
+int gemm_block_rows(int fmt, int akind, int64_t M_hint);
+hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
+                       const char** name);
+
+// ---- MoE stages ------------------------------------------------------------------
+hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,
+                               int renormalize, int32_t* ids, float* w, hipStream_t s,
+                               const char** name);
+
+struct PermuteParams {
+  const int32_t* ids;      // [T*k]
+  int64_t T;
+  int k;
+  int64_t E;
+  int bm;                  // row-block height for the block table
+  int64_t n_mblocks;       // capacity of the block table
+  int32_t* expert_offsets; // [E+1]
+  int32_t* sorted_rows;    // [T*k]
+  int32_t* inverse;        // [T*k]
+  int32_t* row_expert;     // [T*k]
+  int32_t* src_token;      // [T*k]
+  int32_t* mblk_expert;    // [n_mblocks]
+  int32_t* mblk_row0;      // [n_mblocks]
+  int32_t* group_end;      // [E]
+};
+hipError_t launch_permute(const PermuteParams& p, hipStream_t s, const char** name);
+
+struct SwigluParams {
+  const float* gu;          // [R, 2I] fp32
+  int64_t R, I;
+  int mode_w4a16;           // 1: write bf16 h, 0: quantize h
+  int fmt;
+  const int32_t* row_grp;   // optional: group (expert) of each row -> grp_g
+  const float* grp_g;       // per-group quantize multiplier (NVFP4)
+  float g;                  // scalar multiplier when row_grp == nullptr
+  uint8_t* h_codes;         // [R, I/2]
+  uint8_t* h_scales;        // [R, I/G]
+  uint16_t* h_bf16;         // [R, I]
+};
+hipError_t launch_swiglu(const SwigluParams& p, hipStream_t s, const char** name);
+
+struct CombineParams {
+  const float* y;           // [P + T (shared), H] fp32 in sorted order
+  const int32_t* inverse;   // [T*k]
+  const float* w;           // [T, k]
+  int64_t T, H;
+  int k;
+  const float* y_shared;    // [T, H] or nullptr
+  uint16_t* out;            // [T, H] bf16
+};
+hipError_t launch_combine(const CombineParams& p, hipStream_t s, const char** name);
+
+hipError_t launch_upload_floats(float* dst, const float* host_vals, int64_t n,
+                                hipStream_t s);
+
+}  // namespace fp4

@@ -1,0 +1,347 @@
+// Mixture-of-experts stages on gfx950: router, dispatch bookkeeping, SwiGLU with
+// requantization, and the top-k weighted combine.
+//
+// Stage structure: "vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A Complete
+// Technical Guide", §7.1 (Router -> Quantize-Dispatch -> Permute-Experts-
+// Unpermute -> Combine) and §4.3 (the fused expert: token dispatch, two GEMMs,
+// SwiGLU, top-k weight reduction, in-kernel BF16->FP4 quantization).  The expert
+// GEMMs themselves run in gemm.hip.
+//
+// Everything here is deterministic: routing ties go to the lower expert index,
+// the dispatch is a stable counting sort, and every reduction has a fixed order.
+#include <math.h>
+
+#include "device.h"
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace fp4 {
+
+namespace {
+
+// ---- router: one wave per token -----------------------------------------------
+constexpr int kMaxPerLane = 16;  // E <= 1024
+
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits,
+                                                           int64_t T, int E, int k, int renorm,
+                                                           int32_t* __restrict__ ids,
+                                                           float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform over the wave
+  const float* row = logits + t * E;
+  const int per = (E + 63) / 64;
+  float v[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (i < per && e < E) ? row[e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  int my_e = 0;
+  float my_v = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + 64 * i;
+      if (i < per && e < E && !((taken >> i) & 1u)) {
+        if (v[i] > bv || (v[i] == bv && e < be)) {
+          bv = v[i];
+          be = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) {
+      my_e = be;
+      my_v = bv;
+    }
+  }
+  // softmax over all E, evaluated at the chosen experts
+  const float mx = __shfl(my_v, 0);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    if (i < per && e < E) sum += expf(v[i] - mx);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  float wj = lane < k ? expf(my_v - mx) / sum : 0.f;
+  if (renorm) {
+    float s = wj;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    wj = wj / s;
+  }
+  if (lane < k) {
+    ids[t * k + lane] = my_e;
+    w[t * k + lane] = wj;
+  }
+}
+
+// ---- dispatch: counts, offsets and the row-block table (one workgroup) ---------
+constexpr int kScanThreads = 1024;
+
+__device__ int block_exclusive_scan(int x, int* buf) {
+  // Hillis-Steele inclusive scan over kScanThreads values, then shift
+  const int tid = threadIdx.x;
+  buf[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int add = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const int incl = buf[tid];
+  __syncthreads();
+  return incl - x;
+}
+
+__global__ __launch_bounds__(kScanThreads) void permute_count_kernel(PermuteParams p) {
+  __shared__ int cnt[kScanThreads];
+  __shared__ int buf[kScanThreads];
+  __shared__ int total_mb;
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  const int64_t n = p.T * p.k;
+  for (int64_t i = tid; i < n; i += kScanThreads) {
+    const int e = p.ids[i];
+    if (e >= 0 && e < p.E) atomicAdd(&cnt[e], 1);  // ids outside [0, E) are dropped
+    p.inverse[i] = -1;
+  }
+  __syncthreads();
+  const int c = tid < p.E ? cnt[tid] : 0;
+  const int off = block_exclusive_scan(c, buf);
+  if (tid < p.E) {
+    p.expert_offsets[tid] = off;
+    p.group_end[tid] = off + c;
+  }
+  if (tid == p.E - 1) p.expert_offsets[p.E] = off + c;
+  const int nmb = (c + p.bm - 1) / p.bm;
+  const int mbo = block_exclusive_scan(nmb, buf);
+  if (tid == kScanThreads - 1) total_mb = mbo + nmb;
+  if (tid < p.E) {
+    for (int j = 0; j < nmb; ++j) {
+      p.mblk_expert[mbo + j] = tid;
+      p.mblk_row0[mbo + j] = off + j * p.bm;
+    }
+  }
+  __syncthreads();
+  for (int64_t i = total_mb + tid; i < p.n_mblocks; i += kScanThreads) {
+    p.mblk_expert[i] = -1;
+    p.mblk_row0[i] = 0;
+  }
+}
+
+// ---- dispatch: stable scatter, one wave per expert -----------------------------
+__global__ __launch_bounds__(256) void permute_scatter_kernel(PermuteParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= p.E) return;
+  const int64_t n = p.T * p.k;
+  const int base = p.expert_offsets[e];
+  int running = 0;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t c = 0; c < n; c += 64) {
+    const int64_t i = c + lane;
+    const bool hit = i < n && p.ids[i] == e;
+    const uint64_t mask = __ballot(hit);
+    if (hit) {
+      const int pos = base + running + __popcll(mask & lt);
+      p.sorted_rows[pos] = (int32_t)i;
+      p.inverse[i] = pos;
+      p.row_expert[pos] = (int32_t)e;
+      p.src_token[pos] = (int32_t)(i / p.k);
+    }
+    running += __popcll(mask);
+  }
+}
+
+// ---- SwiGLU + requant: one lane = 8 consecutive intermediate columns -----------
+template <int FMT, bool W4A16>
+__global__ __launch_bounds__(256) void swiglu_kernel(SwigluParams p) {
+  constexpr int LPG = FMT == kNV ? 2 : 4;
+  const int64_t chunks = p.I / 8;
+  const int64_t total = p.R * chunks;
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = c < total;
+  const int64_t row = active ? c / chunks : 0;
+  const int64_t kc = active ? c - row * chunks : 0;
+  float h[8];
+  float amax = 0.f;
+  float g = p.g;
+  if (active) {
+    const float* gate = p.gu + row * (2 * p.I) + kc * 8;
+    const float* up = gate + p.I;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float z = gate[i];
+      const float silu = z / (1.0f + expf(-z));
+      h[i] = silu * up[i];
+      amax = fmaxf(amax, fabsf(h[i]));
+    }
+    if (p.row_grp) g = p.grp_g[p.row_grp[row]];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = 0.f;
+  }
+  if (W4A16) {
+    if (!active) return;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)f32_to_bf16_rne(h[2 * i]) | ((uint32_t)f32_to_bf16_rne(h[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(p.h_bf16 + row * p.I + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    return;
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  if (LPG == 4) amax = fmaxf(amax, __shfl_xor(amax, 2));
+  if (!active) return;
+  uint32_t packed = 0, sc;
+  if (FMT == kNV) {
+    const float sf = (amax * g) / 6.0f;
+    sc = e4m3_code_pos(sf);
+    const float sd = e4m3_value_pos(sc);
+    if (sd != 0.0f) {
+      const float r = g / sd;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        packed |= (e2m1_mag_code(fabsf(h[i]) * r) | ((__float_as_uint(h[i]) >> 31) << 3)) << (4 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) packed |= (__float_as_uint(h[i]) >> 31) << (4 * i + 3);
+    }
+  } else {
+    const uint32_t eb = (__float_as_uint(amax) >> 23) & 0xFFu;
+    const int code = eb == 0 ? 0 : max((int)eb - 2, 0);
+    sc = (uint32_t)code;
+    const int E = code - 127;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      packed |= (e2m1_mag_code(ldexpf(fabsf(h[i]), -E)) | ((__float_as_uint(h[i]) >> 31) << 3)) << (4 * i);
+  }
+  *reinterpret_cast<uint32_t*>(p.h_codes + row * (p.I / 2) + kc * 4) = packed;
+  if ((kc & (LPG - 1)) == 0) {
+    constexpr int G = FMT == kNV ? 16 : 32;
+    p.h_scales[row * (p.I / G) + kc / LPG] = (uint8_t)sc;
+  }
+}
+
+// ---- combine: out[t] = sum_j w[t,j] * y[inverse[t,j]] (+ shared) -> bf16 ------
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  const int64_t chunks = p.H / 8;
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= p.T * chunks) return;
+  const int64_t t = c / chunks;
+  const int64_t col = (c - t * chunks) * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < p.k; ++j) {
+    const int32_t pos = p.inverse[t * p.k + j];
+    if (pos < 0) continue;  // dropped (expert id out of range)
+    const float wj = p.w[t * p.k + j];
+    const float* yr = p.y + (int64_t)pos * p.H + col;
+    const float4 a = reinterpret_cast<const float4*>(yr)[0];
+    const float4 b = reinterpret_cast<const float4*>(yr)[1];
+    acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
+    acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+  }
+  if (p.y_shared) {
+    const float* yr = p.y_shared + t * p.H + col;
+    const float4 a = reinterpret_cast<const float4*>(yr)[0];
+    const float4 b = reinterpret_cast<const float4*>(yr)[1];
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i]) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(p.out + t * p.H + col) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---- per-expert host scalars -> device, passed by value ------------------------
+struct FloatPack {
+  float v[256];
+};
+
+__global__ void upload_kernel(float* dst, int n, FloatPack pk) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = pk.v[i];
+}
+
+}  // namespace
+
+hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,
+                               int renormalize, int32_t* ids, float* w, hipStream_t s,
+                               const char** name) {
+  if (T == 0) return hipSuccess;
+  *name = "topk_softmax";
+  hipLaunchKernelGGL(topk_softmax_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s,
+                     logits, T, (int)E, k, renormalize, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const PermuteParams& p, hipStream_t s, const char** name) {
+  *name = "permute";
+  hipLaunchKernelGGL(permute_count_kernel, dim3(1), dim3(kScanThreads), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)((p.E + 3) / 4)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const SwigluParams& p, hipStream_t s, const char** name) {
+  const int64_t total = p.R * (p.I / 8);
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (p.mode_w4a16) {
+    *name = "swiglu_bf16";
+    hipLaunchKernelGGL((swiglu_kernel<kNV, true>), grid, block, 0, s, p);
+  } else if (p.fmt == kNV) {
+    *name = "swiglu_quant_nvfp4";
+    hipLaunchKernelGGL((swiglu_kernel<kNV, false>), grid, block, 0, s, p);
+  } else {
+    *name = "swiglu_quant_mxfp4";
+    hipLaunchKernelGGL((swiglu_kernel<kMX, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t s, const char** name) {
+  const int64_t total = p.T * (p.H / 8);
+  if (total == 0) return hipSuccess;
+  *name = "combine";
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_upload_floats(float* dst, const float* host_vals, int64_t n, hipStream_t s) {
+  for (int64_t base = 0; base < n; base += 256) {
+    FloatPack pk;
+    const int cnt = (int)((n - base) < 256 ? (n - base) : 256);
+    for (int i = 0; i < 256; ++i) pk.v[i] = i < cnt ? host_vals[base + i] : 0.f;
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, dst + base, cnt, pk);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace fp4

@@ -1,0 +1,102 @@
+"""Tensor-level wrappers over the C ABI: allocate outputs with torch on the input's
+device and call the library.  Plumbing only; no arithmetic happens here."""
+import torch
+
+from . import (FP4_MXFP4, FP4_NVFP4, FP4_OUT_BF16, FP4_OUT_F32, FP4_W4A4, FP4_W4A16, GROUP,
+               _fmt, _mode, fp4_gemm, fp4_gemm_workspace_size, fp4_moe_grouped_gemm,
+               fp4_moe_topk_softmax, fp4_moe_workspace_layout, fp4_moe_workspace_size,
+               fp4_quantize_act, fp4_quantize_weight, make_moe_args)
+
+
+def _alloc_u8(rows, cols, device):
+    return torch.empty((rows, cols), dtype=torch.uint8, device=device)
+
+
+def quantize_act(fmt, x, input_scale=1.0):
+    """x: bf16 [M, K] (row stride may exceed K) -> (codes [M, K/2], scales [M, K/G])."""
+    f = _fmt(fmt)
+    M, K = x.shape
+    codes = _alloc_u8(M, K // 2, x.device)
+    scales = _alloc_u8(M, K // GROUP[f], x.device)
+    fp4_quantize_act(f, x, M, K, x.stride(0), float(input_scale), codes, scales)
+    return codes, scales
+
+
+def quantize_weight(fmt, w, weight_scale_2=1.0):
+    """w: fp32 [N, K] -> (codes [N, K/2], scales [N, K/G])."""
+    f = _fmt(fmt)
+    N, K = w.shape
+    codes = _alloc_u8(N, K // 2, w.device)
+    scales = _alloc_u8(N, K // GROUP[f], w.device)
+    fp4_quantize_weight(f, w, N, K, w.stride(0), float(weight_scale_2), codes, scales)
+    return codes, scales
+
+
+def gemm(fmt, mode, w_codes, w_scales, a_bf16=None, a_codes=None, a_scales=None,
+         weight_scale_2=1.0, input_scale=1.0, out_dtype=torch.bfloat16, flags=0, out=None,
+         workspace=None):
+    """out [M, N] = alpha * a_hat @ w_hat^T.  Returns (out, status)."""
+    f, m = _fmt(fmt), _mode(mode)
+    N, Kh = w_codes.shape
+    K = Kh * 2
+    M = a_bf16.shape[0] if a_bf16 is not None else a_codes.shape[0]
+    dev = w_codes.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    od = FP4_OUT_F32 if out.dtype == torch.float32 else FP4_OUT_BF16
+    wsz = fp4_gemm_workspace_size(f, m, M, K, a_bf16 is not None)
+    if workspace is None and wsz:
+        workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    lda = a_bf16.stride(0) if a_bf16 is not None else 0
+    st = fp4_gemm(f, m, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scales,
+                  float(weight_scale_2), float(input_scale), out, out.stride(0), od, flags,
+                  workspace, wsz if workspace is not None else 0)
+    return out, st
+
+
+def topk_softmax(logits, k, renormalize=True):
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    fp4_moe_topk_softmax(logits, T, E, k, renormalize, ids, w)
+    return ids, w
+
+
+class Moe:
+    """Holds the device weights of a MoE layer and runs fp4_moe_grouped_gemm."""
+
+    def __init__(self, fmt, mode, H, I, E, w13_codes, w13_scales, w2_codes, w2_scales,
+                 w13_scale_2=None, w2_scale_2=None, a13_scale=None, a2_scale=None,
+                 shared=None, flags=0):
+        self.fmt, self.mode = _fmt(fmt), _mode(mode)
+        self.H, self.I, self.E = H, I, E
+        self.w = (w13_codes, w13_scales, w2_codes, w2_scales)
+        self.scales = (w13_scale_2, w2_scale_2, a13_scale, a2_scale)
+        self.shared = shared
+        self.flags = flags
+        self._ws = None
+
+    def args(self, hidden, ids, w, out):
+        T = hidden.shape[0]
+        k = ids.shape[1]
+        return make_moe_args(self.fmt, self.mode, T, self.H, self.I, self.E, k, hidden, ids, w,
+                             *self.w, out, *self.scales, shared=self.shared, flags=self.flags)
+
+    def workspace_for(self, args):
+        need = fp4_moe_workspace_size(args)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.w[0].device)
+        return self._ws, need
+
+    def __call__(self, hidden, ids, w, out=None, check=True):
+        if out is None:
+            out = torch.empty((hidden.shape[0], self.H), dtype=torch.bfloat16, device=hidden.device)
+        args, keep = self.args(hidden, ids, w, out)
+        ws, need = self.workspace_for(args)
+        st = fp4_moe_grouped_gemm(args, ws, ws.numel(), check=check, device_tensor=hidden)
+        self.last_args, self._keep = args, keep
+        return out, st
+
+    def layout(self, hidden, ids, w, out):
+        args, keep = self.args(hidden, ids, w, out)
+        return fp4_moe_workspace_layout(args)

@@ -1,0 +1,203 @@
+"""The C-ABI boundary, on the CPU: the library loads, exports every function that
+include/fp4.h declares, and refuses bad arguments before touching a device.
+
+No call here reaches a kernel: each either fails host-side validation (fake but
+aligned addresses are never dereferenced) or stops at the device check, which on a
+machine without a gfx950 GPU must say FP4_ERR_DEVICE.  Error conventions follow the
+pages' failure modes: "GLM-5.3-Flash on vLLM, on GB10" (a zero activation scale
+must be refused, not computed with) and "vLLM on the NVIDIA DGX Spark (GB10 /
+sm_121): A Complete Technical Guide", §6.3 (unsupported device fails loudly).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_scaled_fp4_quantize_amd as F
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fp4.h")
+A = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
+B = 0x20000
+C = 0x30000
+D = 0x40000
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+NO_GPU = not _has_gpu()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(F.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(F.EXPORTED)
+
+
+def test_arch_predicate():
+    assert F.fp4_arch_supported("gfx950")
+    assert F.fp4_arch_supported("gfx950:sramecc+:xnack-")
+    for bad in ("gfx942", "gfx9500", "gfx90a", "", "sm_121"):
+        assert not F.fp4_arch_supported(bad)
+
+
+def test_status_strings():
+    for code in range(-9, 2):
+        assert F.status_str(code).startswith("FP4_")
+    assert F.status_str(F.FP4_ERR_INPUT_SCALE) == "FP4_ERR_INPUT_SCALE"
+
+
+def q(fmt, x, M, K, ldx, s, codes, scales):
+    return F.fp4_quantize_act(fmt, x, M, K, ldx, s, codes, scales, check=False)
+
+
+def test_quantize_validation():
+    assert q(7, A, 4, 32, 32, 1.0, B, C) == F.FP4_ERR_FORMAT
+    assert q(F.FP4_NVFP4, A, -1, 32, 32, 1.0, B, C) == F.FP4_ERR_SHAPE
+    assert q(F.FP4_NVFP4, A, 4, 24, 24, 1.0, B, C) == F.FP4_ERR_SHAPE       # K % 16
+    assert q(F.FP4_MXFP4, A, 4, 48, 48, 1.0, B, C) == F.FP4_ERR_SHAPE       # K % 32
+    assert q(F.FP4_NVFP4, A, 4, 32, 16, 1.0, B, C) == F.FP4_ERR_SHAPE       # ldx < K
+    assert q(F.FP4_NVFP4, None, 4, 32, 32, 1.0, B, C) == F.FP4_ERR_NULL
+    assert q(F.FP4_NVFP4, A, 4, 32, 32, 1.0, None, C) == F.FP4_ERR_NULL
+    assert q(F.FP4_NVFP4, A + 2, 4, 32, 32, 1.0, B, C) == F.FP4_ERR_ALIGN
+    assert q(F.FP4_NVFP4, A, 4, 32, 36, 1.0, B, C) == F.FP4_ERR_ALIGN       # ldx % 8
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 2.0 ** -101):
+        assert q(F.FP4_NVFP4, A, 4, 32, 32, bad, B, C) == F.FP4_ERR_INPUT_SCALE
+    assert q(F.FP4_MXFP4, A, 4, 32, 32, 0.5, B, C) == F.FP4_ERR_FORMAT
+    # empty problems are a no-op, even with NULL pointers
+    assert q(F.FP4_NVFP4, None, 0, 32, 32, 1.0, None, None) == F.FP4_OK
+    assert q(F.FP4_NVFP4, None, 4, 0, 0, 1.0, None, None) == F.FP4_OK
+    w = F.fp4_quantize_weight(F.FP4_NVFP4, A, 4, 32, 32, 0.0, B, C, check=False)
+    assert w == F.FP4_ERR_WEIGHT_SCALE
+
+
+@pytest.mark.skipif(not NO_GPU, reason="device check only observable without a GPU")
+def test_valid_calls_stop_at_device_check_without_gpu():
+    assert q(F.FP4_NVFP4, A, 4, 32, 32, 1.0, B, C) == F.FP4_ERR_DEVICE
+    st = F.fp4_moe_topk_softmax(A, 4, 8, 2, 1, B, C, check=False)
+    assert st == F.FP4_ERR_DEVICE
+    assert g(F.FP4_MXFP4, F.FP4_W4A4, a_codes=A, a_scales=B) == F.FP4_ERR_DEVICE
+
+
+def g(fmt, mode, M=4, N=8, K=64, a_bf16=None, lda=64, a_codes=None, a_scales=None,
+      w_codes=C, w_scales=D, ws2=1.0, s=1.0, out=0x50000, ldo=8, od=0, flags=0, ws=None,
+      wsb=0):
+    return F.fp4_gemm(fmt, mode, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scales,
+                      ws2, s, out, ldo, od, flags, ws, wsb, check=False)
+
+
+def test_gemm_validation():
+    NV, MX, W44, W416 = F.FP4_NVFP4, F.FP4_MXFP4, F.FP4_W4A4, F.FP4_W4A16
+    assert g(NV, 5, a_bf16=A) == F.FP4_ERR_FORMAT
+    assert g(NV, W44, a_bf16=A, od=3) == F.FP4_ERR_FORMAT
+    assert g(NV, W44, a_bf16=A, flags=8) == F.FP4_ERR_FORMAT
+    assert g(NV, W44, K=40, a_bf16=A) == F.FP4_ERR_SHAPE
+    assert g(NV, W44, K=0, a_bf16=A) == F.FP4_ERR_SHAPE
+    assert g(NV, W44, M=0, a_bf16=None, w_codes=None) == F.FP4_OK   # empty: no-op
+    assert g(NV, W44, ldo=4, a_bf16=A) == F.FP4_ERR_SHAPE
+    assert g(NV, W44, a_bf16=A, lda=32) == F.FP4_ERR_SHAPE
+    assert g(NV, W416) == F.FP4_ERR_NULL                            # W4A16 needs a_bf16
+    assert g(NV, W44, a_codes=A) == F.FP4_ERR_NULL                  # scales missing
+    assert g(NV, W44, a_bf16=A, w_codes=None) == F.FP4_ERR_NULL
+    assert g(NV, W44, a_bf16=A + 8) == F.FP4_ERR_ALIGN
+    assert g(NV, W44, a_bf16=A, lda=68) == F.FP4_ERR_ALIGN
+    assert g(NV, W44, a_bf16=A, ws2=0.0) == F.FP4_ERR_WEIGHT_SCALE
+    assert g(MX, W44, a_codes=A, a_scales=B, ws2=2.0) == F.FP4_ERR_FORMAT
+    assert g(MX, W44, a_codes=A, a_scales=B, s=0.5) == F.FP4_ERR_FORMAT
+    # the zeroed-activation-scale case is refused ...
+    assert g(NV, W44, a_bf16=A, s=0.0) == F.FP4_ERR_INPUT_SCALE
+    assert g(NV, W44, a_codes=A, a_scales=B, s=0.0) == F.FP4_ERR_INPUT_SCALE
+    # ... unless weight-only execution is explicitly allowed (needs the bf16 input)
+    st = g(NV, W44, a_bf16=A, s=0.0, flags=F.FP4_FLAG_ALLOW_W4A16_FALLBACK)
+    assert st in (F.FP4_ERR_DEVICE, F.FP4_OK_FELL_BACK_W4A16)
+    st = g(NV, W44, a_codes=A, a_scales=B, s=0.0, flags=F.FP4_FLAG_ALLOW_W4A16_FALLBACK)
+    assert st == F.FP4_ERR_INPUT_SCALE
+    # weight-only ignores input_scale, so 0 is legitimate there
+    assert g(NV, W416, a_bf16=A, s=0.0) in (F.FP4_ERR_DEVICE, F.FP4_OK)
+    # fused W4A4 needs a workspace of the reported size
+    need = F.fp4_gemm_workspace_size(NV, W44, 4, 64, 1)
+    assert need >= 4 * 32 + 4 * 4
+    assert F.fp4_gemm_workspace_size(NV, W416, 4, 64, 1) == 0
+    assert F.fp4_gemm_workspace_size(NV, W44, 4, 64, 0) == 0
+    assert g(NV, W44, a_bf16=A) == F.FP4_ERR_WORKSPACE
+    assert g(NV, W44, a_bf16=A, ws=0x60000, wsb=need - 1) == F.FP4_ERR_WORKSPACE
+
+
+def test_topk_validation():
+    t = lambda T, E, k: F.fp4_moe_topk_softmax(A, T, E, k, 1, B, C, check=False)
+    assert t(4, 8, 0) == F.FP4_ERR_SHAPE
+    assert t(4, 8, 9) == F.FP4_ERR_SHAPE
+    assert t(4, 2048, 8) == F.FP4_ERR_SHAPE
+    assert t(4, 64, 33) == F.FP4_ERR_SHAPE
+    assert t(0, 8, 2) == F.FP4_OK
+    assert F.fp4_moe_topk_softmax(None, 4, 8, 2, 1, B, C, check=False) == F.FP4_ERR_NULL
+
+
+def moe_args(fmt=F.FP4_NVFP4, mode=F.FP4_W4A4, T=4, H=64, I=32, E=4, k=2, a13=None, a2=None,
+             flags=0, shared=None, ws13=None, ws2=None):
+    nv = fmt == F.FP4_NVFP4
+    if nv:
+        ws13 = np.full(E, 0.01, np.float32) if ws13 is None else ws13
+        ws2 = np.full(E, 0.01, np.float32) if ws2 is None else ws2
+        if mode == F.FP4_W4A4:
+            a13 = np.full(E, 0.02, np.float32) if a13 is None else a13
+            a2 = np.full(E, 0.03, np.float32) if a2 is None else a2
+    args, keep = F.make_moe_args(fmt, mode, T, H, I, E, k, A, B, C, 0x50000, 0x60000, 0x70000,
+                                 0x80000, 0x90000, ws13, ws2, a13, a2, shared=shared,
+                                 flags=flags)
+    return args, keep
+
+
+def test_moe_validation_and_layout():
+    NV, MX = F.FP4_NVFP4, F.FP4_MXFP4
+    args, keep = moe_args()
+    size = F.fp4_moe_workspace_size(args)
+    lay = F.fp4_moe_workspace_layout(args)
+    assert size == lay.total_bytes > 0
+    offs = [lay.expert_offsets, lay.sorted_rows, lay.inverse, lay.x_codes, lay.x_scales, lay.gu,
+            lay.h_codes, lay.h_scales, lay.y]
+    assert all(o % 256 == 0 for o in offs) and len(set(offs)) == len(offs)
+    assert lay.x_rows == 4 * 2                      # NVFP4: one row per routed pair
+    st = F.fp4_moe_grouped_gemm(args, 0x100000, size - 1, check=False)
+    assert st == F.FP4_ERR_WORKSPACE
+    # zero activation scale for one expert: refused (the zeroed-MoE failure) ...
+    a13 = np.array([0.02, 0.0, 0.02, 0.02], np.float32)
+    args, keep = moe_args(a13=a13)
+    assert F.fp4_moe_grouped_gemm(args, 0x100000, 1 << 30, check=False) == F.FP4_ERR_INPUT_SCALE
+    assert F.fp4_moe_workspace_size(args) == 0
+    # ... and a missing scale array is the same failure
+    args, keep = moe_args()
+    args.a2_scale = ctypes.POINTER(ctypes.c_float)()
+    assert F.fp4_moe_grouped_gemm(args, 0x100000, 1 << 30, check=False) == F.FP4_ERR_INPUT_SCALE
+    # with the opt-in flag the layer may run weight-only; the layout reserves bf16 space
+    args, keep = moe_args(a13=a13, flags=F.FP4_FLAG_ALLOW_W4A16_FALLBACK)
+    lay = F.fp4_moe_workspace_layout(args)
+    assert lay.h_bf16 > 0
+    # shapes and formats
+    assert F.fp4_moe_grouped_gemm(moe_args(k=5)[0], A, 1 << 30, check=False) == F.FP4_ERR_SHAPE
+    assert F.fp4_moe_grouped_gemm(moe_args(H=40)[0], A, 1 << 30, check=False) == F.FP4_ERR_SHAPE
+    mx, keep = moe_args(fmt=MX)
+    assert F.fp4_moe_workspace_layout(mx).x_rows == 4   # MXFP4: one row per token
+    bad, keep2 = moe_args(fmt=MX, ws13=np.ones(4, np.float32), ws2=np.ones(4, np.float32))
+    assert F.fp4_moe_grouped_gemm(bad, 0x100000, 1 << 30, check=False) == F.FP4_ERR_FORMAT
+    ws_bad, keep3 = moe_args(ws13=np.array([0.01, -1, 0.01, 0.01], np.float32))
+    assert F.fp4_moe_grouped_gemm(ws_bad, 0x100000, 1 << 30, check=False) == F.FP4_ERR_WEIGHT_SCALE
+    half = {"w13_codes": 0x110000}
+    assert F.fp4_moe_grouped_gemm(moe_args(shared=half)[0], 0x100000, 1 << 30,
+                                  check=False) == F.FP4_ERR_NULL

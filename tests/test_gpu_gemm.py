@@ -1,0 +1,186 @@
+"""GPU parity of fp4_gemm against the oracle (dequantize, QDQ, matmul in float64).
+
+Definition: "vLLM per-format kernel capability matrix derived from source", THE
+EMULATION COLUMN; alpha = weight_scale_2 * input_scale ("GLM-5.3-Flash on vLLM, on
+GB10"); W4A16 = bf16 activations x dequantized weights ("vLLM on the DGX Spark, the
+Hard Way: Seven Months of GB10 Field Notes", native-FP4 conditions).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_quantize_amd as F
+from block_scaled_fp4_quantize_amd import tensors as T
+import synth
+from oracle import gemm as OG
+from oracle import quant as OQ
+from tests.gpu_util import DEV, bf16_dev, check_gemm, dequant, to_dev, weights
+
+pytestmark = pytest.mark.gpu
+
+
+def problem(fmt, M, N, K, seed, outliers=False):
+    wc, ws, ws2 = weights(fmt, N, K, seed)
+    a = synth.normal((M, K), seed=seed, role=synth.ACT, index=M)
+    if outliers:
+        a = synth.with_outliers(a, seed=seed)
+    ad, av = bf16_dev(a)
+    s = float(np.float32(np.abs(av).max()) / np.float32(2688.0)) if fmt == "nvfp4" else 1.0
+    return wc, ws, ws2, ad, av, s
+
+
+def run_and_check(fmt, mode, M, N, K, seed=0, out_dtype=torch.bfloat16, prequant=False,
+                  outliers=False, rows=None):
+    wc, ws, ws2, ad, av, s = problem(fmt, M, N, K, seed, outliers)
+    wcd, wsd = to_dev(wc), to_dev(ws)
+    if mode == "w4a16":
+        out, st = T.gemm(fmt, mode, wcd, wsd, a_bf16=ad, weight_scale_2=ws2, out_dtype=out_dtype)
+    elif prequant:
+        ac, asc = T.quantize_act(fmt, ad, s)
+        out, st = T.gemm(fmt, mode, wcd, wsd, a_codes=ac, a_scales=asc, weight_scale_2=ws2,
+                         input_scale=s, out_dtype=out_dtype)
+    else:
+        out, st = T.gemm(fmt, mode, wcd, wsd, a_bf16=ad, weight_scale_2=ws2, input_scale=s,
+                         out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert st == F.FP4_OK
+    got = out.float().cpu().numpy().astype(np.float64)
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    w_hat = dequant(fmt, wc, ws)
+    if mode == "w4a16":
+        a_hat = av[rows].astype(np.float64)
+        al = OG.alpha(fmt, OG.W4A16, ws2)
+    else:
+        ac_r, as_r = OQ.quantize_packed(fmt, av[rows], s)
+        a_hat = dequant(fmt, ac_r, as_r)
+        al = OG.alpha(fmt, OG.W4A4, ws2, s)
+    ref = al * (a_hat @ w_hat.T)
+    check_gemm(got[rows], ref, a_hat, w_hat, al, out_dtype == torch.bfloat16,
+               what=f"{fmt} {mode} M={M} N={N} K={K}")
+    if out_dtype == torch.float32:
+        r = np.linalg.norm(got[rows] - ref) / max(np.linalg.norm(ref), 1e-300)
+        assert r < 1e-5, f"fp32 accumulation error {r:.3g} is larger than expected"
+    return out
+
+
+SMALL = [(1, 16, 128), (5, 37, 256), (33, 50, 512), (17, 24, 384), (2, 8, 16), (3, 40, 96),
+         (6, 20, 48), (40, 64, 1024)]
+
+
+@pytest.mark.parametrize("shape", SMALL)
+@pytest.mark.parametrize("fmt,mode", [("nvfp4", "w4a4"), ("mxfp4", "w4a4"), ("nvfp4", "w4a16"),
+                                      ("mxfp4", "w4a16")])
+def test_small_shapes(fmt, mode, shape):
+    M, N, K = shape
+    if K % OQ.GROUP[fmt]:
+        pytest.skip("K not a multiple of the block size")
+    run_and_check(fmt, mode, M, N, K, seed=sum(shape))
+    run_and_check(fmt, mode, M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_prequantized_equals_fused(fmt):
+    # fused activation quantization gives the same bits as quantize-then-GEMM
+    M, N, K = 24, 48, 512
+    a = run_and_check(fmt, "w4a4", M, N, K, seed=9, prequant=True)
+    b = run_and_check(fmt, "w4a4", M, N, K, seed=9, prequant=False)
+    assert torch.equal(a, b)
+
+
+def test_nvfp4_w4a16_linear_small_config():
+    # weights [256, 512] N(0, 0.02) -> NVFP4, activations [4, 512] bf16 N(0, 1), seed 0
+    run_and_check("nvfp4", "w4a16", 4, 256, 512, seed=0)
+    run_and_check("nvfp4", "w4a16", 4, 256, 512, seed=0, out_dtype=torch.float32)
+
+
+@pytest.fixture(scope="module")
+def decode_problem():
+    fmt, N, K = "mxfp4", 14336, 4096
+    wc, ws, _ = weights(fmt, N, K, seed=0)
+    a = synth.with_outliers(synth.normal((32, K), seed=0, role=synth.ACT), seed=0)
+    return wc, ws, a
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_mxfp4_w4a4_decode_full_size(decode_problem, M):
+    # weights [14336, 4096] -> MXFP4; activations = the first M rows of [32, 4096]
+    # N(0, 1) with 1% x20 outliers, quantized on the fly
+    wc, ws, a = decode_problem
+    ad, av = bf16_dev(a[:M])
+    out, st = T.gemm("mxfp4", "w4a4", to_dev(wc), to_dev(ws), a_bf16=ad)
+    torch.cuda.synchronize()
+    assert st == F.FP4_OK
+    ac, asc = OQ.quantize_packed("mxfp4", av, 1.0)
+    a_hat, w_hat = dequant("mxfp4", ac, asc), dequant("mxfp4", wc, ws)
+    ref = a_hat @ w_hat.T
+    check_gemm(out.float().cpu().numpy().astype(np.float64), ref, a_hat, w_hat, 1.0, True,
+               what=f"decode M={M}")
+
+
+def test_nvfp4_w4a4_prefill_full_size_sampled_rows():
+    # [8192, 4096] x [4096, 4096]^T, fused quantization, bf16 out; the oracle checks
+    # 96 sampled rows (rows are independent) including the first and last
+    fmt, M, N, K = "nvfp4", 8192, 4096, 4096
+    rng = np.random.default_rng(0)
+    rows = np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 94, replace=False)])
+    run_and_check(fmt, "w4a4", M, N, K, seed=0, rows=np.sort(rows))
+
+
+def test_w4a4_is_not_weight_only():
+    # the W4A4 result matches the W4A4 oracle and not the W4A16 one
+    fmt, M, N, K = "nvfp4", 8, 64, 512
+    wc, ws, ws2, ad, av, s = problem(fmt, M, N, K, 11)
+    out, _ = T.gemm(fmt, "w4a4", to_dev(wc), to_dev(ws), a_bf16=ad, weight_scale_2=ws2,
+                    input_scale=s, out_dtype=torch.float32)
+    got = out.cpu().numpy().astype(np.float64)
+    ref44 = OG.gemm_fused(fmt, av, wc, ws, ws2, s)
+    ref416 = OG.gemm_w4a16(fmt, av, wc, ws, ws2)
+    d44 = np.linalg.norm(got - ref44) / np.linalg.norm(ref44)
+    d416 = np.linalg.norm(got - ref416) / np.linalg.norm(ref416)
+    assert d44 < 1e-5 and d416 > 1e-2
+
+
+def test_zero_input_scale_refused_or_explicit_fallback():
+    fmt, M, N, K = "nvfp4", 4, 32, 256
+    wc, ws, ws2, ad, av, _ = problem(fmt, M, N, K, 12)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    st = F.fp4_gemm(F.FP4_NVFP4, F.FP4_W4A4, M, N, K, ad, K, None, None, to_dev(wc),
+                    to_dev(ws), ws2, 0.0, out, N, F.FP4_OUT_F32, 0, None, 0, check=False)
+    torch.cuda.synchronize()
+    assert st == F.FP4_ERR_INPUT_SCALE
+    assert torch.isnan(out).all()                      # nothing was written
+    wcd, wsd = to_dev(wc), to_dev(ws)
+    st = F.fp4_gemm(F.FP4_NVFP4, F.FP4_W4A4, M, N, K, ad, K, None, None, wcd, wsd, ws2, 0.0,
+                    out, N, F.FP4_OUT_F32, F.FP4_FLAG_ALLOW_W4A16_FALLBACK, None, 0, check=False)
+    torch.cuda.synchronize()
+    assert st == F.FP4_OK_FELL_BACK_W4A16
+    ref = OG.gemm_w4a16(fmt, av, wc, ws, ws2)
+    assert np.linalg.norm(out.cpu().numpy() - ref) / np.linalg.norm(ref) < 1e-5
+
+
+def test_deterministic_canaries_and_two_streams():
+    fmt, M, N, K = "mxfp4", 40, 96, 1024
+    wc, ws, _, ad, av, _ = problem(fmt, M, N, K, 13)
+    wcd, wsd = to_dev(wc), to_dev(ws)
+    big = torch.full((M + 1, N + 8), float("nan"), dtype=torch.float32, device=DEV)
+    out = big[:M, :N]
+    T.gemm(fmt, "w4a4", wcd, wsd, a_bf16=ad, out=out)
+    torch.cuda.synchronize()
+    first = out.clone()
+    assert torch.isnan(big[M]).all() and torch.isnan(big[:, N:]).all()
+    # the same problem on two streams at once, next to a different one, stays bitwise equal
+    wc2, ws2_, _, ad2, _, _ = problem("nvfp4", 64, 128, 512, 14)
+    w2d, s2d = to_dev(wc2), to_dev(ws2_)
+    ref2, _ = T.gemm("nvfp4", "w4a16", w2d, s2d, a_bf16=ad2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for i in range(4):
+        with torch.cuda.stream(s1 if i % 2 == 0 else s2):
+            o1, _ = T.gemm(fmt, "w4a4", wcd, wsd, a_bf16=ad, out_dtype=torch.float32)
+            o2, _ = T.gemm("nvfp4", "w4a16", w2d, s2d, a_bf16=ad2)
+            outs.append((o1, o2))
+    torch.cuda.synchronize()
+    for o1, o2 in outs:
+        assert torch.equal(o1, first)
+        assert torch.equal(o2, ref2)
