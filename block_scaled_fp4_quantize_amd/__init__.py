@@ -46,7 +46,26 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -m block_scaled_fp4_quantize_amd.build` "
         "(there is no fallback implementation)")
 
+# torch (the device-memory and stream plumbing) ships its own HIP runtime under
+# the same soname as the system one.  Load it first so that libfp4 binds to that
+# same runtime: two HIP/HSA runtimes in one process do not share queues, memory
+# bookkeeping or synchronization, and kernels launched through one race copies
+# and syncs made through the other.
+import torch  # noqa: E402,F401
+
+
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
 _lib = ctypes.CDLL(LIB_PATH)
+if len(_hip_runtimes()) > 1:
+    raise ImportError("more than one HIP runtime is mapped into this process: "
+                      + ", ".join(_hip_runtimes()))
 
 _i64, _u32, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_uint32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _int = ctypes.c_int

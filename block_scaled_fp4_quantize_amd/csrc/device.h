@@ -16,6 +16,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -68,23 +71,56 @@ __device__ __forceinline__ float e8m0_value(uint32_t c) {
   return c == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((c & 0xFFu) << 23);
 }
 
-// Two e2m1 codes in byte `sel` of `packed` -> two bf16 values times `scale` (low
-// nibble first).  gfx950's scaled conversion multiplies in fp32; every product of
-// an e2m1 value and an e4m3 or e8m0 scale fits bf16 exactly.
-template <int SEL>
-__device__ __forceinline__ bf16x2 fp4x2_to_bf16(uint32_t packed, float scale) {
-  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, SEL);
-}
+// gfx950's scaled fp4 conversions apply only the exponent of their fp32 scale
+// operand (an e4m3 scale of 1.25 acts as 1.0), which is exactly an e8m0 scale.
+// So: MXFP4 codes decode in one instruction with the e8m0 scale; NVFP4 codes are
+// converted at unit scale and multiplied by the e4m3 block scale separately.
 
-// 8 e2m1 codes (one dword) -> bf16x8 operand, elements in k order.
-__device__ __forceinline__ bf16x8 decode8(uint32_t packed, float scale) {
-  bf16x2 p0 = fp4x2_to_bf16<0>(packed, scale);
-  bf16x2 p1 = fp4x2_to_bf16<1>(packed, scale);
-  bf16x2 p2 = fp4x2_to_bf16<2>(packed, scale);
-  bf16x2 p3 = fp4x2_to_bf16<3>(packed, scale);
+// 8 e2m1 codes (one dword, low nibble first) times an e8m0 scale -> bf16x8.
+__device__ __forceinline__ bf16x8 decode8_bf16_pow2(uint32_t packed, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 3);
   bf16x8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// 8 e2m1 codes times an arbitrary (e4m3) scale -> fp16x8, exactly: every product of
+// an e2m1 value and an e4m3 value lies in [2^-10, 2688] with at most six
+// significant bits, so it is an fp16 number.  One unit-scale convert and one
+// packed fp16 multiply per pair.
+__device__ __forceinline__ f16x8 decode8_f16(uint32_t packed, f16x2 scale2) {
+  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 0) * scale2;
+  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 1) * scale2;
+  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 2) * scale2;
+  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 3) * scale2;
+  f16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// 8 e2m1 codes times an arbitrary fp32 scale -> bf16x8 (for bf16 MFMA against bf16
+// activations).  The products are exact in fp32 and representable in bf16, so
+// keeping the upper half of each fp32 pattern is exact.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
+}
+
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_bf16_scaled(uint32_t packed, float scale) {
+  v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
+  return pack_bf16_exact(v[0] * scale, v[1] * scale);
+}
+
+__device__ __forceinline__ bf16x8 decode8_bf16(uint32_t packed, float scale) {
+  uint32_t w[4] = {fp4x2_bf16_scaled<0>(packed, scale), fp4x2_bf16_scaled<1>(packed, scale),
+                   fp4x2_bf16_scaled<2>(packed, scale), fp4x2_bf16_scaled<3>(packed, scale)};
+  bf16x8 r;
+  __builtin_memcpy(&r, w, 16);
   return r;
 }
 

@@ -8,10 +8,12 @@
 //    the instruction's scale operand ("vLLM on the NVIDIA DGX Spark ... Technical
 //    Guide", §6.4: MXFP4 = e2m1 + e8m0 per 32).
 //  * NVFP4 (e4m3 scale per 16) has no such mapping: e2m1 x e4m3 needs up to six
-//    significant bits, more than an fp8 operand holds, so codes are decoded
-//    exactly to bf16 (gfx950's scaled fp4->bf16 conversion) and multiplied with
-//    bf16 MFMA.  W4A16 (Field Notes: weight-only checkpoints keep 16-bit
-//    activations) uses the same path with the bf16 activations as they are.
+//    significant bits, more than an fp8 operand holds.  For W4A4 both operands
+//    are decoded exactly to fp16 (all such products are fp16 numbers) and
+//    multiplied with fp16 MFMA.  W4A16 ("vLLM on the DGX Spark, the Hard Way:
+//    Seven Months of GB10 Field Notes": weight-only checkpoints keep 16-bit
+//    activations) decodes the weights exactly to bf16 and uses bf16 MFMA against
+//    the bf16 activations as given.
 //
 // This file holds the "row-block" kernel: a workgroup owns one 16-row tile of W
 // and 16*MT rows of activations, its 4 waves split K and reduce through LDS in a
@@ -82,10 +84,16 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int j) {
   return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
 }
 
+// Block scale of sub-step `sub` (8 elements) of a lane's 32-element chunk.
 template <int FMT>
 __device__ __forceinline__ float scale_value(uint32_t sb, int sub) {
   if (FMT == kMX) return e8m0_value(sb & 0xFFu);
   return e4m3_value_pos((sb >> (8 * (sub >> 1))) & 0xFFu);
+}
+
+__device__ __forceinline__ f16x2 f16_pair(float v) {
+  const _Float16 h = (_Float16)v;  // exact: e4m3 values are fp16 numbers
+  return f16x2{h, h};
 }
 
 // FMT: kNV / kMX.  AK: kA_FP4 (activation codes) / kA_BF16.  MT: 16-row
@@ -178,17 +186,34 @@ __global__ __launch_bounds__(256) void rowblock_gemm(GemmParams p) {
           acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wop, aop, acc[t], 4, 4, 0, (int)wsb[u], 0, (int)asb[u][t]);
         }
-      } else {
+      } else if (FMT == kNV && AK == kA_FP4) {
+        // NVFP4 W4A4: both operands decoded exactly to fp16, fp16 MFMA
+        const f16x2 ws_lo = f16_pair(scale_value<FMT>(wsb[u], 0));
+        const f16x2 ws_hi = f16_pair(scale_value<FMT>(wsb[u], 2));
+        f16x2 as_lo[MT], as_hi[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          as_lo[t] = f16_pair(scale_value<FMT>(asb[u][t], 0));
+          as_hi[t] = f16_pair(scale_value<FMT>(asb[u][t], 2));
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x8 wop = decode8(dword_of(wq[u], j), scale_value<FMT>(wsb[u], j));
+          const f16x8 wop = decode8_f16(dword_of(wq[u], j), j < 2 ? ws_lo : ws_hi);
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
-            bf16x8 aop;
-            if (AK == kA_FP4)
-              aop = decode8(dword_of(aq[u][t], j), scale_value<FMT>(asb[u][t], j));
-            else
-              aop = bits_to_bf16x8(ab[u][t][j]);
+            const f16x8 aop = decode8_f16(dword_of(aq[u][t], j), j < 2 ? as_lo[t] : as_hi[t]);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t], 0, 0, 0);
+          }
+        }
+      } else {
+        // W4A16: weights decoded exactly to bf16, bf16 activations as given
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 wop = FMT == kMX ? decode8_bf16_pow2(dword_of(wq[u], j), scale_value<FMT>(wsb[u], j))
+                                        : decode8_bf16(dword_of(wq[u], j), scale_value<FMT>(wsb[u], j));
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const bf16x8 aop = bits_to_bf16x8(ab[u][t][j]);
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, aop, acc[t], 0, 0, 0);
           }
         }

@@ -127,22 +127,30 @@ class Expert:
         self.a13_scale, self.a2_scale = a13_scale, a2_scale
 
 
-def expert_h(fmt, mode, x, ex, buggy=False):
-    """gate/up projection and SwiGLU for rows x [n, H] -> h float64 [n, I]."""
+def expert_gu(fmt, mode, x, ex, buggy=False):
+    """gate/up projection of rows x [n, H] -> float64 [n, 2I] (gate cols [0, I), up [I, 2I))."""
     x = np.asarray(x, dtype=np.float32)
     if mode == Gm.W4A16:
-        gu = Gm.gemm_w4a16(fmt, x, ex.w13_codes, ex.w13_scales, ex.w13_scale_2)
-    elif fmt == Q.NVFP4:
+        return Gm.gemm_w4a16(fmt, x, ex.w13_codes, ex.w13_scales, ex.w13_scale_2)
+    if fmt == Q.NVFP4:
         s = ex.a13_scale
         if buggy and float(s) == 0.0:
             # the GLM page's fault: a zero activation scale zeroes alpha
-            gu = Gm.gemm_fused(fmt, x, ex.w13_codes, ex.w13_scales, ex.w13_scale_2, 1.0) * 0.0
-        else:
-            gu = Gm.gemm_fused(fmt, x, ex.w13_codes, ex.w13_scales, ex.w13_scale_2, s)
-    else:
-        gu = Gm.gemm_fused(fmt, x, ex.w13_codes, ex.w13_scales)
+            return Gm.gemm_fused(fmt, x, ex.w13_codes, ex.w13_scales, ex.w13_scale_2, 1.0) * 0.0
+        return Gm.gemm_fused(fmt, x, ex.w13_codes, ex.w13_scales, ex.w13_scale_2, s)
+    return Gm.gemm_fused(fmt, x, ex.w13_codes, ex.w13_scales)
+
+
+def swiglu(gu):
+    """h = SiLU(gate) * up for gu [n, 2I] (float64)."""
+    gu = np.asarray(gu, dtype=np.float64)
     I = gu.shape[1] // 2
     return silu(gu[:, :I]) * gu[:, I:]
+
+
+def expert_h(fmt, mode, x, ex, buggy=False):
+    """gate/up projection and SwiGLU for rows x [n, H] -> h float64 [n, I]."""
+    return swiglu(expert_gu(fmt, mode, x, ex, buggy))
 
 
 def expert_down(fmt, mode, h, ex, buggy=False):

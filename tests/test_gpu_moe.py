@@ -1,0 +1,347 @@
+"""GPU parity of the MoE path (router, dispatch, expert GEMMs, SwiGLU + requant,
+combine) against the oracle.
+
+Stages: "vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A Complete Technical Guide",
+§7.1 and §4.3; alpha and the zero-activation-scale refusal: "GLM-5.3-Flash on vLLM,
+on GB10".
+
+Integer work (routing ids, dispatch order, activation codes) must match exactly.
+The intermediate h is quantized from an fp32 value that both sides compute with
+different accumulation orders, so a code may differ where the oracle's value sits
+within a relative 1e-4 of a rounding decision: such differences are checked to be
+exactly that, and their effect on the expert output is added to the tolerance
+(computed from the two candidate codes).  Everything else follows the GEMM
+tolerance: |err| <= 2e-3 * alpha * ||a_hat|| * ||w_hat_n|| per element, and a
+relative Frobenius error <= 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_quantize_amd as F
+from block_scaled_fp4_quantize_amd import tensors as T
+import synth
+from oracle import formats as OF
+from oracle import moe as OM
+from oracle import quant as OQ
+from tests.gpu_util import DEV, bf16_ulp, round_bf16, to_dev
+from tests.moe_data import MoeProblem
+
+pytestmark = pytest.mark.gpu
+
+E2M1_THR = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+E4M3_MID = (OF.E4M3_TABLE[1:0x7F] + OF.E4M3_TABLE[:0x7E]) / 2
+EPS = 1e-4
+
+
+# ---------------------------------------------------------------------------------
+# device side
+# ---------------------------------------------------------------------------------
+
+
+def device_moe(pb, flags=0, a13=None):
+    st = pb.stacked()
+    dev = {n: to_dev(st[n]) for n in ("w13_codes", "w13_scales", "w2_codes", "w2_scales")}
+    shared = None
+    if pb.shared is not None:
+        sh = pb.shared
+        shared = dict(w13_codes=to_dev(sh.w13_codes), w13_scales=to_dev(sh.w13_scales),
+                      w2_codes=to_dev(sh.w2_codes), w2_scales=to_dev(sh.w2_scales))
+        if pb.fmt == OQ.NVFP4:
+            shared.update(w13_scale_2=sh.w13_scale_2, w2_scale_2=sh.w2_scale_2)
+            if pb.mode == "w4a4":
+                shared.update(a13_scale=sh.a13_scale, a2_scale=sh.a2_scale)
+    m = T.Moe(pb.fmt, pb.mode, pb.H, pb.I, pb.E, dev["w13_codes"], dev["w13_scales"],
+              dev["w2_codes"], dev["w2_scales"], st.get("w13_scale_2"), st.get("w2_scale_2"),
+              st.get("a13_scale") if a13 is None else a13, st.get("a2_scale"), shared=shared,
+              flags=flags)
+    hidden = to_dev(pb.hidden_bits.view(np.int16)).view(torch.bfloat16)
+    ids = to_dev(pb.ids.astype(np.int32))
+    w = to_dev(pb.w.astype(np.float32))
+    return m, hidden, ids, w, dev
+
+
+def ws_view(ws, off, count, dtype):
+    nbytes = count * torch.tensor([], dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype)
+
+
+def run_gpu(pb, flags=0):
+    m, hidden, ids, w, dev = device_moe(pb, flags)
+    out = torch.full((pb.T, pb.H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    _, st = m(hidden, ids, w, out)
+    torch.cuda.synchronize()
+    lay = m.layout(hidden, ids, w, out)
+    ws = m._ws
+    P = pb.T * pb.k
+    R = P + (pb.T if pb.shared is not None else 0)
+    G = OQ.GROUP[pb.fmt]
+    r = dict(status=st, out=out.float().cpu().numpy().astype(np.float64), layout=lay)
+    r["offsets"] = ws_view(ws, lay.expert_offsets, pb.E + 1, torch.int32).cpu().numpy()
+    r["sorted_rows"] = ws_view(ws, lay.sorted_rows, P, torch.int32).cpu().numpy()
+    r["inverse"] = ws_view(ws, lay.inverse, P, torch.int32).cpu().numpy()
+    r["gu"] = ws_view(ws, lay.gu, R * 2 * pb.I, torch.float32).view(R, 2 * pb.I)
+    r["y"] = ws_view(ws, lay.y, R * pb.H, torch.float32).view(R, pb.H)
+    if pb.mode == "w4a4":
+        r["x_codes"] = ws_view(ws, lay.x_codes, lay.x_rows * pb.H // 2, torch.uint8).view(lay.x_rows, -1)
+        r["x_scales"] = ws_view(ws, lay.x_scales, lay.x_rows * pb.H // G, torch.uint8).view(lay.x_rows, -1)
+        r["h_codes"] = ws_view(ws, lay.h_codes, R * pb.I // 2, torch.uint8).view(R, -1)
+        r["h_scales"] = ws_view(ws, lay.h_scales, R * pb.I // G, torch.uint8).view(R, -1)
+    else:
+        r["h_bf16"] = ws_view(ws, lay.h_bf16, R * pb.I, torch.bfloat16).view(R, pb.I)
+    r["_keep"] = (m, hidden, ids, w, dev)
+    return r
+
+
+# ---------------------------------------------------------------------------------
+# validity of a differing requantization code
+# ---------------------------------------------------------------------------------
+
+
+def allowed_diffs(fmt, h32, s):
+    """Elements of h (fp32 [n, I]) whose quantization sits within EPS of a decision:
+    a whole block when its scale choice is that close, else single elements."""
+    n, I = h32.shape
+    G = OQ.GROUP[fmt]
+    hb = np.abs(h32.astype(np.float64)).reshape(n, I // G, G)
+    amax = hb.max(-1)
+    if fmt == OQ.NVFP4:
+        g = float(np.float32(1.0) / np.float32(s))
+        sf = amax * g / 6.0
+        near_scale = np.min(np.abs(sf[..., None] - E4M3_MID), axis=-1) <= EPS * np.maximum(sf, 1e-30)
+        sc = OF.e4m3_encode_pos((amax.astype(np.float32) * np.float32(g)) / np.float32(6.0))
+        sd = OF.E4M3_TABLE[sc]
+        r = np.where(sd > 0, g / np.where(sd > 0, sd, 1.0), 0.0)
+        y = hb * r[..., None]
+    else:
+        lg = np.log2(np.maximum(amax, 1e-300))
+        near_scale = np.abs(lg - np.round(lg)) <= EPS
+        E = OF.mx_scale_exponent(amax)
+        y = hb * np.ldexp(1.0, -E)[..., None]
+    near_elem = np.min(np.abs(y[..., None] - E2M1_THR), axis=-1) <= EPS * np.maximum(y, 1e-30)
+    return (near_elem | near_scale[..., None]).reshape(n, I)
+
+
+# ---------------------------------------------------------------------------------
+# oracle side, per routed row
+# ---------------------------------------------------------------------------------
+
+
+def oracle_rows(pb, pairs, expert):
+    """Oracle intermediates for rows (token t) all routed to one expert object."""
+    x = pb.hidden[[t for t in pairs]]
+    gu = OM.expert_gu(pb.fmt, pb.mode, x, expert)
+    h = OM.swiglu(gu)
+    if pb.mode == "w4a4":
+        s2 = expert.a2_scale if pb.fmt == OQ.NVFP4 else 1.0
+        h32 = h.astype(np.float32)
+        hc, hs = OQ.quantize_packed(pb.fmt, h32, s2)
+        h_hat = OQ.dequantize_packed(pb.fmt, hc, hs)
+        a2 = expert.w2_scale_2 * s2 if pb.fmt == OQ.NVFP4 else 1.0
+    else:
+        h32, hc, hs, s2 = None, None, None, None
+        h_hat = round_bf16(h)
+        a2 = expert.w2_scale_2 if pb.fmt == OQ.NVFP4 else 1.0
+    w2_hat = OQ.dequantize_packed(pb.fmt, expert.w2_codes, expert.w2_scales)
+    y = a2 * (h_hat @ w2_hat.T)
+    w13_hat = OQ.dequantize_packed(pb.fmt, expert.w13_codes, expert.w13_scales)
+    if pb.mode == "w4a4":
+        s13 = expert.a13_scale if pb.fmt == OQ.NVFP4 else 1.0
+        xc, xs = OQ.quantize_packed(pb.fmt, x, s13)
+        x_hat = OQ.dequantize_packed(pb.fmt, xc, xs)
+        a13 = expert.w13_scale_2 * s13 if pb.fmt == OQ.NVFP4 else 1.0
+    else:
+        xc = xs = None
+        x_hat = x.astype(np.float64)
+        a13 = expert.w13_scale_2 if pb.fmt == OQ.NVFP4 else 1.0
+    return dict(gu=gu, h=h, h32=h32, hc=hc, hs=hs, s2=s2, h_hat=h_hat, y=y, w2_hat=w2_hat,
+                a2=a2, w13_hat=w13_hat, x_hat=x_hat, a13=a13, xc=xc, xs=xs)
+
+
+def verify(pb, r, tokens=None, max_diff_frac=1e-3):
+    """Check every stage for the given tokens (all by default)."""
+    T_, k, E, H, I = pb.T, pb.k, pb.E, pb.H, pb.I
+    tokens = np.arange(T_) if tokens is None else np.asarray(tokens)
+    G = OQ.GROUP[pb.fmt]
+    assert r["status"] == F.FP4_OK, F.status_str(r["status"])
+    # dispatch bookkeeping: exact
+    off, rows, inv = OM.permute(pb.ids, E)
+    assert np.array_equal(r["offsets"], off)
+    assert np.array_equal(r["sorted_rows"], rows)
+    assert np.array_equal(r["inverse"], inv)
+    P = T_ * k
+    # rows to check: (sorted position, token, expert object, routing weight)
+    work = {}
+    for t in tokens:
+        for j in range(k):
+            e = int(pb.ids[t, j])
+            work.setdefault(e, []).append((int(inv[t * k + j]), int(t), float(np.float32(pb.w[t, j]))))
+    if pb.shared is not None:
+        work["shared"] = [(P + int(t), int(t), 1.0) for t in tokens]
+    contrib = {int(t): [] for t in tokens}       # per token: (y_ref, bound_vec, allowance_vec, w)
+    n_diff = n_total = 0
+    gu_all = r["gu"]
+    y_all = r["y"]
+    for e, items in work.items():
+        ex = pb.shared if e == "shared" else pb.experts[e]
+        pos = np.array([p for p, _, _ in items])
+        toks = [t for _, t, _ in items]
+        o = oracle_rows(pb, toks, ex)
+        # GEMM1 input codes (W4A4): exact
+        if pb.mode == "w4a4":
+            if pb.fmt == OQ.MXFP4:
+                xr = np.array(toks)
+            else:
+                xr = pos
+            assert np.array_equal(r["x_codes"][xr].cpu().numpy(), o["xc"]), f"x codes, expert {e}"
+            assert np.array_equal(r["x_scales"][xr].cpu().numpy(), o["xs"]), f"x scales, expert {e}"
+        # GEMM1 output (fp32)
+        gu = gu_all[pos].cpu().numpy().astype(np.float64)
+        b1 = 2e-3 * abs(o["a13"]) * np.outer(np.linalg.norm(o["x_hat"], axis=1),
+                                             np.linalg.norm(o["w13_hat"], axis=1))
+        assert (np.abs(gu - o["gu"]) <= b1).all(), f"gate/up outside tolerance, expert {e}"
+        assert np.linalg.norm(gu - o["gu"]) <= 1e-5 * np.linalg.norm(o["gu"]) + 1e-30
+        # intermediate
+        if pb.mode == "w4a4":
+            gc = OF.unpack_nibbles(r["h_codes"][pos].cpu().numpy())
+            gs = r["h_scales"][pos].cpu().numpy()
+            oc = OF.unpack_nibbles(o["hc"])
+            diff = (gc != oc) | np.repeat(gs != o["hs"], G, axis=1)
+            ok = allowed_diffs(pb.fmt, o["h32"], o["s2"])
+            assert not (diff & ~ok).any(), f"intermediate codes differ away from a rounding decision, expert {e}"
+            n_diff += int(diff.sum())
+            n_total += diff.size
+            g_hat = OQ.dequantize(pb.fmt, gc, gs)
+            dh = np.abs(g_hat - o["h_hat"])
+        else:
+            g_hat = r["h_bf16"][pos].float().cpu().numpy().astype(np.float64)
+            # bf16 rounding of an fp32 value computed in another order: one bf16 ulp
+            dh = np.abs(g_hat - o["h_hat"])
+            assert (dh <= bf16_ulp(o["h_hat"]) + 1e-30).all() or \
+                np.linalg.norm(dh) <= 1e-2 * np.linalg.norm(o["h_hat"]), f"h (bf16), expert {e}"
+        allow = abs(o["a2"]) * (dh @ np.abs(o["w2_hat"]).T)          # [rows, H]
+        y = y_all[pos].cpu().numpy().astype(np.float64)
+        b2 = 2e-3 * abs(o["a2"]) * np.outer(np.linalg.norm(o["h_hat"], axis=1),
+                                            np.linalg.norm(o["w2_hat"], axis=1))
+        assert (np.abs(y - o["y"]) <= b2 + allow * (1 + 1e-6) + 1e-30).all(), f"down projection, expert {e}"
+        for i, (_, t, wt) in enumerate(items):
+            contrib[t].append((o["y"][i], b2[i], allow[i], wt))
+    assert n_total == 0 or n_diff <= max_diff_frac * n_total, f"{n_diff}/{n_total} intermediate codes differ"
+    # combine
+    for t in tokens:
+        ref = sum(wt * yr for yr, _, _, wt in contrib[int(t)])
+        bound = sum(wt * (b + a) for _, b, a, wt in contrib[int(t)])
+        ref_c = round_bf16(ref)
+        got = r["out"][t]
+        assert (np.abs(got - ref_c) <= bound + bf16_ulp(ref_c) + 1e-30).all(), f"out row {t}"
+    ref_all = np.stack([sum(wt * yr for yr, _, _, wt in contrib[int(t)]) for t in tokens])
+    rel = np.linalg.norm(r["out"][tokens] - round_bf16(ref_all)) / np.linalg.norm(round_bf16(ref_all))
+    assert rel <= 1e-3, f"relative Frobenius error {rel:.3g}"
+    return n_diff, n_total
+
+
+# ---------------------------------------------------------------------------------
+# tests
+# ---------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("T_,E,k", [(64, 128, 8), (5, 100, 3), (300, 256, 8), (7, 8, 8)])
+def test_topk_softmax(T_, E, k):
+    logits = synth.normal((T_, E), seed=T_, role=synth.LOGITS)
+    logits[0, :4] = logits[0, 4]                    # a tie: lower index first
+    ids, w = T.topk_softmax(to_dev(logits), k)
+    torch.cuda.synchronize()
+    rid, rw = OM.topk_softmax(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+    ids2, w2 = T.topk_softmax(to_dev(logits), k, renormalize=False)
+    _, rw2 = OM.topk_softmax(logits, k, renormalize=False)
+    assert np.allclose(w2.cpu().numpy(), rw2, rtol=2e-6, atol=1e-7)
+
+
+def test_topk_zipf_8192():
+    logits = synth.zipf_gumbel_logits(8192, 256, 1.1, seed=0)
+    ids, w = T.topk_softmax(to_dev(logits), 8)
+    torch.cuda.synchronize()
+    rid, rw = OM.topk_softmax(logits, 8)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+
+
+SMALL = [
+    ("nvfp4", "w4a4", dict(T=5, H=64, I=32, E=8, k=2, shared=True)),
+    ("mxfp4", "w4a4", dict(T=5, H=64, I=32, E=8, k=2, shared=True)),
+    ("nvfp4", "w4a16", dict(T=6, H=128, I=64, E=4, k=2, shared=True)),
+    ("mxfp4", "w4a16", dict(T=6, H=128, I=64, E=4, k=2, shared=False)),
+    ("nvfp4", "w4a4", dict(T=40, H=256, I=96, E=16, k=4, shared=False)),
+    ("mxfp4", "w4a4", dict(T=33, H=256, I=96, E=16, k=4, shared=True)),
+    ("nvfp4", "w4a4", dict(T=1, H=64, I=48, E=4, k=1, shared=False)),
+]
+
+
+@pytest.mark.parametrize("fmt,mode,kw", SMALL)
+def test_moe_small(fmt, mode, kw):
+    pb = MoeProblem(fmt, mode, seed=kw["T"] + kw["E"], **kw)
+    r = run_gpu(pb)
+    verify(pb, r, max_diff_frac=0.02)
+
+
+def test_moe_deterministic():
+    pb = MoeProblem("nvfp4", "w4a4", T=20, H=128, I=64, E=8, k=2, seed=3, shared=True)
+    a = run_gpu(pb)["out"]
+    b = run_gpu(pb)["out"]
+    assert np.array_equal(a, b)
+
+
+def test_zero_activation_scale_rejected_not_zeroed():
+    pb = MoeProblem("nvfp4", "w4a4", T=8, H=64, I=32, E=4, k=2, seed=5, shared=True)
+    st = pb.stacked()
+    a13 = st["a13_scale"].copy()
+    a13[2] = 0.0                                  # a weight-only checkpoint's missing scale
+    m, hidden, ids, w, dev = device_moe(pb, a13=a13)
+    out = torch.full((pb.T, pb.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    _, s = m(hidden, ids, w, out, check=False)
+    torch.cuda.synchronize()
+    assert s == F.FP4_ERR_INPUT_SCALE
+    assert (out == 7.0).all()                     # nothing ran
+    # with the opt-in flag the layer runs weight-only and says so
+    m2, hidden, ids, w, dev = device_moe(pb, flags=F.FP4_FLAG_ALLOW_W4A16_FALLBACK, a13=a13)
+    _, s = m2(hidden, ids, w, out, check=False)
+    torch.cuda.synchronize()
+    assert s == F.FP4_OK_FELL_BACK_W4A16
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref16 = OM.moe("nvfp4", "w4a16", pb.hidden, pb.ids, pb.w.astype(np.float32).astype(np.float64),
+                   pb.experts, pb.shared)
+    assert np.linalg.norm(got - round_bf16(ref16)) <= 1e-2 * np.linalg.norm(ref16)
+    # and it is not the zeroed-experts output of the page's bug
+    for ex in pb.experts:
+        ex.a13_scale = 0.0
+    buggy = OM.moe("nvfp4", "w4a4", pb.hidden, pb.ids, pb.w, pb.experts, pb.shared, buggy=True)
+    assert np.linalg.norm(got - buggy) > 0.1 * np.linalg.norm(got)
+
+
+@pytest.fixture(scope="module")
+def nvfp4_moe_layer():
+    return dict()
+
+
+@pytest.mark.parametrize("T_", [1, 64, 4096])
+def test_nvfp4_moe_128_experts(T_):
+    # 128 experts, top-8 softmax routing from N(0,1) logits, hidden 2048, gate+up
+    # 2048 -> 1536, down 768 -> 2048; tokens sampled for the oracle at T = 4096
+    pb = MoeProblem("nvfp4", "w4a4", T=T_, H=2048, I=768, E=128, k=8, seed=0, n_base=8)
+    r = run_gpu(pb)
+    toks = None if T_ <= 64 else np.random.default_rng(0).choice(T_, 6, replace=False)
+    if T_ == 64:
+        toks = np.arange(0, 64, 8)
+    verify(pb, r, tokens=toks)
+
+
+@pytest.mark.parametrize("T_", [64, 8192])
+def test_mxfp4_moe_256_experts_shared_zipf(T_):
+    # 256 experts top-8 + 1 shared, hidden 6144, intermediate 2048, Zipf(1.1) routing
+    pb = MoeProblem("mxfp4", "w4a4", T=T_, H=6144, I=2048, E=256, k=8, seed=0, n_base=4,
+                    shared=True, zipf=1.1)
+    r = run_gpu(pb)
+    toks = np.random.default_rng(1).choice(T_, 3, replace=False)
+    verify(pb, r, tokens=toks)
