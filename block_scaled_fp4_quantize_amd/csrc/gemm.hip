@@ -21,6 +21,8 @@
 // block with 16-byte loads (4 lanes cover 64 contiguous bytes of a row), which is
 // what decode-shaped problems need.  Grouped problems (MoE experts) enumerate
 // (row block, n tile) pairs from a device-side table, so no host sync is needed.
+#include <stdlib.h>
+
 #include "device.h"
 #include "internal.h"
 
@@ -254,6 +256,1022 @@ __global__ __launch_bounds__(256) void rowblock_gemm(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Streaming kernel for few activation rows (decode, and MoE experts at decode token
+// counts), fp4 activations, K a multiple of 128.  A workgroup owns 64 weight rows
+// (16 per wave, the full K range, so no cross-wave reduction) and 16*MT activation
+// rows.  The activation codes and scales are staged once per workgroup in LDS, in
+// chunks of 1024 K (double-buffered), instead of being re-read by every wave; each
+// wave keeps the next chunk's eight 16-byte weight loads per lane in flight while it
+// computes the current chunk (two register buffers used in turn).
+//
+// No load is predicated: a predicated load becomes a divergent branch, after which
+// the compiler waits for every outstanding load.  Rows past the end are clamped to
+// the last valid row (they only reach outputs that are not stored), and offsets
+// past K are clamped to chunks already read (those steps are not computed).
+// ---------------------------------------------------------------------------------
+constexpr int kSKC = 1024;               // K per staged chunk
+constexpr int kSSteps = kSKC / kKStep;   // 8 MFMA K-steps per chunk
+
+template <int FMT, int MT>
+struct StreamCfg {
+  static constexpr int G = FMT == kNV ? 16 : 32;
+  static constexpr int AROWS = 16 * MT;
+  static constexpr int ASTR = kSKC / 2 + 16;   // padded LDS row stride of staged codes
+  static constexpr int SSTR = kSKC / G;        // scale bytes per staged row per chunk
+  static constexpr int SDW = SSTR / 16;        // 16-byte scale loads per lane per chunk
+  static constexpr int TPR = 256 / AROWS;      // staging threads per activation row
+  static constexpr int CBT = (kSKC / 2) / TPR; // code bytes staged per thread (64 or 32)
+  static constexpr int NCL = CBT / 16;         // 16-byte code loads per staging thread
+  static constexpr int SBT = SSTR / TPR;       // scale bytes staged per thread (2, 4 or 8)
+  static constexpr int NSW = (SBT + 3) / 4;    // scale dwords per staging thread
+};
+
+// Activation staging of one chunk: every thread of the workgroup moves CBT code
+// bytes and SBT scale bytes of one activation row (global -> registers -> LDS).
+// The register copy is held in named variables (an array here ends up on the
+// stack, whose reloads the in-order load counter cannot wait for separately).
+struct StageRegs {
+  uint4 c0, c1, c2, c3, c4, c5, c6, c7;
+  uint32_t s0, s1, s2, s3;
+};
+
+template <int FMT, int MT>
+__device__ __forceinline__ StageRegs stage_load(const uint8_t* codes, const uint8_t* scales,
+                                                int64_t c, int64_t KB, int64_t KS, int sseg) {
+  using C = StreamCfg<FMT, MT>;
+  static_assert(C::NCL <= 8 && C::SBT <= 16 && C::SBT >= 2, "staging registers");
+  StageRegs rg;
+  const int64_t kb0 = c * (kSKC / 2) + sseg * C::CBT;
+  auto ld16 = [&](int i) {
+    const int64_t off = kb0 + i * 16;
+    return *reinterpret_cast<const uint4*>(codes + (off < KB ? off : 0));
+  };
+  const int64_t so = c * C::SSTR + sseg * C::SBT;
+  auto ld4 = [&](int i) {
+    const int64_t o = so + 4 * i;
+    return *reinterpret_cast<const uint32_t*>(scales + (o < KS ? o : 0));
+  };
+  rg.c0 = ld16(0); rg.c1 = ld16(1);
+  if (C::NCL > 2) { rg.c2 = ld16(2); rg.c3 = ld16(3); }
+  if (C::NCL > 4) { rg.c4 = ld16(4); rg.c5 = ld16(5); rg.c6 = ld16(6); rg.c7 = ld16(7); }
+  if (C::SBT == 2)  // KS is a multiple of 4, so so < KS implies so + 2 <= KS
+    rg.s0 = *reinterpret_cast<const uint16_t*>(scales + (so < KS ? so : 0));
+  else
+    rg.s0 = ld4(0);
+  if (C::SBT >= 8) rg.s1 = ld4(1);
+  if (C::SBT >= 16) { rg.s2 = ld4(2); rg.s3 = ld4(3); }
+  return rg;
+}
+
+template <int FMT, int MT>
+__device__ __forceinline__ void stage_store(uint8_t* a_lds, uint8_t* s_lds, int srow, int sseg,
+                                            const StageRegs& rg) {
+  using C = StreamCfg<FMT, MT>;
+  uint8_t* a = a_lds + srow * C::ASTR + sseg * C::CBT;
+  *reinterpret_cast<uint4*>(a) = rg.c0;
+  *reinterpret_cast<uint4*>(a + 16) = rg.c1;
+  if (C::NCL > 2) {
+    *reinterpret_cast<uint4*>(a + 32) = rg.c2;
+    *reinterpret_cast<uint4*>(a + 48) = rg.c3;
+  }
+  if (C::NCL > 4) {
+    *reinterpret_cast<uint4*>(a + 64) = rg.c4;
+    *reinterpret_cast<uint4*>(a + 80) = rg.c5;
+    *reinterpret_cast<uint4*>(a + 96) = rg.c6;
+    *reinterpret_cast<uint4*>(a + 112) = rg.c7;
+  }
+  if (C::SBT == 2) {
+    *reinterpret_cast<uint16_t*>(s_lds + srow * C::SSTR + sseg * C::SBT) = (uint16_t)rg.s0;
+    return;
+  }
+  uint32_t* sp = reinterpret_cast<uint32_t*>(s_lds + srow * C::SSTR + sseg * C::SBT);
+  sp[0] = rg.s0;
+  if (C::SBT >= 8) sp[1] = rg.s1;
+  if (C::SBT >= 16) { sp[2] = rg.s2; sp[3] = rg.s3; }
+}
+
+template <int FMT, bool SVEC>
+__device__ __forceinline__ void stream_w_load(const uint8_t* wrow, const uint8_t* wsrow,
+                                              int64_t c, int64_t K, int64_t KS, int gq,
+                                              uint4 (&q)[kSSteps],
+                                              uint4 (&sc)[StreamCfg<FMT, 1>::SDW]) {
+  constexpr int SSTR = StreamCfg<FMT, 1>::SSTR;
+  const int64_t k0 = c * kSKC;
+#pragma unroll
+  for (int j = 0; j < kSSteps; ++j) {
+    const int64_t kk = k0 + j * kKStep + gq * 32;
+    q[j] = *reinterpret_cast<const uint4*>(wrow + (kk < K ? (kk >> 1) : 0));
+  }
+#pragma unroll
+  for (int i = 0; i < StreamCfg<FMT, 1>::SDW; ++i) {
+    const int64_t so = c * SSTR + i * 16;
+    if (SVEC) {  // scale rows a multiple of 16 bytes: so < KS implies so + 16 <= KS
+      sc[i] = *reinterpret_cast<const uint4*>(wsrow + (so < KS ? so : 0));
+    } else {     // 4-byte granularity (KS is a multiple of 4)
+      uint32_t d[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const int64_t o = so + 4 * q2;
+        d[q2] = *reinterpret_cast<const uint32_t*>(wsrow + (o < KS ? o : 0));
+      }
+      sc[i] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+  }
+}
+
+// Branch-free over all kSSteps steps (a data-dependent exit would stop the full
+// unroll and turn the register buffers into stack memory); steps at or past
+// nsteps get an all-zero weight operand.
+template <int FMT, int MT>
+__device__ __forceinline__ void stream_compute(
+    const uint8_t* a_lds, const uint8_t* s_lds, const uint4 (&wq)[kSSteps],
+    const uint4 (&wsc)[StreamCfg<FMT, 1>::SDW], int nsteps, int r, int gq, v4f (&acc)[MT]) {
+  using C = StreamCfg<FMT, MT>;
+#pragma unroll
+  for (int j = 0; j < kSSteps; ++j) {
+    const uint32_t keep = j < nsteps ? 0xFFFFFFFFu : 0u;
+    const uint4 wj = make_uint4(wq[j].x & keep, wq[j].y & keep, wq[j].z & keep, wq[j].w & keep);
+    if (FMT == kMX) {
+      // scale byte 4j + gq of the chunk: dword j of the scale window
+      const uint32_t wsd = dword_of(wsc[j >> 2], j & 3);
+      const uint32_t wsb = (wsd >> (8 * gq)) & 0xFFu;
+      const v8i wop = {(int)wj.x, (int)wj.y, (int)wj.z, (int)wj.w, 0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int ar = t * 16 + r;
+        const uint4 aq = *reinterpret_cast<const uint4*>(a_lds + ar * C::ASTR + j * 64 + gq * 16);
+        const uint32_t asb = s_lds[ar * C::SSTR + j * 4 + gq];
+        const v8i aop = {(int)aq.x, (int)aq.y, (int)aq.z, (int)aq.w, 0, 0, 0, 0};
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop, aop, acc[t], 4, 4, 0,
+                                                                   (int)wsb, 0, (int)asb);
+      }
+    } else {
+      // scale bytes 8j + 2gq, +1 of the chunk: dword 2j + gq/2 of the scale window
+      const uint32_t d0 = dword_of(wsc[(2 * j) >> 2], (2 * j) & 3);
+      const uint32_t d1 = dword_of(wsc[(2 * j + 1) >> 2], (2 * j + 1) & 3);
+      const uint32_t wsd2 = (gq >> 1) ? d1 : d0;
+      const uint32_t wsb = (wsd2 >> (16 * (gq & 1))) & 0xFFFFu;
+      const f16x2 ws_lo = f16_pair(e4m3_value_pos(wsb & 0xFFu));
+      const f16x2 ws_hi = f16_pair(e4m3_value_pos(wsb >> 8));
+      uint4 aq[MT];
+      f16x2 as_lo[MT], as_hi[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int ar = t * 16 + r;
+        aq[t] = *reinterpret_cast<const uint4*>(a_lds + ar * C::ASTR + j * 64 + gq * 16);
+        const uint32_t asb = *reinterpret_cast<const uint16_t*>(s_lds + ar * C::SSTR + j * 8 + gq * 2);
+        as_lo[t] = f16_pair(e4m3_value_pos(asb & 0xFFu));
+        as_hi[t] = f16_pair(e4m3_value_pos(asb >> 8));
+      }
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const f16x8 wop = decode8_f16(dword_of(wj, sub), sub < 2 ? ws_lo : ws_hi);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const f16x8 aop = decode8_f16(dword_of(aq[t], sub), sub < 2 ? as_lo[t] : as_hi[t]);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int MT, bool SVEC>
+__global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
+  using C = StreamCfg<FMT, MT>;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][C::AROWS * C::ASTR];
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[2][C::AROWS * C::SSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t ntiles = (p.N + 63) >> 6;
+  const int64_t mb = (int64_t)blockIdx.x / ntiles;
+  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
+  int grp = 0;
+  int64_t row0, row_end;
+  if (p.mblk_expert) {
+    grp = p.mblk_expert[mb];
+    if (grp < 0) return;  // uniform over the workgroup
+    row0 = p.mblk_row0[mb];
+    row_end = p.group_end[grp];
+  } else {
+    row0 = mb * C::AROWS;
+    row_end = p.M;
+  }
+  const int64_t K = p.K;
+  const int64_t KB = K >> 1;
+  const int64_t KS = K / C::G;
+
+  const int r = lane & 15;
+  const int gq = lane >> 4;
+  const int64_t wn_raw = nt * 64 + wave * 16 + r;
+  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;
+  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
+  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
+
+  // activation staging: thread -> (row, segment of the row's chunk)
+  const int srow = tid / C::TPR;
+  const int sseg = tid % C::TPR;
+  int64_t pv = row0 + srow;
+  if (pv >= row_end) pv = row_end - 1;  // row0 < row_end for every block
+  const int64_t s_src = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
+  const uint8_t* s_codes = p.a_codes + s_src * KB;
+  const uint8_t* s_scales = p.a_scales + s_src * KS;
+  const int64_t nchunks = (K + kSKC - 1) / kSKC;
+  StageRegs st;
+
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wA[kSSteps], wB[kSSteps];
+  uint4 sA[C::SDW], sB[C::SDW];
+  auto steps_of = [&](int64_t c) {
+    const int64_t rem = (K - c * kSKC) / kKStep;
+    return rem < kSSteps ? (int)rem : kSSteps;
+  };
+
+  st = stage_load<FMT, MT>(s_codes, s_scales, 0, KB, KS, sseg);
+  stream_w_load<FMT, SVEC>(wrow, wsrow, 0, K, KS, gq, wA, sA);
+  stage_store<FMT, MT>(a_lds[0], s_lds[0], srow, sseg, st);
+  __syncthreads();
+  for (int64_t c = 0; c < nchunks; c += 2) {
+    // chunk c from (buffer 0, wA); prefetch chunk c+1 (clamped) into (buffer 1, wB)
+    {
+      const int64_t cn = c + 1 < nchunks ? c + 1 : c;
+      // issued before the weight loads, so waiting for it leaves those in flight
+      st = stage_load<FMT, MT>(s_codes, s_scales, cn, KB, KS, sseg);
+      __builtin_amdgcn_sched_barrier(0);  // keep the staging loads ahead of the weight loads
+      stream_w_load<FMT, SVEC>(wrow, wsrow, cn, K, KS, gq, wB, sB);
+      stream_compute<FMT, MT>(a_lds[0], s_lds[0], wA, sA, steps_of(c), r, gq, acc);
+      stage_store<FMT, MT>(a_lds[1], s_lds[1], srow, sseg, st);
+      __syncthreads();
+    }
+    if (c + 1 >= nchunks) break;
+    // chunk c+1 from (buffer 1, wB); prefetch chunk c+2 (clamped) into (buffer 0, wA)
+    {
+      const int64_t cn = c + 2 < nchunks ? c + 2 : c + 1;
+      st = stage_load<FMT, MT>(s_codes, s_scales, cn, KB, KS, sseg);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_w_load<FMT, SVEC>(wrow, wsrow, cn, K, KS, gq, wA, sA);
+      stream_compute<FMT, MT>(a_lds[1], s_lds[1], wB, sB, steps_of(c + 1), r, gq, acc);
+      stage_store<FMT, MT>(a_lds[0], s_lds[0], srow, sseg, st);
+      __syncthreads();
+    }
+  }
+
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = row0 + t * 16 + (lane & 15);
+    if (m >= row_end) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t n = nt * 64 + wave * 16 + 4 * (lane >> 4) + v;
+      if (n >= p.N) continue;
+      const float x = acc[t][v] * alpha;
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
+      else
+        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
+    }
+  }
+}
+
+template <int FMT, int MT>
+hipError_t launch_stream(const GemmParams& p, hipStream_t s, const char** name) {
+  const int64_t ntiles = (p.N + 63) / 64;
+  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
+  const int64_t grid = ntiles * mblocks;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  *name = FMT == kNV ? (MT == 1 ? "stream_nvfp4_m16" : "stream_nvfp4_m32")
+                     : (MT == 1 ? "stream_mxfp4_m16" : "stream_mxfp4_m32");
+  const bool svec = ((p.K / StreamCfg<FMT, MT>::G) % 16) == 0;
+  if (svec)
+    hipLaunchKernelGGL((stream_gemm<FMT, MT, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((stream_gemm<FMT, MT, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Split-K kernel for few activation rows, fp4 activations, K a multiple of 128.  A
+// workgroup owns 16 weight rows and 16*MT activation rows; its 4 waves take
+// contiguous quarters of K and reduce through LDS in wave order.  Each wave issues
+// the loads of up to 8 K-steps at once (weights, activations and their scales, all
+// unpredicated from clamped addresses), so with ~14 waves per CU the whole weight
+// matrix of a decode GEMM is requested within the first microseconds.
+// ---------------------------------------------------------------------------------
+constexpr int kBatch = 8;
+
+template <int FMT, int MT>
+struct SplitBatch {
+  uint4 w[kBatch];
+  uint32_t ws[kBatch];
+  uint4 a[kBatch][MT];
+  uint32_t as[kBatch][MT];
+};
+
+template <int FMT>
+__device__ __forceinline__ uint32_t load_scale_bytes(const uint8_t* srow, int64_t k0) {
+  if (FMT == kMX) return srow[k0 >> 5];
+  return *reinterpret_cast<const uint16_t*>(srow + (k0 >> 4));  // 2 e4m3 bytes, 2-aligned
+}
+
+template <int FMT, int MT>
+__device__ __forceinline__ void split_load(SplitBatch<FMT, MT>& b, const uint8_t* wrow,
+                                           const uint8_t* wsrow, const uint8_t* const (&arow)[MT],
+                                           const uint8_t* const (&asrow)[MT], int64_t s_begin,
+                                           int64_t s_end, int gq) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    int64_t s = s_begin + j;
+    if (s >= s_end) s = s_begin;  // clamp to a step of this batch (not computed)
+    const int64_t k0 = s * kKStep + gq * 32;
+    b.w[j] = *reinterpret_cast<const uint4*>(wrow + (k0 >> 1));
+    b.ws[j] = load_scale_bytes<FMT>(wsrow, k0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      b.a[j][t] = *reinterpret_cast<const uint4*>(arow[t] + (k0 >> 1));
+      b.as[j][t] = load_scale_bytes<FMT>(asrow[t], k0);
+    }
+  }
+}
+
+// All kBatch steps are computed without branches (a branch per step lets the
+// compiler sink each step's loads into it, serializing them); steps at or past n
+// get an all-zero weight operand, which contributes exactly zero.
+template <int FMT, int MT>
+__device__ __forceinline__ void split_compute(const SplitBatch<FMT, MT>& b, int n, v4f (&acc)[MT]) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const uint32_t keep = j < n ? 0xFFFFFFFFu : 0u;
+    const uint4 wj = make_uint4(b.w[j].x & keep, b.w[j].y & keep, b.w[j].z & keep, b.w[j].w & keep);
+    if (FMT == kMX) {
+      const v8i wop = {(int)wj.x, (int)wj.y, (int)wj.z, (int)wj.w, 0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const v8i aop = {(int)b.a[j][t].x, (int)b.a[j][t].y, (int)b.a[j][t].z, (int)b.a[j][t].w,
+                         0, 0, 0, 0};
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop, aop, acc[t], 4, 4, 0,
+                                                                   (int)b.ws[j], 0, (int)b.as[j][t]);
+      }
+    } else {
+      const f16x2 ws_lo = f16_pair(e4m3_value_pos(b.ws[j] & 0xFFu));
+      const f16x2 ws_hi = f16_pair(e4m3_value_pos((b.ws[j] >> 8) & 0xFFu));
+      f16x2 as_lo[MT], as_hi[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        as_lo[t] = f16_pair(e4m3_value_pos(b.as[j][t] & 0xFFu));
+        as_hi[t] = f16_pair(e4m3_value_pos((b.as[j][t] >> 8) & 0xFFu));
+      }
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const f16x8 wop = decode8_f16(dword_of(wj, sub), sub < 2 ? ws_lo : ws_hi);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const f16x8 aop = decode8_f16(dword_of(b.a[j][t], sub), sub < 2 ? as_lo[t] : as_hi[t]);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int MT>
+__global__ __launch_bounds__(256) void splitk_gemm(GemmParams p) {
+  constexpr int G = FMT == kNV ? 16 : 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t ntiles = (p.N + 15) >> 4;
+  const int64_t mb = (int64_t)blockIdx.x / ntiles;
+  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
+  int grp = 0;
+  int64_t row0, row_end;
+  if (p.mblk_expert) {
+    grp = p.mblk_expert[mb];
+    if (grp < 0) return;  // uniform over the workgroup
+    row0 = p.mblk_row0[mb];
+    row_end = p.group_end[grp];
+  } else {
+    row0 = mb * (16 * MT);
+    row_end = p.M;
+  }
+  const int64_t K = p.K;
+  const int64_t KB = K >> 1;
+  const int64_t KS = K / G;
+  const int r = lane & 15;
+  const int gq = lane >> 4;
+  // padded rows are clamped to the last valid one (their outputs are not stored)
+  const int64_t wn_raw = nt * 16 + r;
+  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;
+  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
+  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
+  const uint8_t* arow[MT];
+  const uint8_t* asrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    int64_t pv = row0 + t * 16 + r;
+    if (pv >= row_end) pv = row_end - 1;
+    const int64_t src = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
+    arow[t] = p.a_codes + src * KB;
+    asrow[t] = p.a_scales + src * KS;
+  }
+
+  const int64_t nsteps = K / kKStep;
+  const int64_t per = (nsteps + 3) / 4;
+  const int64_t s0 = wave * per;
+  const int64_t s1 = s0 + per < nsteps ? s0 + per : nsteps;
+
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // one batch of up to 8 steps in registers at a time (K <= 4096 is one batch per
+  // wave); a single buffer keeps the register count low enough for ~4 waves per SIMD
+  for (int64_t s = s0; s < s1; s += kBatch) {
+    SplitBatch<FMT, MT> b;
+    split_load<FMT, MT>(b, wrow, wsrow, arow, asrow, s, s1, gq);
+    // all of the batch's loads are issued before the first MFMA waits for data
+    __builtin_amdgcn_sched_barrier(0);
+    split_compute<FMT, MT>(b, (int)((s1 - s) < kBatch ? (s1 - s) : kBatch), acc);
+  }
+
+  __shared__ float red[3][MT][64][4];
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave - 1][t][lane][v] = acc[t][v];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = row0 + t * 16 + (lane & 15);
+    if (m >= row_end) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t n = nt * 16 + 4 * (lane >> 4) + v;
+      if (n >= p.N) continue;
+      float x = acc[t][v];
+      x += red[0][t][lane][v];
+      x += red[1][t][lane][v];
+      x += red[2][t][lane][v];
+      x *= alpha;
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
+      else
+        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
+    }
+  }
+}
+
+template <int FMT, int MT>
+hipError_t launch_splitk(const GemmParams& p, hipStream_t s, const char** name) {
+  const int64_t ntiles = (p.N + 15) / 16;
+  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
+  const int64_t grid = ntiles * mblocks;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  *name = FMT == kNV ? (MT == 1 ? "splitk_nvfp4_m16" : "splitk_nvfp4_m32")
+                     : (MT == 1 ? "splitk_mxfp4_m16" : "splitk_mxfp4_m32");
+  hipLaunchKernelGGL((splitk_gemm<FMT, MT>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Wide streaming kernel: the stream kernel's tiling (64 weight rows, activations
+// staged once per workgroup in LDS) with a 4096-wide K chunk, so each wave has all
+// 32 of its 16-byte weight loads per lane (and the scales) in flight at once and a
+// decode GEMM with K <= 4096 takes a single memory round trip.  Longer K loops
+// over 4096-wide chunks.
+// ---------------------------------------------------------------------------------
+constexpr int kWKC = 4096;
+constexpr int kWSteps = kWKC / kKStep;   // 32
+
+template <int FMT, int MT>
+struct WideCfg {
+  static constexpr int G = FMT == kNV ? 16 : 32;
+  static constexpr int AROWS = 16 * MT;
+  static constexpr int ASTR = kWKC / 2 + 16;    // padded LDS row stride of staged codes
+  static constexpr int SSTR = kWKC / G;         // scale bytes per staged row (128 / 256)
+  static constexpr int SDW = SSTR / 16;         // 16-byte scale loads per lane (8 / 16)
+  static constexpr int TPR = 256 / AROWS;       // staging threads per row (8 / 16)
+  static constexpr int CBT = (kWKC / 2) / TPR;  // code bytes staged per thread (256 / 128)
+  static constexpr int NCL = CBT / 16;          // 16-byte loads per staging thread (16 / 8)
+  static constexpr int SBT = SSTR / TPR;        // scale bytes staged per thread
+  static constexpr int NSW = SBT / 4;           // dwords (SBT is 8, 16 or 32)
+};
+
+template <int FMT, int MT>
+__global__ __launch_bounds__(256) void wide_gemm(GemmParams p) {
+  using C = WideCfg<FMT, MT>;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[C::AROWS * C::ASTR];
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[C::AROWS * C::SSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t ntiles = (p.N + 63) >> 6;
+  const int64_t mb = (int64_t)blockIdx.x / ntiles;
+  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
+  int grp = 0;
+  int64_t row0, row_end;
+  if (p.mblk_expert) {
+    grp = p.mblk_expert[mb];
+    if (grp < 0) return;  // uniform over the workgroup
+    row0 = p.mblk_row0[mb];
+    row_end = p.group_end[grp];
+  } else {
+    row0 = mb * C::AROWS;
+    row_end = p.M;
+  }
+  const int64_t K = p.K;
+  const int64_t KB = K >> 1;
+  const int64_t KS = K / C::G;
+  const int r = lane & 15;
+  const int gq = lane >> 4;
+  const int64_t wn_raw = nt * 64 + wave * 16 + r;
+  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;   // padded rows: outputs not stored
+  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
+  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
+
+  const int srow = tid / C::TPR;
+  const int sseg = tid % C::TPR;
+  int64_t pv = row0 + srow;
+  if (pv >= row_end) pv = row_end - 1;  // row0 < row_end for every block
+  const int64_t s_src = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
+  const uint8_t* s_codes = p.a_codes + s_src * KB;
+  const uint8_t* s_scales = p.a_scales + s_src * KS;
+  const int64_t nchunks = (K + kWKC - 1) / kWKC;
+
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t c = 0; c < nchunks; ++c) {
+    if (c > 0) __syncthreads();  // every wave is done with the previous chunk's LDS
+    // 1. activation staging loads (issued first, so waiting for them leaves the
+    //    weight loads in flight)
+    uint4 stc[C::NCL];
+    uint32_t sts[C::NSW];
+    {
+      const int64_t kb0 = c * (kWKC / 2) + sseg * C::CBT;
+#pragma unroll
+      for (int i = 0; i < C::NCL; ++i) {
+        const int64_t off = kb0 + i * 16;
+        stc[i] = *reinterpret_cast<const uint4*>(s_codes + (off < KB ? off : 0));
+      }
+      const int64_t so = c * C::SSTR + sseg * C::SBT;
+#pragma unroll
+      for (int i = 0; i < C::NSW; ++i) {
+        const int64_t o = so + 4 * i;
+        sts[i] = *reinterpret_cast<const uint32_t*>(s_scales + (o < KS ? o : 0));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. all weight loads of the chunk (steps past K are clamped, not computed)
+    uint4 wq[kWSteps];
+    uint4 wsc[C::SDW];
+    {
+      const int64_t k0 = c * kWKC;
+#pragma unroll
+      for (int j = 0; j < kWSteps; ++j) {
+        const int64_t kk = k0 + j * kKStep + gq * 32;
+        wq[j] = *reinterpret_cast<const uint4*>(wrow + (kk < K ? (kk >> 1) : 0));
+      }
+      // scale rows are a multiple of 4 bytes; 16-byte loads where the row allows
+#pragma unroll
+      for (int i = 0; i < C::SDW; ++i) {
+        const int64_t so = c * C::SSTR + i * 16;
+        uint32_t d[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const int64_t o = so + 4 * q2;
+          d[q2] = *reinterpret_cast<const uint32_t*>(wsrow + (o < KS ? o : 0));
+        }
+        wsc[i] = make_uint4(d[0], d[1], d[2], d[3]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. publish the activation chunk
+    {
+#pragma unroll
+      for (int i = 0; i < C::NCL; ++i)
+        *reinterpret_cast<uint4*>(a_lds + srow * C::ASTR + sseg * C::CBT + i * 16) = stc[i];
+#pragma unroll
+      for (int i = 0; i < C::NSW; ++i)
+        *reinterpret_cast<uint32_t*>(s_lds + srow * C::SSTR + sseg * C::SBT + 4 * i) = sts[i];
+    }
+    __syncthreads();
+    // 4. compute (steps past K get a zero weight operand: no branches)
+    const int64_t rem = (K - c * kWKC) / kKStep;
+    const uint32_t* wsd = reinterpret_cast<const uint32_t*>(wsc);
+#pragma unroll
+    for (int j = 0; j < kWSteps; ++j) {
+      const uint32_t keep = j < rem ? 0xFFFFFFFFu : 0u;
+      const uint4 wj = make_uint4(wq[j].x & keep, wq[j].y & keep, wq[j].z & keep, wq[j].w & keep);
+      if (FMT == kMX) {
+        const uint32_t wsb = (wsd[j] >> (8 * gq)) & 0xFFu;
+        const v8i wop = {(int)wj.x, (int)wj.y, (int)wj.z, (int)wj.w, 0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int ar = t * 16 + r;
+          const uint4 aq = *reinterpret_cast<const uint4*>(a_lds + ar * C::ASTR + j * 64 + gq * 16);
+          const uint32_t asb = s_lds[ar * C::SSTR + j * 4 + gq];
+          const v8i aop = {(int)aq.x, (int)aq.y, (int)aq.z, (int)aq.w, 0, 0, 0, 0};
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop, aop, acc[t], 4, 4, 0,
+                                                                     (int)wsb, 0, (int)asb);
+        }
+      } else {
+        const uint32_t wsd2 = (gq >> 1) ? wsd[2 * j + 1] : wsd[2 * j];
+        const uint32_t wsb = (wsd2 >> (16 * (gq & 1))) & 0xFFFFu;
+        const f16x2 ws_lo = f16_pair(e4m3_value_pos(wsb & 0xFFu));
+        const f16x2 ws_hi = f16_pair(e4m3_value_pos(wsb >> 8));
+        uint4 aq[MT];
+        f16x2 as_lo[MT], as_hi[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int ar = t * 16 + r;
+          aq[t] = *reinterpret_cast<const uint4*>(a_lds + ar * C::ASTR + j * 64 + gq * 16);
+          const uint32_t asb = *reinterpret_cast<const uint16_t*>(s_lds + ar * C::SSTR + j * 8 + gq * 2);
+          as_lo[t] = f16_pair(e4m3_value_pos(asb & 0xFFu));
+          as_hi[t] = f16_pair(e4m3_value_pos(asb >> 8));
+        }
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          const f16x8 wop = decode8_f16(dword_of(wj, sub), sub < 2 ? ws_lo : ws_hi);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const f16x8 aop = decode8_f16(dword_of(aq[t], sub), sub < 2 ? as_lo[t] : as_hi[t]);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = row0 + t * 16 + (lane & 15);
+    if (m >= row_end) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t n = nt * 64 + wave * 16 + 4 * (lane >> 4) + v;
+      if (n >= p.N) continue;
+      const float x = acc[t][v] * alpha;
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
+      else
+        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
+    }
+  }
+}
+
+template <int FMT, int MT>
+hipError_t launch_wide(const GemmParams& p, hipStream_t s, const char** name) {
+  const int64_t ntiles = (p.N + 63) / 64;
+  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
+  const int64_t grid = ntiles * mblocks;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  *name = FMT == kNV ? (MT == 1 ? "wide_nvfp4_m16" : "wide_nvfp4_m32")
+                     : (MT == 1 ? "wide_mxfp4_m16" : "wide_mxfp4_m32");
+  hipLaunchKernelGGL((wide_gemm<FMT, MT>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Resident-activation streaming kernel (decode and small expert batches, fp4
+// activations, K a multiple of 128, activations for the full K fitting in LDS).
+// A workgroup owns 64 weight rows (16 per wave, full K) and 16*MT activation rows.
+// The activation codes and scales for the whole K are staged in LDS once, behind a
+// single barrier; after that every wave streams its weight rows in a barrier-free
+// loop of 8-step batches with the next batch's loads in flight (two register
+// buffers used in turn).  The first weight batch is requested before the staging,
+// so its latency overlaps it.
+// ---------------------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ void rk_w_load(const uint8_t* wrow, const uint8_t* wsrow, int64_t s0,
+                                          int64_t nsteps, int gq, uint4 (&q)[kBatch],
+                                          uint32_t (&sc)[kBatch]) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    int64_t st = s0 + j;
+    if (st >= nsteps) st = nsteps - 1;      // clamped: not computed
+    const int64_t k0 = st * kKStep + gq * 32;
+    q[j] = *reinterpret_cast<const uint4*>(wrow + (k0 >> 1));
+    if (FMT == kMX)
+      sc[j] = wsrow[k0 >> 5];
+    else
+      sc[j] = *reinterpret_cast<const uint16_t*>(wsrow + (k0 >> 4));
+  }
+}
+
+template <int FMT, int MT>
+__device__ __forceinline__ void rk_compute(const uint8_t* a_lds, const uint8_t* s_lds, int astr,
+                                           int sstr, int64_t s0, int64_t nsteps, int r, int gq,
+                                           const uint4 (&q)[kBatch], const uint32_t (&sc)[kBatch],
+                                           v4f (&acc)[MT]) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int64_t st = s0 + j;
+    const uint32_t keep = st < nsteps ? 0xFFFFFFFFu : 0u;   // zero operand past K (no branch)
+    const int64_t stc = st < nsteps ? st : nsteps - 1;
+    const uint4 wj = make_uint4(q[j].x & keep, q[j].y & keep, q[j].z & keep, q[j].w & keep);
+    const int kbyte = (int)(stc * 64) + gq * 16;            // code byte offset in a staged row
+    if (FMT == kMX) {
+      const int kscale = (int)(stc * 4) + gq;
+      const v8i wop = {(int)wj.x, (int)wj.y, (int)wj.z, (int)wj.w, 0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int ar = t * 16 + r;
+        const uint4 aq = *reinterpret_cast<const uint4*>(a_lds + ar * astr + kbyte);
+        const uint32_t asb = s_lds[ar * sstr + kscale];
+        const v8i aop = {(int)aq.x, (int)aq.y, (int)aq.z, (int)aq.w, 0, 0, 0, 0};
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop, aop, acc[t], 4, 4, 0,
+                                                                   (int)sc[j], 0, (int)asb);
+      }
+    } else {
+      const int kscale = (int)(stc * 8) + gq * 2;
+      const f16x2 ws_lo = f16_pair(e4m3_value_pos(sc[j] & 0xFFu));
+      const f16x2 ws_hi = f16_pair(e4m3_value_pos((sc[j] >> 8) & 0xFFu));
+      uint4 aq[MT];
+      f16x2 as_lo[MT], as_hi[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int ar = t * 16 + r;
+        aq[t] = *reinterpret_cast<const uint4*>(a_lds + ar * astr + kbyte);
+        const uint32_t asb = *reinterpret_cast<const uint16_t*>(s_lds + ar * sstr + kscale);
+        as_lo[t] = f16_pair(e4m3_value_pos(asb & 0xFFu));
+        as_hi[t] = f16_pair(e4m3_value_pos(asb >> 8));
+      }
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const f16x8 wop = decode8_f16(dword_of(wj, sub), sub < 2 ? ws_lo : ws_hi);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const f16x8 aop = decode8_f16(dword_of(aq[t], sub), sub < 2 ? as_lo[t] : as_hi[t]);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// LDS bytes the resident kernel needs: staged code rows (padded) + scale rows
+inline int64_t rk_lds_bytes(int fmt, int mt, int64_t K) {
+  const int64_t G = fmt == kNV ? 16 : 32;
+  return 16 * mt * ((K / 2 + 16) + K / G);
+}
+constexpr int64_t kRkMaxLds = 120 * 1024;
+
+template <int FMT, int MT>
+__global__ __launch_bounds__(256) void rk_gemm(GemmParams p) {
+  constexpr int G = FMT == kNV ? 16 : 32;
+  constexpr int AROWS = 16 * MT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t rk_smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t ntiles = (p.N + 63) >> 6;
+  const int64_t mb = (int64_t)blockIdx.x / ntiles;
+  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
+  int grp = 0;
+  int64_t row0, row_end;
+  if (p.mblk_expert) {
+    grp = p.mblk_expert[mb];
+    if (grp < 0) return;  // uniform over the workgroup
+    row0 = p.mblk_row0[mb];
+    row_end = p.group_end[grp];
+  } else {
+    row0 = mb * AROWS;
+    row_end = p.M;
+  }
+  const int64_t K = p.K;
+  const int64_t KB = K >> 1;
+  const int64_t KS = K / G;
+  const int astr = (int)KB + 16;          // padded row stride (bank spread)
+  const int sstr = (int)KS;
+  uint8_t* a_lds = rk_smem;
+  uint8_t* s_lds = rk_smem + AROWS * astr;
+
+  const int r = lane & 15;
+  const int gq = lane >> 4;
+  const int64_t wn_raw = nt * 64 + wave * 16 + r;
+  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;   // padded rows: outputs not stored
+  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
+  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
+  const int64_t nsteps = K / kKStep;
+
+  // first weight batch in flight before the staging
+  uint4 qA[kBatch], qB[kBatch];
+  uint32_t sA[kBatch], sB[kBatch];
+  rk_w_load<FMT>(wrow, wsrow, 0, nsteps, gq, qA, sA);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // source row of each staged activation row (gathered once; padded rows repeat
+  // the last valid row)
+  __shared__ int64_t rk_src[AROWS];
+  if (tid < AROWS) {
+    int64_t pv = row0 + tid;
+    if (pv >= row_end) pv = row_end - 1;
+    rk_src[tid] = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
+  }
+  __syncthreads();
+  // stage the activation rows for the full K: codes in 16-byte pieces, scales in
+  // 4-byte pieces (KB is a multiple of 64, KS of 4), 8 loads per thread issued
+  // before their LDS stores
+  {
+    const int64_t cpr = KB / 16;                      // code pieces per row
+    const int64_t pieces = AROWS * cpr;
+    for (int64_t base = 0; base < pieces; base += 256 * 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        int64_t i = base + u * 256 + tid;
+        if (i >= pieces) i = pieces - 1;              // clamped load, store skipped below
+        const int row = (int)(i / cpr);
+        v[u] = *reinterpret_cast<const uint4*>(p.a_codes + rk_src[row] * KB + (i - (int64_t)row * cpr) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // the group's loads go out before its stores
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = base + u * 256 + tid;
+        if (i < pieces) {
+          const int row = (int)(i / cpr);
+          *reinterpret_cast<uint4*>(a_lds + row * astr + (i - (int64_t)row * cpr) * 16) = v[u];
+        }
+      }
+    }
+    const int64_t spr = KS / 4;                       // scale pieces per row
+    const int64_t spieces = AROWS * spr;
+    for (int64_t base = 0; base < spieces; base += 256 * 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        int64_t i = base + u * 256 + tid;
+        if (i >= spieces) i = spieces - 1;
+        const int row = (int)(i / spr);
+        v[u] = *reinterpret_cast<const uint32_t*>(p.a_scales + rk_src[row] * KS + (i - (int64_t)row * spr) * 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = base + u * 256 + tid;
+        if (i < spieces) {
+          const int row = (int)(i / spr);
+          *reinterpret_cast<uint32_t*>(s_lds + row * sstr + (i - (int64_t)row * spr) * 4) = v[u];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int64_t s0 = 0; s0 < nsteps; s0 += 2 * kBatch) {
+    // batch s0 from qA (prefetch s0 + 8 into qB), then batch s0 + 8 from qB
+    // (prefetch s0 + 16 into qA); clamped prefetches past K re-read the last step
+    rk_w_load<FMT>(wrow, wsrow, s0 + kBatch, nsteps, gq, qB, sB);
+    rk_compute<FMT, MT>(a_lds, s_lds, astr, sstr, s0, nsteps, r, gq, qA, sA, acc);
+    if (s0 + kBatch >= nsteps) break;
+    rk_w_load<FMT>(wrow, wsrow, s0 + 2 * kBatch, nsteps, gq, qA, sA);
+    rk_compute<FMT, MT>(a_lds, s_lds, astr, sstr, s0 + kBatch, nsteps, r, gq, qB, sB, acc);
+  }
+
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = row0 + t * 16 + (lane & 15);
+    if (m >= row_end) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t n = nt * 64 + wave * 16 + 4 * (lane >> 4) + v;
+      if (n >= p.N) continue;
+      const float x = acc[t][v] * alpha;
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
+      else
+        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
+    }
+  }
+}
+
+template <int FMT, int MT>
+hipError_t launch_rk(const GemmParams& p, hipStream_t s, const char** name) {
+  const int64_t ntiles = (p.N + 63) / 64;
+  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
+  const int64_t grid = ntiles * mblocks;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  *name = FMT == kNV ? (MT == 1 ? "resident_nvfp4_m16" : "resident_nvfp4_m32")
+                     : (MT == 1 ? "resident_mxfp4_m16" : "resident_mxfp4_m32");
+  const size_t lds = (size_t)rk_lds_bytes(FMT, MT, p.K);
+  hipLaunchKernelGGL((rk_gemm<FMT, MT>), dim3((unsigned)grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Direct streaming kernel (decode, fp4 activations, K a multiple of 128): 64 weight
+// rows per workgroup, 16 per wave over the full K, no LDS and no barriers.  Each
+// wave loads its activation fragments straight from global memory next to the
+// weights (the 4 waves of a workgroup read the same activation bytes, which the
+// caches absorb); batches of 8 K-steps with the next batch in flight.
+// ---------------------------------------------------------------------------------
+template <int FMT, int MT>
+__global__ __launch_bounds__(256) void direct_gemm(GemmParams p) {
+  constexpr int G = FMT == kNV ? 16 : 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t ntiles = (p.N + 63) >> 6;
+  const int64_t mb = (int64_t)blockIdx.x / ntiles;
+  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
+  int grp = 0;
+  int64_t row0, row_end;
+  if (p.mblk_expert) {
+    grp = p.mblk_expert[mb];
+    if (grp < 0) return;  // uniform over the workgroup
+    row0 = p.mblk_row0[mb];
+    row_end = p.group_end[grp];
+  } else {
+    row0 = mb * (16 * MT);
+    row_end = p.M;
+  }
+  const int64_t K = p.K;
+  const int64_t KB = K >> 1;
+  const int64_t KS = K / G;
+  const int r = lane & 15;
+  const int gq = lane >> 4;
+  const int64_t wn_raw = nt * 64 + wave * 16 + r;
+  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;   // padded rows: outputs not stored
+  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
+  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
+  const uint8_t* arow[MT];
+  const uint8_t* asrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    int64_t pv = row0 + t * 16 + r;
+    if (pv >= row_end) pv = row_end - 1;
+    const int64_t src = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
+    arow[t] = p.a_codes + src * KB;
+    asrow[t] = p.a_scales + src * KS;
+  }
+  const int64_t nsteps = K / kKStep;
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  SplitBatch<FMT, MT> bA, bB;
+  split_load<FMT, MT>(bA, wrow, wsrow, arow, asrow, 0, nsteps, gq);
+  for (int64_t s = 0; s < nsteps; s += 2 * kBatch) {
+    const int64_t s1 = s + kBatch;
+    split_load<FMT, MT>(bB, wrow, wsrow, arow, asrow, s1 < nsteps ? s1 : s, nsteps, gq);
+    __builtin_amdgcn_sched_barrier(0);
+    split_compute<FMT, MT>(bA, (int)((nsteps - s) < kBatch ? (nsteps - s) : kBatch), acc);
+    if (s1 >= nsteps) break;
+    const int64_t s2 = s1 + kBatch;
+    split_load<FMT, MT>(bA, wrow, wsrow, arow, asrow, s2 < nsteps ? s2 : s1, nsteps, gq);
+    __builtin_amdgcn_sched_barrier(0);
+    split_compute<FMT, MT>(bB, (int)((nsteps - s1) < kBatch ? (nsteps - s1) : kBatch), acc);
+  }
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = row0 + t * 16 + (lane & 15);
+    if (m >= row_end) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t n = nt * 64 + wave * 16 + 4 * (lane >> 4) + v;
+      if (n >= p.N) continue;
+      const float x = acc[t][v] * alpha;
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
+      else
+        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
+    }
+  }
+}
+
+template <int FMT, int MT>
+hipError_t launch_direct(const GemmParams& p, hipStream_t s, const char** name) {
+  const int64_t ntiles = (p.N + 63) / 64;
+  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
+  const int64_t grid = ntiles * mblocks;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  *name = FMT == kNV ? (MT == 1 ? "direct_nvfp4_m16" : "direct_nvfp4_m32")
+                     : (MT == 1 ? "direct_mxfp4_m16" : "direct_mxfp4_m32");
+  hipLaunchKernelGGL((direct_gemm<FMT, MT>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int FMT, int AK, int MT>
 hipError_t launch_rowblock(const GemmParams& p, hipStream_t s, const char** name) {
   const int64_t ntiles = (p.N + 15) / 16;
@@ -284,6 +1302,31 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   // rows use one tile
   const bool one = !p.mblk_expert && p.M <= 16;
   if (p.mblk_expert && p.bm != 32) return hipErrorInvalidValue;
+  // fp4 activations with K a multiple of 128 take the streaming kernel
+  const bool fast = akind == kA_FP4 && p.K % kKStep == 0;
+  // measurement switch between the fp4-activation kernels (default: stream)
+  const char* sel = getenv("FP4_GEMM_KERNEL");
+  const char c0 = (fast && sel) ? sel[0] : 0, c1 = c0 ? sel[1] : 0;
+  if (fast) {
+    if (c0 == 's' && c1 == 'p') {
+      if (fmt == kNV) return one ? launch_splitk<kNV, 1>(p, s, name) : launch_splitk<kNV, 2>(p, s, name);
+      return one ? launch_splitk<kMX, 1>(p, s, name) : launch_splitk<kMX, 2>(p, s, name);
+    }
+    if (c0 == 'w') {
+      if (fmt == kNV) return one ? launch_wide<kNV, 1>(p, s, name) : launch_wide<kNV, 2>(p, s, name);
+      return one ? launch_wide<kMX, 1>(p, s, name) : launch_wide<kMX, 2>(p, s, name);
+    }
+    if (c0 == 'r' && rk_lds_bytes(fmt, one ? 1 : 2, p.K) <= kRkMaxLds) {
+      if (fmt == kNV) return one ? launch_rk<kNV, 1>(p, s, name) : launch_rk<kNV, 2>(p, s, name);
+      return one ? launch_rk<kMX, 1>(p, s, name) : launch_rk<kMX, 2>(p, s, name);
+    }
+    if (c0 == 'd') {
+      if (fmt == kNV) return one ? launch_direct<kNV, 1>(p, s, name) : launch_direct<kNV, 2>(p, s, name);
+      return one ? launch_direct<kMX, 1>(p, s, name) : launch_direct<kMX, 2>(p, s, name);
+    }
+    if (fmt == kNV) return one ? launch_stream<kNV, 1>(p, s, name) : launch_stream<kNV, 2>(p, s, name);
+    return one ? launch_stream<kMX, 1>(p, s, name) : launch_stream<kMX, 2>(p, s, name);
+  }
   if (fmt == kNV) {
     if (akind == kA_FP4)
       return one ? launch_rowblock<kNV, kA_FP4, 1>(p, s, name) : launch_rowblock<kNV, kA_FP4, 2>(p, s, name);
