@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the block-scaled FP4 hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|moe-nvfp4|moe-mxfp4]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode|prefill|prefill-mxfp4|moe-nvfp4|moe-mxfp4]
 
 Default workload (decode): MXFP4 W4A4 GEMM, N=14336, K=4096, activations
 [32, 4096] bf16 N(0,1) with 1% x20 outliers quantized on the fly.  One step = the
@@ -13,6 +14,7 @@ same way and reported under "per_m".
 
 Other workloads (one JSON line each, not the default):
   prefill    NVFP4 W4A4 GEMM M=8192 N=4096 K=4096, fused quantization, bf16 out
+  prefill-mxfp4  the same GEMM in MXFP4
   moe-nvfp4  NVFP4 MoE, 128 experts top-8, hidden 2048, intermediate 768, T=--tokens
   moe-mxfp4  MXFP4 MoE, 256 experts top-8 + shared, hidden 6144, intermediate 2048,
              Zipf(1.1) routing, T=--tokens
@@ -37,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp4": 10100.0, "fp8": 5000.0}
-KERNEL_SOURCES = ["gemm.hip", "quant.hip", "moe.hip", "device.h", "internal.h"]
+KERNEL_SOURCES = ["gemm.hip", "gemm_tile.hip", "quant.hip", "moe.hip", "device.h", "internal.h"]
 
 
 def parse():
@@ -46,7 +48,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "moe-nvfp4", "moe-mxfp4"])
+                   choices=["decode", "prefill", "prefill-mxfp4", "moe-nvfp4", "moe-mxfp4"])
     p.add_argument("--tokens", type=int, default=None, help="MoE token count")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
@@ -199,31 +201,33 @@ def bench_decode(args, torch, F):
     return res
 
 
-def bench_prefill(args, torch, F):
+def bench_prefill(args, torch, F, fmt="nvfp4"):
     import numpy as np
     import synth
     dev = torch.device("cuda:0")
     M, N, K = 8192, 4096, 4096
+    nv = fmt == "nvfp4"
+    fm, G = (F.FP4_NVFP4, 16) if nv else (F.FP4_MXFP4, 32)
     w = synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT)
-    ws2 = float(np.float32(np.abs(w).max()) / np.float32(2688.0))
+    ws2 = float(np.float32(np.abs(w).max()) / np.float32(2688.0)) if nv else 1.0
     wd = torch.from_numpy(w).to(dev)
     wc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    wsc = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
-    F.fp4_quantize_weight(F.FP4_NVFP4, wd, N, K, K, ws2, wc, wsc)
+    wsc = torch.empty((N, K // G), dtype=torch.uint8, device=dev)
+    F.fp4_quantize_weight(fm, wd, N, K, K, ws2, wc, wsc)
     del wd
     bits, av = synth.bf16_bits(synth.normal((M, K), seed=0, role=synth.ACT, index=3))
-    s = float(np.float32(np.abs(av).max()) / np.float32(2688.0))
+    s = float(np.float32(np.abs(av).max()) / np.float32(2688.0)) if nv else 1.0
     a = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // G), dtype=torch.uint8, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     names = {}
 
     def quant(i):
-        F.fp4_quantize_act(F.FP4_NVFP4, a, M, K, K, s, codes, scales)
+        F.fp4_quantize_act(fm, a, M, K, K, s, codes, scales)
 
     def gemm(i):
-        F.fp4_gemm(F.FP4_NVFP4, F.FP4_W4A4, M, N, K, None, 0, codes, scales, wc, wsc, ws2, s,
+        F.fp4_gemm(fm, F.FP4_W4A4, M, N, K, None, 0, codes, scales, wc, wsc, ws2, s,
                    out, N, F.FP4_OUT_BF16, 0, None, 0)
         names["gemm"] = F.fp4_last_kernel()
 
@@ -236,17 +240,20 @@ def bench_prefill(args, torch, F):
     kms, _ = timed_graph(torch, gemm, steps, 2)
     flops = 2.0 * M * N * K
     tf = flops / (kms * 1e-3) / 1e12
+    # NVFP4 runs its products on fp16 MFMAs (exact decode), MXFP4 on the scaled FP4 MFMA
+    pk = PEAK_TFLOPS["fp16"] if nv else PEAK_TFLOPS["fp4"]
+    F_ = fmt.upper()
     return {
-        "metric": "FP4 prefill GEMM TFLOP/s (NVFP4 W4A4, M=8192, N=4096, K=4096)",
+        "metric": f"FP4 prefill GEMM TFLOP/s ({F_} W4A4, M=8192, N=4096, K=4096)",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": ms,
         "steps_override": steps,
-        "dtype": "fp16",
-        "config": {"workload": "NVFP4 W4A4 prefill GEMM, fused activation quant, bf16 out",
+        "dtype": "fp16" if nv else "fp4",
+        "config": {"workload": f"{F_} W4A4 prefill GEMM, fused activation quant, bf16 out",
                    "M": M, "N": N, "K": K},
-        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS["fp16"],
-                     "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS["fp16"], 4),
-                     "frac_of_fp8_peak": round(tf / PEAK_TFLOPS["fp8"], 4),
-                     "traffic": stored_traffic("prefill_gemm"), "kernel": names.get("gemm"),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": pk,
+                     "unit": "TFLOP/s", "frac": round(tf / pk, 4),
+                     "frac_of_fp4_peak": round(tf / PEAK_TFLOPS["fp4"], 4),
+                     "traffic": stored_traffic("prefill_gemm_" + fmt), "kernel": names.get("gemm"),
                      "avg_launch_us": round(kms * 1e3, 2)},
         "wall_s_timed": wall,
     }
@@ -417,8 +424,8 @@ def main():
     if args.workload == "decode":
         res = bench_decode(args, torch, F)
         steps = args.steps
-    elif args.workload == "prefill":
-        res = bench_prefill(args, torch, F)
+    elif args.workload in ("prefill", "prefill-mxfp4"):
+        res = bench_prefill(args, torch, F, "nvfp4" if args.workload == "prefill" else "mxfp4")
         steps = res.pop("steps_override")
     else:
         res = bench_moe(args, torch, F, args.workload.split("-")[1])

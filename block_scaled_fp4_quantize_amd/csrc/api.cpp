@@ -91,7 +91,8 @@ void moe_plan(const fp4_moe_args* a, bool w4a4, bool may_w4a16, MoePlan* pl) {
   const int64_t P = a->T * a->k;
   const bool sh = moe_shared(a);
   const int64_t R = P + (sh ? a->T : 0);
-  const int bm = fp4::gemm_block_rows(a->fmt, w4a4 ? fp4::kA_FP4 : fp4::kA_BF16, P);
+  const int bm = fp4::gemm_block_rows(a->fmt, w4a4 ? fp4::kA_FP4 : fp4::kA_BF16,
+                                      a->E > 0 ? P / a->E : P, a->H, a->I);
   const int64_t nmb = (P + bm - 1) / bm + a->E;
   size_t off = 0;
   auto take = [&](size_t bytes) {

@@ -19,6 +19,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -122,6 +123,16 @@ __device__ __forceinline__ bf16x8 decode8_bf16(uint32_t packed, float scale) {
   bf16x8 r;
   __builtin_memcpy(&r, w, 16);
   return r;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& q, int j) {
+  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+}
+
+// An e4m3 block-scale value as a packed fp16 pair (exact: e4m3 values are fp16 numbers).
+__device__ __forceinline__ f16x2 f16_pair(float v) {
+  const _Float16 h = (_Float16)v;
+  return f16x2{h, h};
 }
 
 __device__ __forceinline__ bf16x8 bits_to_bf16x8(uint4 v) {

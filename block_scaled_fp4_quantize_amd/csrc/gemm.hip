@@ -82,9 +82,6 @@ __device__ __forceinline__ void load_bf16x32(const uint16_t* row, int64_t k0, in
   }
 }
 
-__device__ __forceinline__ uint32_t dword_of(const uint4& q, int j) {
-  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-}
 
 // Block scale of sub-step `sub` (8 elements) of a lane's 32-element chunk.
 template <int FMT>
@@ -93,10 +90,6 @@ __device__ __forceinline__ float scale_value(uint32_t sb, int sub) {
   return e4m3_value_pos((sb >> (8 * (sub >> 1))) & 0xFFu);
 }
 
-__device__ __forceinline__ f16x2 f16_pair(float v) {
-  const _Float16 h = (_Float16)v;  // exact: e4m3 values are fp16 numbers
-  return f16x2{h, h};
-}
 
 // FMT: kNV / kMX.  AK: kA_FP4 (activation codes) / kA_BF16.  MT: 16-row
 // activation tiles per workgroup.  GEN: K not a multiple of 128 (byte loads).
@@ -1294,19 +1287,28 @@ hipError_t launch_rowblock(const GemmParams& p, hipStream_t s, const char** name
 
 }  // namespace
 
-int gemm_block_rows(int /*fmt*/, int /*akind*/, int64_t /*M_hint*/) { return 32; }
+int gemm_block_rows(int /*fmt*/, int akind, int64_t rows_per_group, int64_t H, int64_t I) {
+  const bool tiled = akind == kA_FP4 && H % kKStep == 0 && I % kKStep == 0;
+  return (tiled && rows_per_group >= 48) ? 128 : 32;
+}
 
 hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
                        const char** name) {
   // row blocks of 32 (two 16-row activation tiles); dense problems of at most 16
   // rows use one tile
   const bool one = !p.mblk_expert && p.M <= 16;
-  if (p.mblk_expert && p.bm != 32) return hipErrorInvalidValue;
-  // fp4 activations with K a multiple of 128 take the streaming kernel
+  // fp4 activations with K a multiple of 128 take the streaming kernel, or the
+  // LDS-tiled one when there are many activation rows
   const bool fast = akind == kA_FP4 && p.K % kKStep == 0;
+  if (p.mblk_expert && p.bm != 32) {
+    if (p.bm != 128 || !fast) return hipErrorInvalidValue;
+    return launch_gemm_tiled(fmt, 128, p, s, name);
+  }
   // measurement switch between the fp4-activation kernels (default: stream)
   const char* sel = getenv("FP4_GEMM_KERNEL");
   const char c0 = (fast && sel) ? sel[0] : 0, c1 = c0 ? sel[1] : 0;
+  if (fast && !sel && !p.mblk_expert && p.M > 64)
+    return launch_gemm_tiled(fmt, p.M >= 192 ? 256 : 128, p, s, name);
   if (fast) {
     if (c0 == 's' && c1 == 'p') {
       if (fmt == kNV) return one ? launch_splitk<kNV, 1>(p, s, name) : launch_splitk<kNV, 2>(p, s, name);

@@ -50,10 +50,14 @@ struct GemmParams {
   int out_f32;
 };
 enum AKind : int { kA_FP4 = 0, kA_BF16 = 1 };
-// Row-block height the launcher will use for a problem of this shape.
-int gemm_block_rows(int fmt, int akind, int64_t M_hint);
+// Row-block height of the block table for grouped (MoE) GEMMs of these shapes
+// (GEMM1 has K = H, GEMM2 has K = I); launch_gemm picks its kernel from it.
+int gemm_block_rows(int fmt, int akind, int64_t rows_per_group, int64_t H, int64_t I);
 hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
                        const char** name);
+// tiled kernel for many activation rows (fp4 activations, K % 128 == 0), bm 128 or 256
+hipError_t launch_gemm_tiled(int fmt, int bm, const GemmParams& p, hipStream_t s,
+                             const char** name);
 
 // ---- MoE stages ------------------------------------------------------------------
 hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,

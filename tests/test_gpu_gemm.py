@@ -117,6 +117,50 @@ def test_mxfp4_w4a4_decode_full_size(decode_problem, M):
                what=f"decode M={M}")
 
 
+# more than 64 activation rows and K % 128 == 0: the LDS-tiled kernel (128-row
+# tiles below 192 rows, 256-row MXFP4 tiles from 192), with ragged rows and columns
+TILED = [(65, 40, 128), (130, 256, 1024), (200, 300, 512), (257, 513, 384), (64 + 128 + 1, 17, 256)]
+
+
+@pytest.mark.parametrize("shape", TILED)
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_tiled_shapes(fmt, shape):
+    M, N, K = shape
+    run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape))
+    name = F.fp4_last_kernel()
+    assert name.startswith("tile_" + fmt), name
+    if fmt == "mxfp4":
+        assert name.endswith("m256" if M >= 192 else "m128"), name
+    run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32,
+                  prequant=True)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_tiled_strided_output_canaries(fmt):
+    # output rows with a stride that is not a multiple of 4 take the scalar stores;
+    # the padding columns and the row after the output stay untouched
+    M, N, K = 150, 70, 256
+    wc, ws, ws2, ad, av, s = problem(fmt, M, N, K, 21)
+    wcd, wsd = to_dev(wc), to_dev(ws)
+    ref, _ = T.gemm(fmt, "w4a4", wcd, wsd, a_bf16=ad, weight_scale_2=ws2, input_scale=s)
+    big = torch.full((M + 1, N + 3), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = big[:M, :N]
+    _, st = T.gemm(fmt, "w4a4", wcd, wsd, a_bf16=ad, weight_scale_2=ws2, input_scale=s, out=out)
+    torch.cuda.synchronize()
+    assert st == F.FP4_OK
+    assert F.fp4_last_kernel().startswith("tile_")
+    assert torch.equal(out, ref)
+    assert (big[M] == -7.0).all() and (big[:, N:] == -7.0).all()
+
+
+def test_mxfp4_w4a4_prefill_full_size_sampled_rows():
+    # MXFP4 at the prefill shape, 256-row tiles; 64 sampled rows incl. first and last
+    fmt, M, N, K = "mxfp4", 8192, 4096, 4096
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 62, replace=False)])
+    run_and_check(fmt, "w4a4", M, N, K, seed=1, rows=np.sort(rows))
+
+
 def test_nvfp4_w4a4_prefill_full_size_sampled_rows():
     # [8192, 4096] x [4096, 4096]^T, fused quantization, bf16 out; the oracle checks
     # 96 sampled rows (rows are independent) including the first and last

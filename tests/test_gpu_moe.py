@@ -276,6 +276,10 @@ SMALL = [
     ("nvfp4", "w4a4", dict(T=40, H=256, I=96, E=16, k=4, shared=False)),
     ("mxfp4", "w4a4", dict(T=33, H=256, I=96, E=16, k=4, shared=True)),
     ("nvfp4", "w4a4", dict(T=1, H=64, I=48, E=4, k=1, shared=False)),
+    # >= 48 routed rows per expert on average, H and I multiples of 128: the grouped
+    # GEMMs run on 128-row tiles, with ragged expert row counts
+    ("nvfp4", "w4a4", dict(T=150, H=256, I=128, E=4, k=2, shared=True)),
+    ("mxfp4", "w4a4", dict(T=200, H=384, I=256, E=6, k=3, shared=True)),
 ]
 
 
