@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=None, help="MoE token count")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="first run a plain 256 MiB device copy (for counter scaling)")
+                   help="first run a plain elementwise kernel over 256 MiB (counter scaling)")
     return p.parse_args()
 
 
@@ -416,11 +416,14 @@ def main():
         sys.exit(1)
     import block_scaled_fp4_quantize_amd as F   # raises if libfp4.so is missing
     if args.copy_calibration:
-        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
+        # a plain elementwise kernel that reads 256 MiB and writes 256 MiB: the
+        # counter scale for FETCH_SIZE / WRITE_SIZE of the kernels measured after it
+        src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
+        del src, dst
     if args.workload == "decode":
         res = bench_decode(args, torch, F)
         steps = args.steps
