@@ -39,7 +39,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp4": 10100.0, "fp8": 5000.0}
-KERNEL_SOURCES = ["gemm.hip", "gemm_tile.hip", "quant.hip", "moe.hip", "device.h", "internal.h"]
+KERNEL_SOURCES = ["gemm.hip", "gemm_tile.hip", "gemm_resident.hip", "quant.hip", "moe.hip", "device.h",
+                  "internal.h"]
 
 
 def parse():

@@ -43,7 +43,7 @@ EXPORTED = [
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m block_scaled_fp4_quantize_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python block_scaled_fp4_quantize_amd/build.py` "
         "(there is no fallback implementation)")
 
 # torch (the device-memory and stream plumbing) ships its own HIP runtime under

@@ -1,6 +1,6 @@
 """Build libfp4.so (the gfx950 HIP kernels + C ABI) in place with hipcc.
 
-    python -m block_scaled_fp4_quantize_amd.build
+    python block_scaled_fp4_quantize_amd/build.py
 
 Every source is compiled for gfx950 only.  Packed fp32 VALU instructions are
 disabled for the device code (``-packed-fp32-ops``); the host pass warns that it
@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["quant.hip", "gemm.hip", "gemm_tile.hip", "moe.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_tile.hip", "gemm_resident.hip", "moe.hip", "api.cpp"]
 
 DEVICE_FLAGS = [
     "--offload-arch=gfx950",

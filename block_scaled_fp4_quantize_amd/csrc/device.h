@@ -62,9 +62,12 @@ __device__ __forceinline__ uint32_t e4m3_code_pos(float sf) {
 
 // Value of a non-negative e4m3fn code (0..0x7E).
 __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
-  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  // both forms computed and selected: a branch here would split every MFMA loop
+  // that decodes scales into exec-masked pieces
+  const float sub = (float)m * 0.001953125f;                         // m * 2^-9
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
 }
 
 // Value 2^(c-127) of an e8m0 code (c = 0 gives the fp32 subnormal 2^-127).

@@ -98,7 +98,7 @@ template <int FMT, int AK, int MT, bool GEN, int U>
 __global__ __launch_bounds__(256) void rowblock_gemm(GemmParams p) {
   constexpr int G = FMT == kNV ? 16 : 32;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int64_t ntiles = (p.N + 15) >> 4;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int64_t ntiles = (p.N + 63) >> 6;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
@@ -638,7 +638,7 @@ template <int FMT, int MT>
 __global__ __launch_bounds__(256) void splitk_gemm(GemmParams p) {
   constexpr int G = FMT == kNV ? 16 : 32;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int64_t ntiles = (p.N + 15) >> 4;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
@@ -769,7 +769,7 @@ __global__ __launch_bounds__(256) void wide_gemm(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int64_t ntiles = (p.N + 63) >> 6;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
@@ -941,238 +941,6 @@ hipError_t launch_wide(const GemmParams& p, hipStream_t s, const char** name) {
 }
 
 // ---------------------------------------------------------------------------------
-// Resident-activation streaming kernel (decode and small expert batches, fp4
-// activations, K a multiple of 128, activations for the full K fitting in LDS).
-// A workgroup owns 64 weight rows (16 per wave, full K) and 16*MT activation rows.
-// The activation codes and scales for the whole K are staged in LDS once, behind a
-// single barrier; after that every wave streams its weight rows in a barrier-free
-// loop of 8-step batches with the next batch's loads in flight (two register
-// buffers used in turn).  The first weight batch is requested before the staging,
-// so its latency overlaps it.
-// ---------------------------------------------------------------------------------
-template <int FMT>
-__device__ __forceinline__ void rk_w_load(const uint8_t* wrow, const uint8_t* wsrow, int64_t s0,
-                                          int64_t nsteps, int gq, uint4 (&q)[kBatch],
-                                          uint32_t (&sc)[kBatch]) {
-#pragma unroll
-  for (int j = 0; j < kBatch; ++j) {
-    int64_t st = s0 + j;
-    if (st >= nsteps) st = nsteps - 1;      // clamped: not computed
-    const int64_t k0 = st * kKStep + gq * 32;
-    q[j] = *reinterpret_cast<const uint4*>(wrow + (k0 >> 1));
-    if (FMT == kMX)
-      sc[j] = wsrow[k0 >> 5];
-    else
-      sc[j] = *reinterpret_cast<const uint16_t*>(wsrow + (k0 >> 4));
-  }
-}
-
-template <int FMT, int MT>
-__device__ __forceinline__ void rk_compute(const uint8_t* a_lds, const uint8_t* s_lds, int astr,
-                                           int sstr, int64_t s0, int64_t nsteps, int r, int gq,
-                                           const uint4 (&q)[kBatch], const uint32_t (&sc)[kBatch],
-                                           v4f (&acc)[MT]) {
-#pragma unroll
-  for (int j = 0; j < kBatch; ++j) {
-    const int64_t st = s0 + j;
-    const uint32_t keep = st < nsteps ? 0xFFFFFFFFu : 0u;   // zero operand past K (no branch)
-    const int64_t stc = st < nsteps ? st : nsteps - 1;
-    const uint4 wj = make_uint4(q[j].x & keep, q[j].y & keep, q[j].z & keep, q[j].w & keep);
-    const int kbyte = (int)(stc * 64) + gq * 16;            // code byte offset in a staged row
-    if (FMT == kMX) {
-      const int kscale = (int)(stc * 4) + gq;
-      const v8i wop = {(int)wj.x, (int)wj.y, (int)wj.z, (int)wj.w, 0, 0, 0, 0};
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int ar = t * 16 + r;
-        const uint4 aq = *reinterpret_cast<const uint4*>(a_lds + ar * astr + kbyte);
-        const uint32_t asb = s_lds[ar * sstr + kscale];
-        const v8i aop = {(int)aq.x, (int)aq.y, (int)aq.z, (int)aq.w, 0, 0, 0, 0};
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop, aop, acc[t], 4, 4, 0,
-                                                                   (int)sc[j], 0, (int)asb);
-      }
-    } else {
-      const int kscale = (int)(stc * 8) + gq * 2;
-      const f16x2 ws_lo = f16_pair(e4m3_value_pos(sc[j] & 0xFFu));
-      const f16x2 ws_hi = f16_pair(e4m3_value_pos((sc[j] >> 8) & 0xFFu));
-      uint4 aq[MT];
-      f16x2 as_lo[MT], as_hi[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int ar = t * 16 + r;
-        aq[t] = *reinterpret_cast<const uint4*>(a_lds + ar * astr + kbyte);
-        const uint32_t asb = *reinterpret_cast<const uint16_t*>(s_lds + ar * sstr + kscale);
-        as_lo[t] = f16_pair(e4m3_value_pos(asb & 0xFFu));
-        as_hi[t] = f16_pair(e4m3_value_pos(asb >> 8));
-      }
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const f16x8 wop = decode8_f16(dword_of(wj, sub), sub < 2 ? ws_lo : ws_hi);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const f16x8 aop = decode8_f16(dword_of(aq[t], sub), sub < 2 ? as_lo[t] : as_hi[t]);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t], 0, 0, 0);
-        }
-      }
-    }
-  }
-}
-
-// LDS bytes the resident kernel needs: staged code rows (padded) + scale rows
-inline int64_t rk_lds_bytes(int fmt, int mt, int64_t K) {
-  const int64_t G = fmt == kNV ? 16 : 32;
-  return 16 * mt * ((K / 2 + 16) + K / G);
-}
-constexpr int64_t kRkMaxLds = 120 * 1024;
-
-template <int FMT, int MT>
-__global__ __launch_bounds__(256) void rk_gemm(GemmParams p) {
-  constexpr int G = FMT == kNV ? 16 : 32;
-  constexpr int AROWS = 16 * MT;
-  extern __shared__ __attribute__((aligned(16))) uint8_t rk_smem[];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t ntiles = (p.N + 63) >> 6;
-  const int64_t mb = (int64_t)blockIdx.x / ntiles;
-  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
-  int grp = 0;
-  int64_t row0, row_end;
-  if (p.mblk_expert) {
-    grp = p.mblk_expert[mb];
-    if (grp < 0) return;  // uniform over the workgroup
-    row0 = p.mblk_row0[mb];
-    row_end = p.group_end[grp];
-  } else {
-    row0 = mb * AROWS;
-    row_end = p.M;
-  }
-  const int64_t K = p.K;
-  const int64_t KB = K >> 1;
-  const int64_t KS = K / G;
-  const int astr = (int)KB + 16;          // padded row stride (bank spread)
-  const int sstr = (int)KS;
-  uint8_t* a_lds = rk_smem;
-  uint8_t* s_lds = rk_smem + AROWS * astr;
-
-  const int r = lane & 15;
-  const int gq = lane >> 4;
-  const int64_t wn_raw = nt * 64 + wave * 16 + r;
-  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;   // padded rows: outputs not stored
-  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
-  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
-  const int64_t nsteps = K / kKStep;
-
-  // first weight batch in flight before the staging
-  uint4 qA[kBatch], qB[kBatch];
-  uint32_t sA[kBatch], sB[kBatch];
-  rk_w_load<FMT>(wrow, wsrow, 0, nsteps, gq, qA, sA);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // source row of each staged activation row (gathered once; padded rows repeat
-  // the last valid row)
-  __shared__ int64_t rk_src[AROWS];
-  if (tid < AROWS) {
-    int64_t pv = row0 + tid;
-    if (pv >= row_end) pv = row_end - 1;
-    rk_src[tid] = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
-  }
-  __syncthreads();
-  // stage the activation rows for the full K: codes in 16-byte pieces, scales in
-  // 4-byte pieces (KB is a multiple of 64, KS of 4), 8 loads per thread issued
-  // before their LDS stores
-  {
-    const int64_t cpr = KB / 16;                      // code pieces per row
-    const int64_t pieces = AROWS * cpr;
-    for (int64_t base = 0; base < pieces; base += 256 * 8) {
-      uint4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        int64_t i = base + u * 256 + tid;
-        if (i >= pieces) i = pieces - 1;              // clamped load, store skipped below
-        const int row = (int)(i / cpr);
-        v[u] = *reinterpret_cast<const uint4*>(p.a_codes + rk_src[row] * KB + (i - (int64_t)row * cpr) * 16);
-      }
-      __builtin_amdgcn_sched_barrier(0);   // the group's loads go out before its stores
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = base + u * 256 + tid;
-        if (i < pieces) {
-          const int row = (int)(i / cpr);
-          *reinterpret_cast<uint4*>(a_lds + row * astr + (i - (int64_t)row * cpr) * 16) = v[u];
-        }
-      }
-    }
-    const int64_t spr = KS / 4;                       // scale pieces per row
-    const int64_t spieces = AROWS * spr;
-    for (int64_t base = 0; base < spieces; base += 256 * 8) {
-      uint32_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        int64_t i = base + u * 256 + tid;
-        if (i >= spieces) i = spieces - 1;
-        const int row = (int)(i / spr);
-        v[u] = *reinterpret_cast<const uint32_t*>(p.a_scales + rk_src[row] * KS + (i - (int64_t)row * spr) * 4);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = base + u * 256 + tid;
-        if (i < spieces) {
-          const int row = (int)(i / spr);
-          *reinterpret_cast<uint32_t*>(s_lds + row * sstr + (i - (int64_t)row * spr) * 4) = v[u];
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  v4f acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int64_t s0 = 0; s0 < nsteps; s0 += 2 * kBatch) {
-    // batch s0 from qA (prefetch s0 + 8 into qB), then batch s0 + 8 from qB
-    // (prefetch s0 + 16 into qA); clamped prefetches past K re-read the last step
-    rk_w_load<FMT>(wrow, wsrow, s0 + kBatch, nsteps, gq, qB, sB);
-    rk_compute<FMT, MT>(a_lds, s_lds, astr, sstr, s0, nsteps, r, gq, qA, sA, acc);
-    if (s0 + kBatch >= nsteps) break;
-    rk_w_load<FMT>(wrow, wsrow, s0 + 2 * kBatch, nsteps, gq, qA, sA);
-    rk_compute<FMT, MT>(a_lds, s_lds, astr, sstr, s0 + kBatch, nsteps, r, gq, qB, sB, acc);
-  }
-
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int64_t m = row0 + t * 16 + (lane & 15);
-    if (m >= row_end) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t n = nt * 64 + wave * 16 + 4 * (lane >> 4) + v;
-      if (n >= p.N) continue;
-      const float x = acc[t][v] * alpha;
-      if (p.out_f32)
-        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
-    }
-  }
-}
-
-template <int FMT, int MT>
-hipError_t launch_rk(const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ntiles = (p.N + 63) / 64;
-  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
-  const int64_t grid = ntiles * mblocks;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  *name = FMT == kNV ? (MT == 1 ? "resident_nvfp4_m16" : "resident_nvfp4_m32")
-                     : (MT == 1 ? "resident_mxfp4_m16" : "resident_mxfp4_m32");
-  const size_t lds = (size_t)rk_lds_bytes(FMT, MT, p.K);
-  hipLaunchKernelGGL((rk_gemm<FMT, MT>), dim3((unsigned)grid), dim3(256), lds, s, p);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------------
 // Direct streaming kernel (decode, fp4 activations, K a multiple of 128): 64 weight
 // rows per workgroup, 16 per wave over the full K, no LDS and no barriers.  Each
 // wave loads its activation fragments straight from global memory next to the
@@ -1183,7 +951,7 @@ template <int FMT, int MT>
 __global__ __launch_bounds__(256) void direct_gemm(GemmParams p) {
   constexpr int G = FMT == kNV ? 16 : 32;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int64_t ntiles = (p.N + 63) >> 6;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
@@ -1309,6 +1077,12 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   const char c0 = (fast && sel) ? sel[0] : 0, c1 = c0 ? sel[1] : 0;
   if (fast && !sel && !p.mblk_expert && p.M > 64)
     return launch_gemm_tiled(fmt, p.M >= 192 ? 256 : 128, p, s, name);
+  // at most 16 rows (one 16-row activation tile): activations resident in LDS with
+  // a deep weight stream, when they fit; two-tile blocks measure faster on the
+  // streaming kernel below
+  if (fast && (!sel || c0 == 'r') && (one || c0 == 'r') &&
+      resident_fits(fmt, one ? 1 : 2, p.K))
+    return launch_gemm_resident(fmt, one ? 1 : 2, p, s, name);
   if (fast) {
     if (c0 == 's' && c1 == 'p') {
       if (fmt == kNV) return one ? launch_splitk<kNV, 1>(p, s, name) : launch_splitk<kNV, 2>(p, s, name);
@@ -1317,10 +1091,6 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
     if (c0 == 'w') {
       if (fmt == kNV) return one ? launch_wide<kNV, 1>(p, s, name) : launch_wide<kNV, 2>(p, s, name);
       return one ? launch_wide<kMX, 1>(p, s, name) : launch_wide<kMX, 2>(p, s, name);
-    }
-    if (c0 == 'r' && rk_lds_bytes(fmt, one ? 1 : 2, p.K) <= kRkMaxLds) {
-      if (fmt == kNV) return one ? launch_rk<kNV, 1>(p, s, name) : launch_rk<kNV, 2>(p, s, name);
-      return one ? launch_rk<kMX, 1>(p, s, name) : launch_rk<kMX, 2>(p, s, name);
     }
     if (c0 == 'd') {
       if (fmt == kNV) return one ? launch_direct<kNV, 1>(p, s, name) : launch_direct<kNV, 2>(p, s, name);

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void tile_gemm(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave & 1;
   const int wn = wave >> 1;
   const int64_t ntiles = (p.N + kTBN - 1) / kTBN;

@@ -55,6 +55,13 @@ enum AKind : int { kA_FP4 = 0, kA_BF16 = 1 };
 int gemm_block_rows(int fmt, int akind, int64_t rows_per_group, int64_t H, int64_t I);
 hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
                        const char** name);
+// decode kernel with the activations resident in LDS (fp4 activations, 16*mt rows
+// per workgroup); usable when resident_fits()
+constexpr int64_t kResidentMaxLds = 160 * 1024;
+int64_t resident_lds_bytes(int fmt, int mt, int64_t K);
+bool resident_fits(int fmt, int mt, int64_t K);
+hipError_t launch_gemm_resident(int fmt, int mt, const GemmParams& p, hipStream_t s,
+                                const char** name);
 // tiled kernel for many activation rows (fp4 activations, K % 128 == 0), bm 128 or 256
 hipError_t launch_gemm_tiled(int fmt, int bm, const GemmParams& p, hipStream_t s,
                              const char** name);

@@ -135,6 +135,37 @@ def test_tiled_shapes(fmt, shape):
                   prequant=True)
 
 
+# at most 64 activation rows: the resident-activation kernel whenever the scale rows
+# are whole 16-byte pieces and the activations fit in LDS (ring of 8, 16 or 32 K
+# steps; K = 6144 refills the ring once), otherwise the streaming kernel
+RESIDENT = [(1, 300, 6144), (16, 100, 2048), (17, 64, 768), (32, 520, 4096), (50, 70, 1536),
+            (64, 33, 512)]
+
+
+def resident_expected(fmt, M, K):
+    G = 16 if fmt == "nvfp4" else 32
+    if M > 16:
+        return False    # two-tile blocks take the streaming kernel
+    mt = 1
+    kb = lambda b: (b + 1023) // 1024 * 1024
+    lds = 16 * mt * K // 2 + kb(16 * mt * (K // G)) + kb(64 * (K // G))
+    return (K // G) % 16 == 0 and lds <= 160 * 1024
+
+
+@pytest.mark.parametrize("shape", RESIDENT)
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_resident_shapes(fmt, shape):
+    M, N, K = shape
+    run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 7)
+    name = F.fp4_last_kernel()
+    if resident_expected(fmt, M, K):
+        assert name == f"resident_{fmt}_m16", name
+    else:
+        assert name.startswith("stream_"), name
+    run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 8, out_dtype=torch.float32,
+                  prequant=True)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_tiled_strided_output_canaries(fmt):
     # output rows with a stride that is not a multiple of 4 take the scalar stores;
