@@ -74,6 +74,7 @@ struct MoePlan {
   size_t src_token;     // int32 [P]
   size_t mblk_expert;   // int32 [n_mblocks]
   size_t mblk_row0;     // int32 [n_mblocks]
+  size_t chunk_base;    // int32 [ceil(P / kPermuteChunk)][E]
   int64_t P, R;         // routed rows, routed + shared rows
   int64_t n_mblocks;
   int bm;
@@ -110,6 +111,8 @@ void moe_plan(const fp4_moe_args* a, bool w4a4, bool may_w4a16, MoePlan* pl) {
   pl->src_token = take(sizeof(int32_t) * (size_t)P);
   pl->mblk_expert = take(sizeof(int32_t) * (size_t)nmb);
   pl->mblk_row0 = take(sizeof(int32_t) * (size_t)nmb);
+  pl->chunk_base = take(sizeof(int32_t) * (size_t)((P + fp4::kPermuteChunk - 1) /
+                                                   fp4::kPermuteChunk) * (size_t)a->E);
   const int64_t x_rows = a->fmt == FP4_MXFP4 ? a->T : R;
   pl->L.x_rows = x_rows;
   pl->L.x_codes = take((size_t)x_rows * (size_t)(a->H / 2));
@@ -464,6 +467,7 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
     pp.mblk_expert = mblk_expert;
     pp.mblk_row0 = mblk_row0;
     pp.group_end = group_end;
+    pp.chunk_base = reinterpret_cast<int32_t*>(ws + pl.chunk_base);
     FP4_TRY(fp4::launch_permute(pp, s, &name));
   }
 

@@ -1076,7 +1076,7 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   const char* sel = getenv("FP4_GEMM_KERNEL");
   const char c0 = (fast && sel) ? sel[0] : 0, c1 = c0 ? sel[1] : 0;
   if (fast && !sel && !p.mblk_expert && p.M > 64)
-    return launch_gemm_tiled(fmt, p.M >= 192 ? 256 : 128, p, s, name);
+    return launch_gemm_tiled(fmt, 128, p, s, name);
   // at most 16 rows (one 16-row activation tile): activations resident in LDS with
   // a deep weight stream, when they fit; two-tile blocks measure faster on the
   // streaming kernel below

@@ -8,8 +8,8 @@
 // Technical Guide", §6.1 and §6.4 for the two block-scale formats).
 //
 // Tiling: a workgroup (4 waves, 2 x 2) owns 256 weight rows and BM activation rows
-// (BM = 256 for dense MXFP4 prefill; 128 for NVFP4 and for MoE experts, whose row
-// counts are smaller).
+// (BM = 128: MXFP4 runs two such workgroups per CU; a 256-row MXFP4 variant is
+// kept for callers that ask for it).
 // Each wave computes a 128 x BM/2 tile with 16x16 MFMAs (weights as the A operand,
 // so a lane ends up holding 4 consecutive output columns).  K advances in stages
 // of 128: the packed codes (64 bytes per row) and block scales of the BM + 256
@@ -71,8 +71,10 @@ __device__ __forceinline__ void stage_store(uint8_t* base, const u32x4 (&creg)[C
       *reinterpret_cast<uint32_t*>(base + C::CODE_BYTES + (tid + 256 * i) * 4) = sreg[i];
 }
 
+// MXFP4 128-row tiles fit in 256 registers, so two workgroups share a CU and one
+// computes while the other waits for its next stage (NVFP4 would spill).
 template <int FMT, int BM>
-__global__ __launch_bounds__(256) void tile_gemm(GemmParams p) {
+__global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_gemm(GemmParams p) {
   using C = TileCfg<FMT, BM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   const int tid = threadIdx.x;
@@ -288,8 +290,9 @@ hipError_t launch_gemm_tiled(int fmt, int bm, const GemmParams& p, hipStream_t s
   // NVFP4 runs on fp16 MFMAs (four per 128-deep stage where MXFP4 needs one), so
   // 128-row tiles already give it enough MFMA work per staged byte; 256-row NVFP4
   // tiles would also exceed the register file.
-  if (fmt == kNV) return launch_tile<kNV, 128>(p, s, name);
-  return bm == 256 ? launch_tile<kMX, 256>(p, s, name) : launch_tile<kMX, 128>(p, s, name);
+  if (fmt == kNV || bm != 256) return fmt == kNV ? launch_tile<kNV, 128>(p, s, name)
+                                                 : launch_tile<kMX, 128>(p, s, name);
+  return launch_tile<kMX, 256>(p, s, name);
 }
 
 }  // namespace fp4

@@ -86,7 +86,9 @@ struct PermuteParams {
   int32_t* mblk_expert;    // [n_mblocks]
   int32_t* mblk_row0;      // [n_mblocks]
   int32_t* group_end;      // [E]
+  int32_t* chunk_base;     // [ceil(T*k / kPermuteChunk)][E] scratch
 };
+constexpr int kPermuteChunk = 256;   // routed slots per histogram / scatter chunk
 hipError_t launch_permute(const PermuteParams& p, hipStream_t s, const char** name);
 
 struct SwigluParams {

@@ -111,27 +111,87 @@ __device__ int block_exclusive_scan(int x, int* buf) {
   return incl - x;
 }
 
-__global__ __launch_bounds__(kScanThreads) void permute_count_kernel(PermuteParams p) {
-  __shared__ int cnt[kScanThreads];
-  __shared__ int buf[kScanThreads];
-  __shared__ int total_mb;
+// ---- dispatch: stable counting sort over the flat slot index i = t*k + j -------
+// (1) per-chunk expert histograms; (2) one workgroup turns them into each chunk's
+// first position per expert, and builds the offsets and the row-block table;
+// (3) per chunk, slot i goes to base[chunk][e] + (number of earlier slots of the
+// chunk routed to e).  Positions follow i within every expert, as the stable
+// order requires.  Ids outside [0, E) are dropped (inverse -1).
+__global__ __launch_bounds__(kPermuteChunk) void permute_hist_kernel(PermuteParams p) {
+  __shared__ int cnt[1024];
   const int tid = threadIdx.x;
-  cnt[tid] = 0;
+  for (int e = tid; e < p.E; e += kPermuteChunk) cnt[e] = 0;
   __syncthreads();
   const int64_t n = p.T * p.k;
-  for (int64_t i = tid; i < n; i += kScanThreads) {
+  const int64_t i = (int64_t)blockIdx.x * kPermuteChunk + tid;
+  if (i < n) {
     const int e = p.ids[i];
-    if (e >= 0 && e < p.E) atomicAdd(&cnt[e], 1);  // ids outside [0, E) are dropped
-    p.inverse[i] = -1;
+    if (e >= 0 && e < p.E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  const int c = tid < p.E ? cnt[tid] : 0;
+  int32_t* out = p.chunk_base + (int64_t)blockIdx.x * p.E;
+  for (int e = tid; e < p.E; e += kPermuteChunk) out[e] = cnt[e];
+}
+
+// Sum (or, with write_base, turn into running positions starting at base) the
+// chunk histogram entries [ch0, ch1) of expert e, 16 loads in flight at a time.
+__device__ __forceinline__ int chunk_walk(int32_t* hist, int64_t E, int e, int64_t ch0,
+                                          int64_t ch1, bool write_base, int base) {
+  int run = base;
+  for (int64_t c0 = ch0; c0 < ch1; c0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t ch = c0 + u < ch1 ? c0 + u : ch1 - 1;
+      v[u] = hist[ch * E + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (c0 + u < ch1) {
+        if (write_base) hist[(c0 + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+  }
+  return run - base;
+}
+
+__global__ __launch_bounds__(kScanThreads) void permute_count_kernel(PermuteParams p) {
+  __shared__ int buf[kScanThreads];
+  __shared__ int partsum[kScanThreads];
+  __shared__ int ebase[1024];
+  __shared__ int total_mb;
+  const int tid = threadIdx.x;
+  const int64_t n = p.T * p.k;
+  const int64_t nchunks = (n + kPermuteChunk - 1) / kPermuteChunk;
+  // thread = (part, expert): the chunks of each expert are split into `parts`
+  // contiguous ranges, one per thread
+  const int E = (int)p.E;
+  const int parts = kScanThreads / E;          // >= 1 (E <= 1024)
+  const int e = tid % E, part = tid / E;
+  const bool act = part < parts;
+  const int64_t cpp = (nchunks + parts - 1) / parts;
+  const int64_t ch0 = act ? (int64_t)part * cpp : 0;
+  const int64_t ch1 = act ? (ch0 + cpp < nchunks ? ch0 + cpp : nchunks) : 0;
+  partsum[tid] = act && ch0 < ch1 ? chunk_walk(p.chunk_base, E, e, ch0, ch1, false, 0) : 0;
+  __syncthreads();
+  int c = 0;
+  if (tid < E)
+    for (int q = 0; q < parts; ++q) c += partsum[q * E + tid];
   const int off = block_exclusive_scan(c, buf);
-  if (tid < p.E) {
+  if (tid < E) {
     p.expert_offsets[tid] = off;
     p.group_end[tid] = off + c;
+    ebase[tid] = off;
   }
-  if (tid == p.E - 1) p.expert_offsets[p.E] = off + c;
+  __syncthreads();
+  // each chunk histogram entry becomes the chunk's first position for its expert
+  if (act && ch0 < ch1) {
+    int base = ebase[e];
+    for (int q = 0; q < part; ++q) base += partsum[q * E + e];
+    chunk_walk(p.chunk_base, E, e, ch0, ch1, true, base);
+  }
+  if (tid == E - 1) p.expert_offsets[E] = off + c;
   const int nmb = (c + p.bm - 1) / p.bm;
   const int mbo = block_exclusive_scan(nmb, buf);
   if (tid == kScanThreads - 1) total_mb = mbo + nmb;
@@ -148,28 +208,36 @@ __global__ __launch_bounds__(kScanThreads) void permute_count_kernel(PermutePara
   }
 }
 
-// ---- dispatch: stable scatter, one wave per expert -----------------------------
-__global__ __launch_bounds__(256) void permute_scatter_kernel(PermuteParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= p.E) return;
+__global__ __launch_bounds__(kPermuteChunk) void permute_scatter_kernel(PermuteParams p) {
+  __shared__ __attribute__((aligned(16))) int ids[kPermuteChunk];
+  const int tid = threadIdx.x;
   const int64_t n = p.T * p.k;
-  const int base = p.expert_offsets[e];
-  int running = 0;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t c = 0; c < n; c += 64) {
-    const int64_t i = c + lane;
-    const bool hit = i < n && p.ids[i] == e;
-    const uint64_t mask = __ballot(hit);
-    if (hit) {
-      const int pos = base + running + __popcll(mask & lt);
-      p.sorted_rows[pos] = (int32_t)i;
-      p.inverse[i] = pos;
-      p.row_expert[pos] = (int32_t)e;
-      p.src_token[pos] = (int32_t)(i / p.k);
-    }
-    running += __popcll(mask);
+  const int64_t i = (int64_t)blockIdx.x * kPermuteChunk + tid;
+  int e = -1;
+  if (i < n) {
+    e = p.ids[i];
+    if (e < 0 || e >= p.E) e = -1;
   }
+  ids[tid] = e;
+  __syncthreads();
+  if (i >= n) return;
+  if (e < 0) {
+    p.inverse[i] = -1;
+    return;
+  }
+  // earlier slots of this chunk routed to the same expert, four at a time
+  int rank = 0;
+  const int4* ids4 = reinterpret_cast<const int4*>(ids);
+  for (int q = 0; q < (tid >> 2); ++q) {
+    const int4 v = ids4[q];
+    rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+  }
+  for (int s2 = tid & ~3; s2 < tid; ++s2) rank += ids[s2] == e;
+  const int pos = p.chunk_base[(int64_t)blockIdx.x * p.E + e] + rank;
+  p.sorted_rows[pos] = (int32_t)i;
+  p.inverse[i] = pos;
+  p.row_expert[pos] = e;
+  p.src_token[pos] = (int32_t)(i / p.k);
 }
 
 // ---- SwiGLU + requant: one lane = 8 consecutive intermediate columns -----------
@@ -300,10 +368,18 @@ hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,
 
 hipError_t launch_permute(const PermuteParams& p, hipStream_t s, const char** name) {
   *name = "permute";
+  const int64_t n = p.T * p.k;
+  const int64_t nchunks = (n + kPermuteChunk - 1) / kPermuteChunk;
+  if (nchunks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)nchunks), dim3(kPermuteChunk), 0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(permute_count_kernel, dim3(1), dim3(kScanThreads), 0, s, p);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)((p.E + 3) / 4)), dim3(256), 0, s, p);
+  if (err != hipSuccess || nchunks == 0) return err;
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nchunks), dim3(kPermuteChunk), 0, s, p);
   return hipGetLastError();
 }
 

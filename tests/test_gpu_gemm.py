@@ -118,7 +118,7 @@ def test_mxfp4_w4a4_decode_full_size(decode_problem, M):
 
 
 # more than 64 activation rows and K % 128 == 0: the LDS-tiled kernel (128-row
-# tiles below 192 rows, 256-row MXFP4 tiles from 192), with ragged rows and columns
+# tiles), with ragged rows and columns
 TILED = [(65, 40, 128), (130, 256, 1024), (200, 300, 512), (257, 513, 384), (64 + 128 + 1, 17, 256)]
 
 
@@ -129,8 +129,7 @@ def test_tiled_shapes(fmt, shape):
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape))
     name = F.fp4_last_kernel()
     assert name.startswith("tile_" + fmt), name
-    if fmt == "mxfp4":
-        assert name.endswith("m256" if M >= 192 else "m128"), name
+    assert name.endswith("m128"), name
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32,
                   prequant=True)
 
@@ -185,7 +184,7 @@ def test_tiled_strided_output_canaries(fmt):
 
 
 def test_mxfp4_w4a4_prefill_full_size_sampled_rows():
-    # MXFP4 at the prefill shape, 256-row tiles; 64 sampled rows incl. first and last
+    # MXFP4 at the prefill shape; 64 sampled rows incl. first and last
     fmt, M, N, K = "mxfp4", 8192, 4096, 4096
     rng = np.random.default_rng(1)
     rows = np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 62, replace=False)])
