@@ -129,7 +129,7 @@ def test_tiled_shapes(fmt, shape):
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape))
     name = F.fp4_last_kernel()
     assert name.startswith("tile_" + fmt), name
-    assert name.endswith("m128"), name
+    assert name.endswith("m128") or name.endswith("m128_k256"), name
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32,
                   prequant=True)
 
