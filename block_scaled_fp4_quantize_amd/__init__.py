@@ -95,7 +95,8 @@ class MoeArgs(ctypes.Structure):
 class MoeLayout(ctypes.Structure):
     _fields_ = [(n, _sz) for n in ("total_bytes", "expert_offsets", "sorted_rows", "inverse",
                                    "x_codes", "x_scales", "gu", "h_codes", "h_scales", "h_bf16",
-                                   "y")] + [("x_rows", _i64)]
+                                   "y")] + [("x_rows", _i64), ("gu_rows", _i64),
+                                            ("swiglu_fused", ctypes.c_int32)]
 
 
 def _proto(name, res, args):

@@ -80,6 +80,8 @@ struct MoePlan {
   int bm;
   bool shared;
   bool w4a4;            // effective mode (after an allowed fallback)
+  bool fuse_routed;     // routed gate/up GEMM takes the fused SwiGLU epilogue
+  bool fuse_shared;     // shared expert's gate/up GEMM does
 };
 
 bool moe_shared(const fp4_moe_args* a) {
@@ -117,7 +119,13 @@ void moe_plan(const fp4_moe_args* a, bool w4a4, bool may_w4a16, MoePlan* pl) {
   pl->L.x_rows = x_rows;
   pl->L.x_codes = take((size_t)x_rows * (size_t)(a->H / 2));
   pl->L.x_scales = take((size_t)x_rows * (size_t)(a->H / G));
-  pl->L.gu = take(sizeof(float) * (size_t)R * (size_t)(2 * a->I));
+  const int akind = w4a4 ? fp4::kA_FP4 : fp4::kA_BF16;
+  pl->fuse_routed = fp4::gemm_can_fuse_swiglu(akind, P, a->H, a->I, true, bm);
+  pl->fuse_shared = sh && fp4::gemm_can_fuse_swiglu(akind, a->T, a->H, a->I, false, bm);
+  const int64_t gu_rows = (pl->fuse_routed ? 0 : P) + (sh && !pl->fuse_shared ? a->T : 0);
+  pl->L.gu_rows = gu_rows;
+  pl->L.swiglu_fused = (pl->fuse_routed ? 1 : 0) | (pl->fuse_shared ? 2 : 0);
+  pl->L.gu = take(sizeof(float) * (size_t)gu_rows * (size_t)(2 * a->I));
   pl->L.h_codes = take((size_t)R * (size_t)(a->I / 2));
   pl->L.h_scales = take((size_t)R * (size_t)(a->I / G));
   pl->L.h_bf16 = may_w4a16 ? take(sizeof(uint16_t) * (size_t)R * (size_t)a->I) : 0;
@@ -507,8 +515,13 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
   }
   const int akind = w4a4 ? fp4::kA_FP4 : fp4::kA_BF16;
 
-  // 4. grouped GEMM1 (gate and up) into gu [R, 2I] fp32
+  // 4. grouped GEMM1 (gate and up) into gu fp32, or straight into the quantized h
+  //    when the SwiGLU + requant epilogue is fused
   float* gu = reinterpret_cast<float*>(ws + pl.L.gu);
+  float* gu_shared = gu + (size_t)(pl.fuse_routed ? 0 : P) * (size_t)(2 * I);
+  uint8_t* h_codes = ws + pl.L.h_codes;
+  uint8_t* h_scales = ws + pl.L.h_scales;
+  uint16_t* h_bf16 = pl.L.h_bf16 ? reinterpret_cast<uint16_t*>(ws + pl.L.h_bf16) : nullptr;
   {
     fp4::GemmParams p{};
     p.M = P;
@@ -534,9 +547,18 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
     p.bm = pl.bm;
     p.alpha_g = nv ? alpha13 : nullptr;
     p.alpha = 1.0f;
-    p.out = gu;
-    p.ldo = 2 * I;
-    p.out_f32 = 1;
+    if (pl.fuse_routed) {
+      p.fuse_swiglu = 1;
+      p.I = I;
+      p.h_grp_g = nv ? g2 : nullptr;
+      p.h_g = 1.0f;
+      p.h_codes = h_codes;
+      p.h_scales = h_scales;
+    } else {
+      p.out = gu;
+      p.ldo = 2 * I;
+      p.out_f32 = 1;
+    }
     FP4_TRY(fp4::launch_gemm(fmt, akind, p, s, &name));
     if (pl.shared) {
       fp4::GemmParams q{};
@@ -554,17 +576,22 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
       q.w_codes = a->sh_w13_codes;
       q.w_scales = a->sh_w13_scales;
       q.alpha = sh_alpha13;
-      q.out = gu + (size_t)P * (2 * I);
-      q.ldo = 2 * I;
-      q.out_f32 = 1;
+      if (pl.fuse_shared) {
+        q.fuse_swiglu = 1;
+        q.I = I;
+        q.h_g = sh_g2;
+        q.h_codes = h_codes + (size_t)P * (I / 2);
+        q.h_scales = h_scales + (size_t)P * (I / G);
+      } else {
+        q.out = gu_shared;
+        q.ldo = 2 * I;
+        q.out_f32 = 1;
+      }
       FP4_TRY(fp4::launch_gemm(fmt, akind, q, s, &name));
     }
   }
 
-  // 5. SwiGLU + requant (or bf16) of the intermediate
-  uint8_t* h_codes = ws + pl.L.h_codes;
-  uint8_t* h_scales = ws + pl.L.h_scales;
-  uint16_t* h_bf16 = pl.L.h_bf16 ? reinterpret_cast<uint16_t*>(ws + pl.L.h_bf16) : nullptr;
+  // 5. SwiGLU + requant (or bf16) of the intermediate, for the unfused parts
   {
     fp4::SwigluParams sp{};
     sp.gu = gu;
@@ -578,10 +605,10 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
     sp.h_codes = h_codes;
     sp.h_scales = h_scales;
     sp.h_bf16 = h_bf16;
-    FP4_TRY(fp4::launch_swiglu(sp, s, &name));
-    if (pl.shared) {
+    if (!pl.fuse_routed) FP4_TRY(fp4::launch_swiglu(sp, s, &name));
+    if (pl.shared && !pl.fuse_shared) {
       fp4::SwigluParams ss = sp;
-      ss.gu = gu + (size_t)P * (2 * I);
+      ss.gu = gu_shared;
       ss.R = T;
       ss.row_grp = nullptr;
       ss.g = sh_g2;

@@ -70,6 +70,17 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
   return e == 0 ? sub : nrm;
 }
 
+// ---- one quantization block, given its amax ---------------------------------------
+// NVFP4 (activation quantizer order): sf = fp32(fp32(amax * g) / 6) -> e4m3 code sc
+// (RNE, saturating); elements are scaled by r = fp32(g / scale).  A zero scale gives
+// r = 0, for which q_nv_code returns magnitude 0 with the sign kept (e2m1 of 0).
+__device__ __forceinline__ uint32_t q_nv_scale(float amax, float g, float* r);
+__device__ __forceinline__ uint32_t q_nv_code(float v, float r);
+// MXFP4 (OCP MX): E = clamp(floor(log2 amax) - 2, -127, 127), code E + 127, read off
+// the exponent field (zero and subnormal amax give code 0); elements are v * 2^-E.
+__device__ __forceinline__ uint32_t q_mx_scale(float amax, int* E);
+__device__ __forceinline__ uint32_t q_mx_code(float v, int E);
+
 // Value 2^(c-127) of an e8m0 code (c = 0 gives the fp32 subnormal 2^-127).
 __device__ __forceinline__ float e8m0_value(uint32_t c) {
   return c == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((c & 0xFFu) << 23);
@@ -144,4 +155,31 @@ __device__ __forceinline__ bf16x8 bits_to_bf16x8(uint4 v) {
   return r;
 }
 
+
+// SwiGLU of one gate/up pair: SiLU(z) * u with SiLU(z) = z / (1 + e^-z), in fp32.
+__device__ __forceinline__ float swiglu1(float z, float u) {
+  const float silu = z / (1.0f + expf(-z));
+  return silu * u;
+}
+
+// ---- block quantization helpers (declared above) ---------------------------------
+__device__ __forceinline__ uint32_t q_nv_scale(float amax, float g, float* r) {
+  const float sf = (amax * g) / 6.0f;
+  const uint32_t sc = e4m3_code_pos(sf);
+  const float sd = e4m3_value_pos(sc);
+  *r = sd != 0.0f ? g / sd : 0.0f;
+  return sc;
+}
+__device__ __forceinline__ uint32_t q_nv_code(float v, float r) {
+  return e2m1_mag_code(fabsf(v) * r) | ((__float_as_uint(v) >> 31) << 3);
+}
+__device__ __forceinline__ uint32_t q_mx_scale(float amax, int* E) {
+  const uint32_t eb = (__float_as_uint(amax) >> 23) & 0xFFu;
+  const int code = eb == 0 ? 0 : max((int)eb - 2, 0);
+  *E = code - 127;
+  return (uint32_t)code;
+}
+__device__ __forceinline__ uint32_t q_mx_code(float v, int E) {
+  return e2m1_mag_code(ldexpf(fabsf(v), -E)) | ((__float_as_uint(v) >> 31) << 3);
+}
 }  // namespace fp4

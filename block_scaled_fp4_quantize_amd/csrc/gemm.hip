@@ -1060,8 +1060,18 @@ int gemm_block_rows(int /*fmt*/, int akind, int64_t rows_per_group, int64_t H, i
   return (tiled && rows_per_group >= 48) ? 128 : 32;
 }
 
+bool gemm_can_fuse_swiglu(int akind, int64_t M, int64_t K, int64_t I, bool grouped, int bm) {
+  if (akind != kA_FP4 || K % kKStep != 0 || I <= 0 || I % 128 != 0) return false;
+  return grouped ? bm == 128 : M > 64;
+}
+
 hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
                        const char** name) {
+  if (p.fuse_swiglu) {   // only the tiled kernel has the fused SwiGLU epilogue
+    if (!gemm_can_fuse_swiglu(akind, p.M, p.K, p.I, p.mblk_expert != nullptr, p.bm))
+      return hipErrorInvalidValue;
+    return launch_gemm_tiled(fmt, 128, p, s, name);
+  }
   // row blocks of 32 (two 16-row activation tiles); dense problems of at most 16
   // rows use one tile
   const bool one = !p.mblk_expert && p.M <= 16;

@@ -73,7 +73,12 @@ __device__ __forceinline__ void stage_store(uint8_t* base, const u32x4 (&creg)[C
 
 // MXFP4 128-row tiles fit in 256 registers, so two workgroups share a CU and one
 // computes while the other waits for its next stage (NVFP4 would spill).
-template <int FMT, int BM>
+// FUSE: the gate/up GEMM of an MoE expert with SwiGLU + requant in the epilogue.  The
+// workgroup's 256 weight rows are then 128 gate rows and the matching 128 up rows of
+// h columns [128 nt, 128 nt + 128): wave column wn takes h columns 64 wn + [0, 64),
+// its weight tiles 0-3 being the gate rows and 4-7 the up rows of the same columns,
+// so a lane holds gate and up of the same (m, h column) in registers.
+template <int FMT, int BM, bool FUSE>
 __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_gemm(GemmParams p) {
   using C = TileCfg<FMT, BM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
@@ -110,7 +115,14 @@ __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_g
       if (pv >= row_end) pv = row_end - 1;
       return p.a_gather ? (int64_t)p.a_gather[pv] : pv;
     }
-    int64_t n = nt * kTBN + (rr - BM);
+    int64_t n;
+    if (FUSE) {
+      const int w = rr - BM, within = w & 127;
+      const int64_t col = nt * 128 + (w >> 7) * 64 + (within & 63);
+      n = within < 64 ? col : p.I + col;
+    } else {
+      n = nt * kTBN + (rr - BM);
+    }
     return n < p.N ? n : p.N - 1;
   };
   const int cseg = tid & 3;
@@ -217,9 +229,72 @@ __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_g
     __syncthreads();
   }
 
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+  if (FUSE) {
+    // h = SiLU(alpha g) * (alpha u) for this lane's 4 consecutive h columns of each
+    // gate tile j; a quantization block (16 or 32 columns of one row) spans the lanes
+    // r, r + 16, r + 32, r + 48 (and, for MXFP4, gate tiles j and j + 1), so its amax is
+    // two lane exchanges away.  Every lane takes part in the exchanges; only rows
+    // that exist are stored.
+    const float g = p.h_grp_g ? p.h_grp_g[grp] : p.h_g;
+    const int64_t hrow = p.I / 2;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
+      const int64_t m = row0 + wm * (BM / 2) + 16 * i + r;
+      const bool store = m < row_end;
+      float h[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) h[j][v] = swiglu1(acc[j][i][v] * alpha, acc[j + 4][i][v] * alpha);
+      const int64_t hc0 = nt * 128 + wn * 64 + 4 * gq;   // + 16 j: this lane's first column
+      if (FMT == kNV) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float amax = fmaxf(fmaxf(fabsf(h[j][0]), fabsf(h[j][1])), fmaxf(fabsf(h[j][2]), fabsf(h[j][3])));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          float rs;
+          const uint32_t sc = q_nv_scale(amax, g, &rs);
+          uint32_t q = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) q |= q_nv_code(h[j][v], rs) << (4 * v);
+          if (store) {
+            const int64_t hc = hc0 + 16 * j;
+            *reinterpret_cast<uint16_t*>(p.h_codes + m * hrow + hc / 2) = (uint16_t)q;
+            if (gq == 0) p.h_scales[m * (p.I / 16) + hc / 16] = (uint8_t)sc;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          float amax = 0.0f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fmaxf(fabsf(h[j][v]), fabsf(h[j + 1][v])));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          int E;
+          const uint32_t sc = q_mx_scale(amax, &E);
+          uint32_t q0 = 0, q1 = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            q0 |= q_mx_code(h[j][v], E) << (4 * v);
+            q1 |= q_mx_code(h[j + 1][v], E) << (4 * v);
+          }
+          if (store) {
+            const int64_t hc = hc0 + 16 * j;
+            *reinterpret_cast<uint16_t*>(p.h_codes + m * hrow + hc / 2) = (uint16_t)q0;
+            *reinterpret_cast<uint16_t*>(p.h_codes + m * hrow + (hc + 16) / 2) = (uint16_t)q1;
+            if (gq == 0) p.h_scales[m * (p.I / 32) + hc / 32] = (uint8_t)sc;
+          }
+        }
+      }
+    }
+    return;
+  }
+
   // epilogue: lane holds out[m][n .. n+3], m = rows of activation tile i,
   // n = 4 consecutive columns of weight tile j
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
   const bool vec = (p.ldo & 3) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
@@ -259,7 +334,7 @@ __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_g
   }
 }
 
-template <int FMT, int BM>
+template <int FMT, int BM, bool FUSE>
 hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
   using C = TileCfg<FMT, BM>;
   const int64_t ntiles = (p.N + kTBN - 1) / kTBN;
@@ -269,17 +344,20 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   static const char* names[2][2] = {{"tile_nvfp4_m128", "tile_nvfp4_m256"},
                                     {"tile_mxfp4_m128", "tile_mxfp4_m256"}};
-  *name = names[FMT][BM == 256 ? 1 : 0];
+  *name = FUSE ? (FMT == kNV ? "tile_nvfp4_m128_swiglu" : "tile_mxfp4_m128_swiglu")
+               : names[FMT][BM == 256 ? 1 : 0];
   if (p.K % kTBK != 0 || p.K <= 0) return hipErrorInvalidValue;
+  if (FUSE && (p.I <= 0 || p.I % 128 != 0 || p.N != 2 * p.I || !p.h_codes || !p.h_scales))
+    return hipErrorInvalidValue;
   const size_t lds = 2 * (size_t)C::STAGE;
   static bool attr_set = false;  // once per instantiation (idempotent, so races are harmless)
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm<FMT, BM>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm<FMT, BM, FUSE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tile_gemm<FMT, BM>), dim3((unsigned)grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((tile_gemm<FMT, BM, FUSE>), dim3((unsigned)grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
@@ -290,9 +368,11 @@ hipError_t launch_gemm_tiled(int fmt, int bm, const GemmParams& p, hipStream_t s
   // NVFP4 runs on fp16 MFMAs (four per 128-deep stage where MXFP4 needs one), so
   // 128-row tiles already give it enough MFMA work per staged byte; 256-row NVFP4
   // tiles would also exceed the register file.
-  if (fmt == kNV || bm != 256) return fmt == kNV ? launch_tile<kNV, 128>(p, s, name)
-                                                 : launch_tile<kMX, 128>(p, s, name);
-  return launch_tile<kMX, 256>(p, s, name);
+  if (p.fuse_swiglu)
+    return fmt == kNV ? launch_tile<kNV, 128, true>(p, s, name) : launch_tile<kMX, 128, true>(p, s, name);
+  if (fmt == kNV || bm != 256) return fmt == kNV ? launch_tile<kNV, 128, false>(p, s, name)
+                                                 : launch_tile<kMX, 128, false>(p, s, name);
+  return launch_tile<kMX, 256, false>(p, s, name);
 }
 
 }  // namespace fp4

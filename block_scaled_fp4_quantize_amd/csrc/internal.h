@@ -48,8 +48,21 @@ struct GemmParams {
   void* out;
   int64_t ldo;
   int out_f32;
+  // Fused SwiGLU + requant of a gate/up GEMM (tiled kernel, fp4 activations): the
+  // weight rows are gate [0, I) and up [I, 2I) (N = 2I, I % 128 == 0); instead of
+  // `out`, h = SiLU(alpha g) * (alpha u) is quantized into h_codes / h_scales, whose
+  // rows are indexed like the output rows.
+  int fuse_swiglu;
+  int64_t I;
+  const float* h_grp_g;   // per-group NVFP4 quantize multiplier (1 / a2_scale), or null
+  float h_g;              // scalar multiplier when h_grp_g is null (MXFP4: unused)
+  uint8_t* h_codes;       // [rows, I/2]
+  uint8_t* h_scales;      // [rows, I/G]
 };
 enum AKind : int { kA_FP4 = 0, kA_BF16 = 1 };
+// Whether a gate/up GEMM of this shape runs on the tiled kernel, and so can take the
+// fused SwiGLU + requant epilogue (grouped: 128-row blocks; dense: more than 64 rows).
+bool gemm_can_fuse_swiglu(int akind, int64_t M, int64_t K, int64_t I, bool grouped, int bm);
 // Row-block height of the block table for grouped (MoE) GEMMs of these shapes
 // (GEMM1 has K = H, GEMM2 has K = I); launch_gemm picks its kernel from it.
 int gemm_block_rows(int fmt, int akind, int64_t rows_per_group, int64_t H, int64_t I);

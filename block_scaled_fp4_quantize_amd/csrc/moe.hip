@@ -258,9 +258,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluParams p) {
     const float* up = gate + p.I;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float z = gate[i];
-      const float silu = z / (1.0f + expf(-z));
-      h[i] = silu * up[i];
+      h[i] = swiglu1(gate[i], up[i]);
       amax = fmaxf(amax, fabsf(h[i]));
     }
     if (p.row_grp) g = p.grp_g[p.row_grp[row]];
@@ -282,26 +280,15 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluParams p) {
   if (!active) return;
   uint32_t packed = 0, sc;
   if (FMT == kNV) {
-    const float sf = (amax * g) / 6.0f;
-    sc = e4m3_code_pos(sf);
-    const float sd = e4m3_value_pos(sc);
-    if (sd != 0.0f) {
-      const float r = g / sd;
+    float r;
+    sc = q_nv_scale(amax, g, &r);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        packed |= (e2m1_mag_code(fabsf(h[i]) * r) | ((__float_as_uint(h[i]) >> 31) << 3)) << (4 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) packed |= (__float_as_uint(h[i]) >> 31) << (4 * i + 3);
-    }
+    for (int i = 0; i < 8; ++i) packed |= q_nv_code(h[i], r) << (4 * i);
   } else {
-    const uint32_t eb = (__float_as_uint(amax) >> 23) & 0xFFu;
-    const int code = eb == 0 ? 0 : max((int)eb - 2, 0);
-    sc = (uint32_t)code;
-    const int E = code - 127;
+    int E;
+    sc = q_mx_scale(amax, &E);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      packed |= (e2m1_mag_code(ldexpf(fabsf(h[i]), -E)) | ((__float_as_uint(h[i]) >> 31) << 3)) << (4 * i);
+    for (int i = 0; i < 8; ++i) packed |= q_mx_code(h[i], E) << (4 * i);
   }
   *reinterpret_cast<uint32_t*>(p.h_codes + row * (p.I / 2) + kc * 4) = packed;
   if ((kc & (LPG - 1)) == 0) {

@@ -73,34 +73,15 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantParams p) {
   uint32_t packed = 0;
   uint32_t sc;
   if (FMT == kNV) {
-    const float sf = (amax * g) / 6.0f;
-    sc = e4m3_code_pos(sf);
-    const float sd = e4m3_value_pos(sc);
-    if (sd != 0.0f) {
-      const float r = g / sd;
+    float r;
+    sc = q_nv_scale(amax, g, &r);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t sign = __float_as_uint(v[i]) >> 31;
-        const uint32_t q = e2m1_mag_code(fabsf(v[i]) * r) | (sign << 3);
-        packed |= q << (4 * i);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) packed |= (__float_as_uint(v[i]) >> 31) << (4 * i + 3);
-    }
+    for (int i = 0; i < 8; ++i) packed |= q_nv_code(v[i], r) << (4 * i);
   } else {
-    // E = clamp(floor(log2 amax) - 2, -127, 127); code = E + 127, read off the
-    // exponent field (zero and subnormal amax give code 0).
-    const uint32_t eb = (__float_as_uint(amax) >> 23) & 0xFFu;
-    const int code = eb == 0 ? 0 : max((int)eb - 2, 0);
-    sc = (uint32_t)code;
-    const int E = code - 127;
+    int E;
+    sc = q_mx_scale(amax, &E);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t sign = __float_as_uint(v[i]) >> 31;
-      const uint32_t q = e2m1_mag_code(ldexpf(fabsf(v[i]), -E)) | (sign << 3);
-      packed |= q << (4 * i);
-    }
+    for (int i = 0; i < 8; ++i) packed |= q_mx_code(v[i], E) << (4 * i);
   }
   *reinterpret_cast<uint32_t*>(p.codes + row * (p.K / 2) + kc * 4) = packed;
   if ((kc & (LPG - 1)) == 0) {

@@ -187,12 +187,19 @@ typedef struct {
   size_t inverse;         /* int32 [T*k]: sorted position of flat index t*k+j */
   size_t x_codes;         /* uint8 [rows, H/2] GEMM1 input codes (W4A4) */
   size_t x_scales;        /* uint8 [rows, H/G] */
-  size_t gu;              /* fp32 [T*k + T, 2I] gate/up outputs, sorted order then shared */
+  size_t gu;              /* fp32 [gu_rows, 2I] gate/up outputs of the parts that do not
+                             take the fused SwiGLU epilogue: the routed rows in sorted order
+                             (unless swiglu_fused bit 0), then the shared rows (unless bit 1) */
   size_t h_codes;         /* uint8 [T*k + T, I/2] quantized intermediate (W4A4) */
   size_t h_scales;        /* uint8 [T*k + T, I/G] */
   size_t h_bf16;          /* bf16 [T*k + T, I] intermediate (W4A16) */
   size_t y;               /* fp32 [T*k + T, H] expert outputs before the combine */
   int64_t x_rows;         /* rows in x_codes: T (MXFP4) or T*k + T (NVFP4) */
+  int64_t gu_rows;        /* rows in gu */
+  int32_t swiglu_fused;   /* bit 0: routed rows, bit 1: shared rows have SwiGLU and the
+                             requant fused into the gate/up GEMM (W4A4 on the tiled kernel:
+                             128-row expert blocks, or more than 64 tokens for the shared
+                             expert, and I % 128 == 0); their h is written without gu */
 } fp4_moe_layout;
 
 size_t fp4_moe_workspace_size(const fp4_moe_args* a);

@@ -80,7 +80,9 @@ def run_gpu(pb, flags=0):
     r["offsets"] = ws_view(ws, lay.expert_offsets, pb.E + 1, torch.int32).cpu().numpy()
     r["sorted_rows"] = ws_view(ws, lay.sorted_rows, P, torch.int32).cpu().numpy()
     r["inverse"] = ws_view(ws, lay.inverse, P, torch.int32).cpu().numpy()
-    r["gu"] = ws_view(ws, lay.gu, R * 2 * pb.I, torch.float32).view(R, 2 * pb.I)
+    # gate/up rows exist only for the parts without the fused SwiGLU epilogue
+    r["gu"] = ws_view(ws, lay.gu, lay.gu_rows * 2 * pb.I, torch.float32).view(lay.gu_rows, 2 * pb.I)
+    r["fused"] = int(lay.swiglu_fused)
     r["y"] = ws_view(ws, lay.y, R * pb.H, torch.float32).view(R, pb.H)
     if pb.mode == "w4a4":
         r["x_codes"] = ws_view(ws, lay.x_codes, lay.x_rows * pb.H // 2, torch.uint8).view(lay.x_rows, -1)
@@ -195,12 +197,17 @@ def verify(pb, r, tokens=None, max_diff_frac=1e-3):
                 xr = pos
             assert np.array_equal(r["x_codes"][xr].cpu().numpy(), o["xc"]), f"x codes, expert {e}"
             assert np.array_equal(r["x_scales"][xr].cpu().numpy(), o["xs"]), f"x scales, expert {e}"
-        # GEMM1 output (fp32)
-        gu = gu_all[pos].cpu().numpy().astype(np.float64)
-        b1 = 2e-3 * abs(o["a13"]) * np.outer(np.linalg.norm(o["x_hat"], axis=1),
-                                             np.linalg.norm(o["w13_hat"], axis=1))
-        assert (np.abs(gu - o["gu"]) <= b1).all(), f"gate/up outside tolerance, expert {e}"
-        assert np.linalg.norm(gu - o["gu"]) <= 1e-5 * np.linalg.norm(o["gu"]) + 1e-30
+        # GEMM1 output (fp32), unless the SwiGLU epilogue was fused into GEMM1: then
+        # gate/up never reach memory and the intermediate codes below check it
+        fused = bool(r["fused"] & (2 if e == "shared" else 1))
+        if not fused:
+            routed_rows = 0 if r["fused"] & 1 else P
+            grow = pos - P + routed_rows if e == "shared" else pos
+            gu = gu_all[grow].cpu().numpy().astype(np.float64)
+            b1 = 2e-3 * abs(o["a13"]) * np.outer(np.linalg.norm(o["x_hat"], axis=1),
+                                                 np.linalg.norm(o["w13_hat"], axis=1))
+            assert (np.abs(gu - o["gu"]) <= b1).all(), f"gate/up outside tolerance, expert {e}"
+            assert np.linalg.norm(gu - o["gu"]) <= 1e-5 * np.linalg.norm(o["gu"]) + 1e-30
         # intermediate
         if pb.mode == "w4a4":
             gc = OF.unpack_nibbles(r["h_codes"][pos].cpu().numpy())
@@ -287,6 +294,12 @@ SMALL = [
 def test_moe_small(fmt, mode, kw):
     pb = MoeProblem(fmt, mode, seed=kw["T"] + kw["E"], **kw)
     r = run_gpu(pb)
+    if mode == "w4a4" and kw["T"] * kw["k"] >= 48 * kw["E"] and kw["H"] % 128 == 0 and \
+            kw["I"] % 128 == 0:
+        # 128-row expert blocks: SwiGLU + requant run in the gate/up GEMM's epilogue
+        # (and in the shared expert's, above 64 tokens)
+        assert r["fused"] & 1, r["fused"]
+        assert bool(r["fused"] & 2) == (kw["shared"] and kw["T"] > 64), r["fused"]
     verify(pb, r, max_diff_frac=0.02)
 
 
