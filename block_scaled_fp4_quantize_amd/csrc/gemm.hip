@@ -1070,7 +1070,7 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   if (p.fuse_swiglu) {   // only the tiled kernel has the fused SwiGLU epilogue
     if (!gemm_can_fuse_swiglu(akind, p.M, p.K, p.I, p.mblk_expert != nullptr, p.bm))
       return hipErrorInvalidValue;
-    return launch_gemm_tiled(fmt, 128, p, s, name);
+    return launch_gemm_tiled(fmt, p, s, name);
   }
   // row blocks of 32 (two 16-row activation tiles); dense problems of at most 16
   // rows use one tile
@@ -1080,13 +1080,13 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   const bool fast = akind == kA_FP4 && p.K % kKStep == 0;
   if (p.mblk_expert && p.bm != 32) {
     if (p.bm != 128 || !fast) return hipErrorInvalidValue;
-    return launch_gemm_tiled(fmt, 128, p, s, name);
+    return launch_gemm_tiled(fmt, p, s, name);
   }
   // measurement switch between the fp4-activation kernels (default: stream)
   const char* sel = getenv("FP4_GEMM_KERNEL");
   const char c0 = (fast && sel) ? sel[0] : 0, c1 = c0 ? sel[1] : 0;
   if (fast && !sel && !p.mblk_expert && p.M > 64)
-    return launch_gemm_tiled(fmt, 128, p, s, name);
+    return launch_gemm_tiled(fmt, p, s, name);
   // at most 16 rows (one 16-row activation tile): activations resident in LDS with
   // a deep weight stream, when they fit; two-tile blocks measure faster on the
   // streaming kernel below

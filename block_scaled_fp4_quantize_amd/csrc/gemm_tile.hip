@@ -7,16 +7,15 @@
 // fp16 for fp16 MFMA ("vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A Complete
 // Technical Guide", §6.1 and §6.4 for the two block-scale formats).
 //
-// Tiling: a workgroup (4 waves, 2 x 2) owns 256 weight rows and BM activation rows
-// (BM = 128: MXFP4 runs two such workgroups per CU; a 256-row MXFP4 variant is
-// kept for callers that ask for it).
-// Each wave computes a 128 x BM/2 tile with 16x16 MFMAs (weights as the A operand,
-// so a lane ends up holding 4 consecutive output columns).  K advances in stages
-// of 128: the packed codes (64 bytes per row) and block scales of the BM + 256
-// rows are staged in LDS, double-buffered, with the next stage's global loads in
-// flight while the current one is multiplied.  Codes travel at 4.5 bits per
-// element all the way into registers; NVFP4 is decoded to fp16 right before the
-// MFMA (unit-scale convert, then one packed fp16 multiply by the e4m3 scale --
+// Tiling: a workgroup (4 waves, 2 x 2) owns 256 weight rows and 128 activation rows
+// (MXFP4 runs two such workgroups per CU).  Each wave computes a 128 x 64 tile with
+// 16x16 MFMAs (weights as the A operand, so a lane ends up holding 4 consecutive
+// output columns).  K advances in stages of 128: the packed codes (64 bytes per row)
+// and block scales of the 384 rows are copied straight from global memory into LDS
+// (no staging registers), with NBUF stages in LDS so that the copies of the next
+// NBUF - 2 stages are in flight while one stage is multiplied.  Codes travel at 4.5
+// bits per element all the way into registers; NVFP4 is decoded to fp16 right before
+// the MFMA (unit-scale convert, then one packed fp16 multiply by the e4m3 scale --
 // exact), MXFP4 needs no decode at all.
 #include "device.h"
 #include "internal.h"
@@ -27,66 +26,169 @@ namespace {
 
 constexpr int kTBK = 128;        // K per stage
 constexpr int kTBN = 256;        // weight rows per workgroup
-constexpr int kTCS = 80;         // LDS row stride of staged codes: 64 bytes + 16 pad
+
+// Staged LDS layout of one K stage (no staging registers: global -> LDS copies).
+// Codes: unpadded 64-byte rows; the 16-byte column c of row x is stored at column
+// c ^ tile_swz(x & 15), which makes the MFMA fragment reads (16 rows x one column per
+// 16 lanes) bank-conflict-free whether the LDS serves 128 or 256 bytes per clock.  A
+// copy is 16 rows x 64 bytes, the swizzle applied through each lane's source address.
+// Scales: the 4-byte words of a row (MXFP4: one word = the row's 4 block scales of the
+// stage; NVFP4: two words, stored as two planes of ROWS words) are stored at word
+// tile_sslot(x), which puts the words of rows 16 j + r, j = 4 k .. 4 k + 3, of a 64-row
+// block next to each other: a lane (row r) then gets its 4 tiles' scales with one
+// 16-byte read, and 16 lanes read 256 consecutive bytes.  Every wave issues the same
+// number OPS of copies per stage (pad copies repeat copy 0 into a pad area), so one
+// compile-time vmcnt serves all waves.  NBUF stages live in LDS at once.
+__device__ __forceinline__ int tile_swz(int r) {
+  return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+}
+__device__ __forceinline__ int tile_sslot(int x) {
+  return (x & ~63) | ((x & 15) << 2) | ((x >> 4) & 3);
+}
+__device__ __forceinline__ int tile_srow(int slot) {   // inverse of tile_sslot
+  return (slot & ~63) | ((slot & 3) << 4) | ((slot >> 2) & 15);
+}
 
 template <int FMT, int BM>
 struct TileCfg {
   static constexpr int G = FMT == kNV ? 16 : 32;
-  static constexpr int SB = kTBK / G;          // scale bytes per row per stage (8 / 4)
-  static constexpr int MI = BM / 32;           // 16-row activation tiles per wave
-  static constexpr int NJ = 8;                 // 16-row weight tiles per wave
-  static constexpr int ROWS = BM + kTBN;       // staged rows: activations, then weights
-  static constexpr int CODE_BYTES = ROWS * kTCS;
-  static constexpr int STAGE = CODE_BYTES + ROWS * SB;
-  static constexpr int CP = ROWS * 4 / 256;    // 16-byte code pieces per thread per stage
-  static constexpr int SPT = ROWS * SB / 4;    // 4-byte scale pieces per stage
-  static constexpr int SP = (SPT + 255) / 256; // scale pieces per thread (last one guarded)
+  static constexpr int SB = kTBK / G;                  // scale bytes per row per stage
+  static constexpr int WM = BM / 64;                   // waves along the activation rows
+  static constexpr int WAVES = 2 * WM;                 // (two along the weight rows)
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int MI = 4;                         // 16-row activation tiles per wave
+  static constexpr int NJ = 8;                         // 16-row weight tiles per wave
+  static constexpr int ROWS = BM + kTBN;               // staged rows: activations, then weights
+  static constexpr int CCOP = ROWS / 16;               // 1 KB code copies per stage
+  static constexpr int CPW = CCOP / WAVES;             // ... per wave
+  static constexpr int SDW = ROWS * SB / 4;            // scale words per stage
+  static constexpr int SCOP = (SDW + 63) / 64;         // 256-byte scale copies
+  static constexpr int SPW = (SCOP + WAVES - 1) / WAVES;  // ... per wave (padded)
+  static constexpr int OPS = CPW + SPW;                // copies per wave per stage
+  static constexpr int CODES = ROWS * 64;
+  static constexpr int STAGE = CODES + WAVES * SPW * 256;  // bytes per LDS stage
+  // MXFP4 128-row tiles: two workgroups per CU (3 stages each); otherwise one
+  static constexpr int NBUF = (FMT == kMX && BM == 128) ? 3 : 4;
+  static constexpr int PER_CU = (FMT == kMX && BM == 128) ? 2 : 1;
+  static constexpr int LDS = NBUF * STAGE;
+  static_assert(CCOP % WAVES == 0, "code copies split evenly over the waves");
+  static_assert(BM % 128 == 0 && ROWS % 64 == 0, "64-row scale blocks, 128-row weight halves");
+  static_assert(NBUF >= 3 && NBUF <= 4, "the stage waits cover up to two stages in flight");
+  static_assert(PER_CU * LDS <= 160 * 1024, "LDS per CU");
+  static_assert(THREADS == 2 * BM, "launch bounds of tile_gemm");
 };
 
-// Global -> register half of staging one K stage: this thread's code pieces (16
-// bytes of one row) and scale pieces (4 bytes), at stage st.
-template <class C>
-__device__ __forceinline__ void stage_load(u32x4 (&creg)[C::CP], uint32_t (&sreg)[C::SP],
-                                           const uint8_t* const (&cptr)[C::CP],
-                                           const uint8_t* const (&sptr)[C::SP], int64_t st) {
-  const int64_t kb = st * (kTBK / 2);
+#define FP4_TILE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+// One LDS-direct copy per lane: 16 bytes to lds + 16 lane, or 4 bytes to lds + 4 lane
+// (M0 = the wave-uniform LDS base, one wait state before its use).  Issued from
+// inline asm: the compiler's wait-count pass would otherwise drain every load before
+// any later LDS read; the kernel waits for these copies itself.
+__device__ __forceinline__ void tile_copy16(const void* g, uint8_t* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)FP4_TILE_LDS(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0v), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void tile_copy4(const void* g, uint8_t* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)FP4_TILE_LDS(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(m0v), "v"(g) : "memory", "m0");
+}
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding): this wave's copies except the last n
+// have landed and its own LDS reads are done, so after the barrier that follows, the
+// buffer just read may be overwritten
+constexpr int tile_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// The MFMA work of one staged K step: fragment reads (codes at row * 64 + ccol, scales
+// at CODES + row * SB) and the MFMAs into acc.
+template <int FMT, int BM>
+__device__ __forceinline__ void tile_step(const uint8_t* cur, int ccol, int r, int gq, int wm, int wn,
+                                          v4f (&acc)[TileCfg<FMT, BM>::NJ][TileCfg<FMT, BM>::MI]) {
+  using C = TileCfg<FMT, BM>;
+  // fragments of this stage: weights (A operand) and activations (B operand).  The
+  // scale word of tile j of this lane's row holds its 4 (MXFP4) or 2 (NVFP4 plane
+  // gq / 2) block scales; the lane's own block starts at bit 8 gq or 16 (gq & 1).
+  uint4 wf[C::NJ];
+  uint32_t wsb[C::NJ];
+  uint4 af[C::MI];
+  uint32_t asb[C::MI];
+  const uint8_t* sc = cur + C::CODES + (FMT == kNV ? (gq >> 1) * C::ROWS * 4 : 0) + r * 16;
+  const int ssh = FMT == kNV ? 16 * (gq & 1) : 8 * gq;
 #pragma unroll
-  for (int i = 0; i < C::CP; ++i) creg[i] = *reinterpret_cast<const u32x4*>(cptr[i] + kb);
-  const int64_t ks = st * C::SB;
+  for (int j = 0; j < C::NJ; ++j)
+    wf[j] = *reinterpret_cast<const uint4*>(cur + (BM + wn * 128 + 16 * j + r) * 64 + ccol);
 #pragma unroll
-  for (int i = 0; i < C::SP; ++i) sreg[i] = *reinterpret_cast<const uint32_t*>(sptr[i] + ks);
+  for (int k = 0; k < C::NJ / 4; ++k) {
+    const uint4 w4 = *reinterpret_cast<const uint4*>(sc + (BM + wn * 128 + 64 * k) * 4);
+    wsb[4 * k + 0] = w4.x >> ssh;
+    wsb[4 * k + 1] = w4.y >> ssh;
+    wsb[4 * k + 2] = w4.z >> ssh;
+    wsb[4 * k + 3] = w4.w >> ssh;
+  }
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+    af[i] = *reinterpret_cast<const uint4*>(cur + (wm * 64 + 16 * i + r) * 64 + ccol);
+  {
+    const uint4 a4 = *reinterpret_cast<const uint4*>(sc + wm * 64 * 4);
+    asb[0] = a4.x >> ssh;
+    asb[1] = a4.y >> ssh;
+    asb[2] = a4.z >> ssh;
+    asb[3] = a4.w >> ssh;
+  }
+  static_assert(C::MI == 4 && C::NJ % 4 == 0, "scale words are read 4 tiles at a time");
+
+  if (FMT == kMX) {
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) {
+      const v8i wop = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        const v8i aop = {(int)af[i].x, (int)af[i].y, (int)af[i].z, (int)af[i].w, 0, 0, 0, 0};
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            wop, aop, acc[j][i], 4, 4, 0, (int)wsb[j], 0, (int)asb[i]);
+      }
+    }
+  } else {
+    // lane group gq holds elements [32 gq, 32 gq + 32) of the stage; k-step s uses
+    // its dword s (block 2 gq + s/2), the same k slots for both operands
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f16x8 aop[C::MI];
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+        aop[i] = decode8_f16(dword_of(af[i], s),
+                             f16_pair(e4m3_value_pos((asb[i] >> (8 * (s >> 1))) & 0xFFu)));
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) {
+        const f16x8 wop = decode8_f16(dword_of(wf[j], s),
+                                      f16_pair(e4m3_value_pos((wsb[j] >> (8 * (s >> 1))) & 0xFFu)));
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop[i], acc[j][i], 0, 0, 0);
+      }
+    }
+  }
+
 }
 
-// Register -> LDS half: code piece i of thread t is row t/4 + 64 i, bytes 16 (t%4)..;
-// scale piece t + 256 i is the 4-byte word at that index of the stage's scale area.
-template <class C>
-__device__ __forceinline__ void stage_store(uint8_t* base, const u32x4 (&creg)[C::CP],
-                                            const uint32_t (&sreg)[C::SP], int tid) {
-#pragma unroll
-  for (int i = 0; i < C::CP; ++i)
-    *reinterpret_cast<u32x4*>(base + ((tid >> 2) + 64 * i) * kTCS + (tid & 3) * 16) = creg[i];
-#pragma unroll
-  for (int i = 0; i < C::SP; ++i)
-    if (tid + 256 * i < C::SPT)
-      *reinterpret_cast<uint32_t*>(base + C::CODE_BYTES + (tid + 256 * i) * 4) = sreg[i];
-}
-
-// MXFP4 128-row tiles fit in 256 registers, so two workgroups share a CU and one
-// computes while the other waits for its next stage (NVFP4 would spill).
+// Each wave holds a 128 (weight rows) x 64 (activation rows) accumulator tile.  MXFP4
+// 128-row tiles fit in 256 registers, so two workgroups share a CU and one computes
+// while the other waits at a barrier; MXFP4 256-row tiles use 8 waves (two per SIMD)
+// on one CU, sharing each staged weight row between twice as many activation rows;
+// NVFP4 runs one 4-wave workgroup per CU (its decode needs more registers).
 // FUSE: the gate/up GEMM of an MoE expert with SwiGLU + requant in the epilogue.  The
 // workgroup's 256 weight rows are then 128 gate rows and the matching 128 up rows of
 // h columns [128 nt, 128 nt + 128): wave column wn takes h columns 64 wn + [0, 64),
 // its weight tiles 0-3 being the gate rows and 4-7 the up rows of the same columns,
 // so a lane holds gate and up of the same (m, h column) in registers.
 template <int FMT, int BM, bool FUSE>
-__global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_gemm(GemmParams p) {
+__global__ __launch_bounds__(2 * BM, (FMT == kMX && BM == 128) ? 2 : 1) void tile_gemm(GemmParams p) {
   using C = TileCfg<FMT, BM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int wm = wave % C::WM;
+  const int wn = wave / C::WM;
   const int64_t ntiles = (p.N + kTBN - 1) / kTBN;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
@@ -107,8 +209,8 @@ __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_g
   const uint8_t* wcodes = p.w_codes + grp * p.w_estride_codes;
   const uint8_t* wscales = p.w_scales + grp * p.w_estride_scales;
 
-  // global source rows of this thread's staging pieces (fixed for all stages);
-  // rows past the end are clamped to the last valid one (outputs not stored)
+  // global source row of staged row rr (fixed for all stages); rows past the end are
+  // clamped to the last valid one (their outputs are not stored)
   auto src_row = [&](int rr) -> int64_t {
     if (rr < BM) {
       int64_t pv = row0 + rr;
@@ -125,20 +227,28 @@ __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_g
     }
     return n < p.N ? n : p.N - 1;
   };
-  const int cseg = tid & 3;
-  const uint8_t* cptr[C::CP];
+  // code copy q of this wave is copy c = wave + WAVES q (staged rows 16 c ..): lane l
+  // fetches row 16 c + l/4, column (l & 3) ^ tile_swz(l/4) into LDS slot l.  Scale
+  // copy q is c = wave + WAVES q (a pad copy past the last repeats copy 0): lane l
+  // fills scale word e = 64 c + l (clamped to the last one), i.e. plane e / ROWS,
+  // staged row tile_srow(e % ROWS).
+  const uint8_t* dcode[C::CPW];
+  const uint8_t* dscale[C::SPW];
 #pragma unroll
-  for (int i = 0; i < C::CP; ++i) {
-    const int rr = (tid >> 2) + 64 * i;
-    cptr[i] = (rr < BM ? p.a_codes : wcodes) + src_row(rr) * KB + cseg * 16;
+  for (int q = 0; q < C::CPW; ++q) {
+    const int rr = 16 * (wave + C::WAVES * q) + (lane >> 2);
+    const int col = (lane & 3) ^ tile_swz(lane >> 2);
+    dcode[q] = (rr < BM ? p.a_codes : wcodes) + src_row(rr) * KB + col * 16;
   }
-  const uint8_t* sptr[C::SP];
 #pragma unroll
-  for (int i = 0; i < C::SP; ++i) {
-    int pc = tid + 256 * i;
-    if (pc >= C::SPT) pc = C::SPT - 1;
-    const int rr = pc / (C::SB / 4);
-    sptr[i] = (rr < BM ? p.a_scales : wscales) + src_row(rr) * KS + (pc - rr * (C::SB / 4)) * 4;
+  for (int q = 0; q < C::SPW; ++q) {
+    int c = wave + C::WAVES * q;
+    if (c >= C::SCOP) c = 0;
+    int e = 64 * c + lane;
+    if (e >= C::SDW) e = C::SDW - 1;
+    const int plane = e / C::ROWS;
+    const int rr = tile_srow(e - plane * C::ROWS);
+    dscale[q] = (rr < BM ? p.a_scales : wscales) + src_row(rr) * KS + plane * 4;
   }
 
   v4f acc[C::NJ][C::MI];
@@ -150,83 +260,42 @@ __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_g
   const int r = lane & 15;
   const int gq = lane >> 4;
   const int64_t nstages = K / kTBK;
-  uint8_t* buf0 = tsm;
-  uint8_t* buf1 = tsm + C::STAGE;
 
-  {
-    u32x4 creg[C::CP];
-    uint32_t sreg[C::SP];
-    stage_load<C>(creg, sreg, cptr, sptr, 0);
-    stage_store<C>(buf0, creg, sreg, tid);
-  }
-  __syncthreads();
+  // Stage t lives in buffer t % NBUF.  Iteration st issues stage st + NBUF - 1 (if it
+  // exists) into the buffer computed at st - 1, computes stage st, then waits until
+  // stage st + 1 has landed -- the stages after it may stay in flight -- and syncs.
+  // The last iteration waits for everything, so no copy is outstanding after the loop.
+  auto issue = [&](int64_t t) {
+    uint8_t* buf = tsm + (int)(t % C::NBUF) * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < C::CPW; ++q)
+      tile_copy16(dcode[q] + t * 64, buf + (wave + C::WAVES * q) * 1024);
+#pragma unroll
+    for (int q = 0; q < C::SPW; ++q)
+      tile_copy4(dscale[q] + t * C::SB, buf + C::CODES + (wave + C::WAVES * q) * 256);
+  };
+  auto sync = [&](int64_t ahead) {   // stages issued after the one needed next
+    if (C::NBUF >= 4 && ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(tile_vmcnt(2 * C::OPS));
+    else if (ahead >= 1)
+      __builtin_amdgcn_s_waitcnt(tile_vmcnt(C::OPS));
+    else
+      __builtin_amdgcn_s_waitcnt(tile_vmcnt(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // fragment rows are 16-row tile starts + r, so their swizzle is tile_swz(r)
+  const int gcol = (gq ^ tile_swz(r)) << 4;
+#pragma unroll
+  for (int t = 0; t < C::NBUF - 1; ++t)
+    if (t < nstages) issue(t);
+  sync(nstages - 1 < C::NBUF - 2 ? nstages - 1 : C::NBUF - 2);
   for (int64_t st = 0; st < nstages; ++st) {
-    uint8_t* cur = (st & 1) ? buf1 : buf0;
-    uint8_t* nxt = (st & 1) ? buf0 : buf1;
-    u32x4 creg[C::CP];
-    uint32_t sreg[C::SP];
-    // clamped prefetch of the next stage (the last iteration reloads its own stage)
-    stage_load<C>(creg, sreg, cptr, sptr, st + 1 < nstages ? st + 1 : st);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // fragments of this stage: weights (A operand) and activations (B operand)
-    uint4 wf[C::NJ];
-    uint32_t wsb[C::NJ];
-    uint4 af[C::MI];
-    uint32_t asb[C::MI];
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) {
-      const int rr = BM + wn * 128 + 16 * j + r;
-      wf[j] = *reinterpret_cast<const uint4*>(cur + rr * kTCS + gq * 16);
-      if (FMT == kMX)
-        wsb[j] = cur[C::CODE_BYTES + rr * C::SB + gq];
-      else
-        wsb[j] = *reinterpret_cast<const uint16_t*>(cur + C::CODE_BYTES + rr * C::SB + gq * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-      const int rr = wm * (BM / 2) + 16 * i + r;
-      af[i] = *reinterpret_cast<const uint4*>(cur + rr * kTCS + gq * 16);
-      if (FMT == kMX)
-        asb[i] = cur[C::CODE_BYTES + rr * C::SB + gq];
-      else
-        asb[i] = *reinterpret_cast<const uint16_t*>(cur + C::CODE_BYTES + rr * C::SB + gq * 2);
-    }
-
-    if (FMT == kMX) {
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        const v8i wop = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i) {
-          const v8i aop = {(int)af[i].x, (int)af[i].y, (int)af[i].z, (int)af[i].w, 0, 0, 0, 0};
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wop, aop, acc[j][i], 4, 4, 0, (int)wsb[j], 0, (int)asb[i]);
-        }
-      }
-    } else {
-      // lane group gq holds elements [32 gq, 32 gq + 32) of the stage; k-step s uses
-      // its dword s (block 2 gq + s/2), the same k slots for both operands
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        f16x8 aop[C::MI];
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-          aop[i] = decode8_f16(dword_of(af[i], s),
-                               f16_pair(e4m3_value_pos((asb[i] >> (8 * (s >> 1))) & 0xFFu)));
-#pragma unroll
-        for (int j = 0; j < C::NJ; ++j) {
-          const f16x8 wop = decode8_f16(dword_of(wf[j], s),
-                                        f16_pair(e4m3_value_pos((wsb[j] >> (8 * (s >> 1))) & 0xFFu)));
-#pragma unroll
-          for (int i = 0; i < C::MI; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop[i], acc[j][i], 0, 0, 0);
-        }
-      }
-    }
-
-    stage_store<C>(nxt, creg, sreg, tid);   // (waits only for the staging loads issued above)
-    __syncthreads();
+    const int64_t t = st + C::NBUF - 1;
+    if (t < nstages) issue(t);
+    tile_step<FMT, BM>(tsm + (int)(st % C::NBUF) * C::STAGE, gcol, r, gq, wm, wn, acc);
+    sync((t < nstages ? t : nstages - 1) - (st + 1));
   }
 
   const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
@@ -240,7 +309,7 @@ __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_g
     const int64_t hrow = p.I / 2;
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) {
-      const int64_t m = row0 + wm * (BM / 2) + 16 * i + r;
+      const int64_t m = row0 + wm * 64 + 16 * i + r;
       const bool store = m < row_end;
       float h[4][4];
 #pragma unroll
@@ -298,7 +367,7 @@ __global__ __launch_bounds__(256, (FMT == kMX && BM == 128) ? 2 : 1) void tile_g
   const bool vec = (p.ldo & 3) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
-    const int64_t m = row0 + wm * (BM / 2) + 16 * i + r;
+    const int64_t m = row0 + wm * 64 + 16 * i + r;
     if (m >= row_end) continue;
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
@@ -342,14 +411,13 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
   const int64_t grid = ntiles * mblocks;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  static const char* names[2][2] = {{"tile_nvfp4_m128", "tile_nvfp4_m256"},
-                                    {"tile_mxfp4_m128", "tile_mxfp4_m256"}};
   *name = FUSE ? (FMT == kNV ? "tile_nvfp4_m128_swiglu" : "tile_mxfp4_m128_swiglu")
-               : names[FMT][BM == 256 ? 1 : 0];
+        : BM == 256 ? "tile_mxfp4_m256"
+                    : (FMT == kNV ? "tile_nvfp4_m128" : "tile_mxfp4_m128");
   if (p.K % kTBK != 0 || p.K <= 0) return hipErrorInvalidValue;
   if (FUSE && (p.I <= 0 || p.I % 128 != 0 || p.N != 2 * p.I || !p.h_codes || !p.h_scales))
     return hipErrorInvalidValue;
-  const size_t lds = 2 * (size_t)C::STAGE;
+  const size_t lds = C::LDS;
   static bool attr_set = false;  // once per instantiation (idempotent, so races are harmless)
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm<FMT, BM, FUSE>),
@@ -357,22 +425,21 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tile_gemm<FMT, BM, FUSE>), dim3((unsigned)grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((tile_gemm<FMT, BM, FUSE>), dim3((unsigned)grid), dim3(C::THREADS), lds, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_tiled(int fmt, int bm, const GemmParams& p, hipStream_t s,
-                             const char** name) {
-  // NVFP4 runs on fp16 MFMAs (four per 128-deep stage where MXFP4 needs one), so
-  // 128-row tiles already give it enough MFMA work per staged byte; 256-row NVFP4
-  // tiles would also exceed the register file.
+hipError_t launch_gemm_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name) {
   if (p.fuse_swiglu)
     return fmt == kNV ? launch_tile<kNV, 128, true>(p, s, name) : launch_tile<kMX, 128, true>(p, s, name);
-  if (fmt == kNV || bm != 256) return fmt == kNV ? launch_tile<kNV, 128, false>(p, s, name)
-                                                 : launch_tile<kMX, 128, false>(p, s, name);
-  return launch_tile<kMX, 256, false>(p, s, name);
+  if (fmt == kNV) return launch_tile<kNV, 128, false>(p, s, name);
+  // dense MXFP4 with enough 256 x 256 tiles to give every CU one: the 8-wave tile
+  const int64_t ntiles = (p.N + kTBN - 1) / kTBN;
+  if (!p.mblk_expert && ((p.M + 255) / 256) * ntiles >= 256)
+    return launch_tile<kMX, 256, false>(p, s, name);
+  return launch_tile<kMX, 128, false>(p, s, name);
 }
 
 }  // namespace fp4

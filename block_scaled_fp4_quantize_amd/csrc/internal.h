@@ -75,9 +75,9 @@ int64_t resident_lds_bytes(int fmt, int mt, int64_t K);
 bool resident_fits(int fmt, int mt, int64_t K);
 hipError_t launch_gemm_resident(int fmt, int mt, const GemmParams& p, hipStream_t s,
                                 const char** name);
-// tiled kernel for many activation rows (fp4 activations, K % 128 == 0), bm 128 or 256
-hipError_t launch_gemm_tiled(int fmt, int bm, const GemmParams& p, hipStream_t s,
-                             const char** name);
+// tiled kernel for many activation rows (fp4 activations, K % 128 == 0, 128-row
+// activation blocks)
+hipError_t launch_gemm_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name);
 
 // ---- MoE stages ------------------------------------------------------------------
 hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,

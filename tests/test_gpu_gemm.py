@@ -134,6 +134,24 @@ def test_tiled_shapes(fmt, shape):
                   prequant=True)
 
 
+# dense MXFP4 with at least 256 tiles of 256 x 256: the 8-wave 256-row tile, with K of
+# one and three stages (fewer than the copy pipeline holds) and of eight, ragged rows
+# and columns; the oracle checks the first and last 300 rows and 200 sampled ones
+TILED_256 = [(2300, 7324, 128), (2049, 7324, 384), (4096, 4096, 1024)]
+
+
+@pytest.mark.parametrize("shape", TILED_256)
+def test_tiled_256_shapes(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(sum(shape))
+    rows = np.unique(np.concatenate([np.arange(300), np.arange(M - 300, M),
+                                     rng.choice(M, 200, replace=False)]))
+    run_and_check("mxfp4", "w4a4", M, N, K, seed=sum(shape), rows=rows)
+    assert F.fp4_last_kernel() == "tile_mxfp4_m256"
+    run_and_check("mxfp4", "w4a4", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32,
+                  prequant=True, rows=rows)
+
+
 # at most 64 activation rows: the resident-activation kernel whenever the scale rows
 # are whole 16-byte pieces and the activations fit in LDS (ring of 8, 16 or 32 K
 # steps; K = 6144 refills the ring once), otherwise the streaming kernel
