@@ -1091,7 +1091,7 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   // a deep weight stream, when they fit; two-tile blocks measure faster on the
   // streaming kernel below
   if (fast && (!sel || c0 == 'r') && (one || c0 == 'r') &&
-      resident_fits(fmt, one ? 1 : 2, p.K))
+      resident_fits(fmt, one ? 1 : 2, p.mblk_expert ? 32 : p.M, p.N, p.K))
     return launch_gemm_resident(fmt, one ? 1 : 2, p, s, name);
   if (fast) {
     if (c0 == 's' && c1 == 'p') {

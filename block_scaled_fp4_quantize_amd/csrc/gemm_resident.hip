@@ -8,7 +8,11 @@
 // COLUMN); MXFP4 on the scaled FP4 MFMA, NVFP4 decoded exactly to fp16 ("vLLM on
 // the NVIDIA DGX Spark (GB10 / sm_121): A Complete Technical Guide", §6.1, §6.4).
 //
-// A workgroup owns 64 weight rows (16 per wave, whole K) and 16*MT activation rows.
+// A workgroup owns 16 * 4 / KSPLIT weight rows and 16*MT activation rows: its 4 waves
+// form 4 / KSPLIT row groups of 16 weight rows, each split over KSPLIT contiguous
+// ranges of K (one wave per range); the partial tiles are added through LDS in wave
+// order (bitwise reproducible).  Splitting K gives decode-sized N enough workgroups to
+// occupy every CU: N = 14336 is 224 workgroups at 64 rows, 448 at 32.
 //  * Activation codes, activation scales and the workgroup's weight scales for the
 //    whole K are copied into LDS once, by LDS-direct 16-byte loads (no registers).
 //  * Each wave keeps a ring of RING K-steps (128 elements, 16 bytes per lane) of
@@ -28,11 +32,12 @@
 //                                          are copied: padded rows of a partial
 //                                          tile feed output columns never stored.
 //   act scales  [K/G/16][16*MT rows][16]  16-byte groups of a row's scales, group-
-//   w scales    [K/G/16][64 rows][16]     major: a 16-byte global piece lands whole,
+//   w scales    [K/G/16][RROWS][16]       major: a 16-byte global piece lands whole,
 //                                          and one step's scale reads across 16
 //                                          rows are 16 bytes apart (distinct banks)
 // The two scale sections are padded to whole 1 KB copies: the lanes of a last,
 // partial copy write into the padding (copies of different waves are unordered).
+//   partials    [KSPLIT-1][4/KSPLIT][MT][64 lanes][16]  the K-split partial tiles
 #include "device.h"
 #include "internal.h"
 
@@ -43,13 +48,15 @@ namespace {
 #define FP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int kRStep = 128;   // K per step (one scaled MFMA, or four fp16 MFMAs)
-constexpr int kRRows = 64;    // weight rows per workgroup
 constexpr int kResPieces = 16;  // max 16-byte activation pieces staged per thread
 
-template <int FMT, int MT>
+template <int FMT, int MT, int KSPLIT = 1>
 struct ResCfg {
   static constexpr int G = FMT == kNV ? 16 : 32;
   static constexpr int AROWS = 16 * MT;
+  static constexpr int RG = 4 / KSPLIT;      // 16-row weight groups per workgroup
+  static constexpr int RROWS = 16 * RG;      // weight rows per workgroup
+  static_assert(KSPLIT == 1 || KSPLIT == 2 || KSPLIT == 4, "4 waves split K evenly");
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -84,7 +91,7 @@ struct StepOps {
 // padded LDS row stride of the activation codes
 __host__ __device__ constexpr int64_t res_astr(int64_t K) { return round_kb(K / 2) + 16; }
 
-template <int FMT, int MT>
+template <int FMT, int MT, int RROWS>
 __device__ __forceinline__ StepOps<MT> res_fetch(const uint8_t* __restrict__ a_lds,
                                                  const uint8_t* __restrict__ as_lds,
                                                  const uint8_t* __restrict__ ws_lds, int KS,
@@ -103,7 +110,7 @@ __device__ __forceinline__ StepOps<MT> res_fetch(const uint8_t* __restrict__ a_l
     const uint8_t* ap = as_lds + (sgrp * C::AROWS + ar) * 16 + sbyte;
     o.asb[t] = FMT == kMX ? (uint32_t)*ap : (uint32_t)*reinterpret_cast<const uint16_t*>(ap);
   }
-  const uint8_t* wp = ws_lds + (sgrp * kRRows + wrow) * 16 + sbyte;
+  const uint8_t* wp = ws_lds + (sgrp * RROWS + wrow) * 16 + sbyte;
   o.wsb = FMT == kMX ? (uint32_t)*wp : (uint32_t)*reinterpret_cast<const uint16_t*>(wp);
   return o;
 }
@@ -142,14 +149,14 @@ __device__ __forceinline__ void res_mma(const StepOps<MT>& o, uint32_t keep, u32
   }
 }
 
-template <int FMT, int MT, int RING>
+template <int FMT, int MT, int RING, int KSPLIT>
 __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
-  using C = ResCfg<FMT, MT>;
+  using C = ResCfg<FMT, MT, KSPLIT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t res_smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int64_t ntiles = (p.N + kRRows - 1) / kRRows;
+  const int64_t ntiles = (p.N + C::RROWS - 1) / C::RROWS;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
   int grp = 0;
@@ -170,7 +177,8 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
   const int astr = (int)res_astr(K);
   uint8_t* a_lds = res_smem;                                            // AROWS * astr
   uint8_t* as_lds = a_lds + (size_t)C::AROWS * astr;                    // AROWS * KS
-  uint8_t* ws_lds = as_lds + round_kb((int64_t)C::AROWS * KS);          // 64 * KS
+  uint8_t* ws_lds = as_lds + round_kb((int64_t)C::AROWS * KS);          // RROWS * KS
+  uint8_t* red_lds = ws_lds + round_kb((int64_t)C::RROWS * KS);         // partial tiles
   const uint8_t* wcodes = p.w_codes + grp * p.w_estride_codes;
   const uint8_t* wscales = p.w_scales + grp * p.w_estride_scales;
 
@@ -233,31 +241,35 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
       const int64_t g = pc / C::AROWS;
       lds_copy16(p.a_scales + act_src(rr) * KS + g * 16, as_lds + c * 1024);
     }
-    const int64_t wpieces = (int64_t)kRRows * (KS / 16);
+    const int64_t wpieces = (int64_t)C::RROWS * (KS / 16);
     for (int64_t c = wave; c * 64 < wpieces; c += 4) {
       int64_t pc = c * 64 + lane;
       if (pc >= wpieces) pc = wpieces - 1;
-      const int rr = (int)(pc % kRRows);
-      const int64_t g = pc / kRRows;
-      int64_t n = nt * kRRows + rr;
+      const int rr = (int)(pc % C::RROWS);
+      const int64_t g = pc / C::RROWS;
+      int64_t n = nt * C::RROWS + rr;
       if (n >= p.N) n = p.N - 1;
       lds_copy16(wscales + n * KS + g * 16, ws_lds + c * 1024);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- the weight ring: steps 0 .. RING-1 (steps past the end are clamped
-  // re-reads, multiplied by zero) ----
+  // ---- the weight ring: steps s0 .. s0+RING-1 of this wave's K range [s0, s1)
+  // (steps past the end are clamped re-reads, multiplied by zero) ----
   const int r = lane & 15;
   const int gq = lane >> 4;
-  const int wrow = wave * 16 + r;
-  const int64_t wn_raw = nt * kRRows + wrow;
+  const int rg = wave % C::RG;          // row group
+  const int kh = wave / C::RG;          // K range
+  const int64_t s0 = KSPLIT == 1 ? 0 : kh * NS / KSPLIT;                // NS >= KSPLIT
+  const int64_t s1 = KSPLIT == 1 ? NS : (kh + 1) * NS / KSPLIT;
+  const int wrow = rg * 16 + r;
+  const int64_t wn_raw = nt * C::RROWS + wrow;
   const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;   // padded rows: outputs not stored
   const uint8_t* wsrc = wcodes + wn * KB + gq * 16;
   u32x4 wq[RING];
 #pragma unroll
   for (int i = 0; i < RING; ++i)
-    wq[i] = *reinterpret_cast<const u32x4*>(wsrc + (i < NS ? i : NS - 1) * 64);
+    wq[i] = *reinterpret_cast<const u32x4*>(wsrc + (s0 + i < s1 ? s0 + i : s1 - 1) * 64);
   __builtin_amdgcn_sched_barrier(0);
   // every activation load and LDS-direct copy of this wave has landed once at most
   // RING loads remain
@@ -291,29 +303,31 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
   // The LDS operands of step j + 1 are fetched before the MFMAs of step j, and a
   // scheduling barrier closes every step: the lookahead stays at one step, which
   // keeps the ring, the operands and the accumulators in ordinary registers.
-  int64_t base = 0;
-  StepOps<MT> cur = res_fetch<FMT, MT>(a_lds, as_lds, ws_lds, KS, astr, 0, wrow, r, gq);
+  int64_t base = s0;
+  StepOps<MT> cur = res_fetch<FMT, MT, C::RROWS>(a_lds, as_lds, ws_lds, KS, astr, s0, wrow, r, gq);
   // full ring passes that refill: step base + i, then load step base + i + RING
-  for (; base + RING < NS; base += RING) {
+  for (; base + RING < s1; base += RING) {
 #pragma unroll
     for (int i = 0; i < RING; ++i) {
       const int64_t j = base + i;
-      const StepOps<MT> nxt = res_fetch<FMT, MT>(a_lds, as_lds, ws_lds, KS, astr, j + 1, wrow, r, gq);
+      const StepOps<MT> nxt =
+          res_fetch<FMT, MT, C::RROWS>(a_lds, as_lds, ws_lds, KS, astr, j + 1, wrow, r, gq);
       res_mma<FMT, MT>(cur, 0xFFFFFFFFu, wq[i], acc, i % kNAcc);
-      const int64_t jn = j + RING < NS ? j + RING : NS - 1;
+      const int64_t jn = j + RING < s1 ? j + RING : s1 - 1;
       wq[i] = *reinterpret_cast<const u32x4*>(wsrc + jn * 64);
       cur = nxt;
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // last pass: no refills; steps at or past NS contribute zero (operands of the
+  // last pass: no refills; steps at or past s1 contribute zero (operands of the
   // clamped last step)
 #pragma unroll
   for (int i = 0; i < RING; ++i) {
     const int64_t j = base + i;
-    const int64_t jn = j + 1 < NS ? j + 1 : NS - 1;
-    const StepOps<MT> nxt = res_fetch<FMT, MT>(a_lds, as_lds, ws_lds, KS, astr, jn, wrow, r, gq);
-    res_mma<FMT, MT>(cur, j < NS ? 0xFFFFFFFFu : 0u, wq[i], acc, i % kNAcc);
+    const int64_t jn = j + 1 < s1 ? j + 1 : s1 - 1;
+    const StepOps<MT> nxt =
+        res_fetch<FMT, MT, C::RROWS>(a_lds, as_lds, ws_lds, KS, astr, jn, wrow, r, gq);
+    res_mma<FMT, MT>(cur, j < s1 ? 0xFFFFFFFFu : 0u, wq[i], acc, i % kNAcc);
     cur = nxt;
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -329,13 +343,34 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
     sum[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
     asm volatile("" : "+v"(sum[t]));
   }
+  if (KSPLIT > 1) {
+    // the waves of K ranges 1.. park their partial tiles in LDS (a region no wave
+    // reads in its loop); the range-0 wave of each row group adds them in order
+    if (kh > 0) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        *reinterpret_cast<v4f*>(red_lds + ((((kh - 1) * C::RG + rg) * MT + t) * 64 + lane) * 16) =
+            sum[t];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kh > 0) return;   // uniform per wave
+#pragma unroll
+    for (int k = 1; k < KSPLIT; ++k)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        sum[t] += *reinterpret_cast<const v4f*>(
+            red_lds + ((((k - 1) * C::RG + rg) * MT + t) * 64 + lane) * 16);
+  }
 
   // a lane holds out[m][n .. n+3]: one 8-byte (bf16) or 16-byte (fp32) store when
   // the row stride and base allow it
   const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
   const bool vec = (p.ldo & 3) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.out) & (p.out_f32 ? 15 : 7)) == 0;
-  const int64_t n = nt * kRRows + wave * 16 + 4 * gq;
+  const int64_t n = nt * C::RROWS + rg * 16 + 4 * gq;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int64_t m = row0 + 16 * t + r;
@@ -369,59 +404,85 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
   }
 }
 
-template <int FMT, int MT, int RING>
+template <int FMT, int MT, int RING, int KSPLIT>
 hipError_t launch_res(const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ntiles = (p.N + kRRows - 1) / kRRows;
+  using C = ResCfg<FMT, MT, KSPLIT>;
+  const int64_t ntiles = (p.N + C::RROWS - 1) / C::RROWS;
   const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
   const int64_t grid = ntiles * mblocks;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (p.K / kRStep < KSPLIT) return hipErrorInvalidValue;
   static const char* names[2][2] = {{"resident_nvfp4_m16", "resident_nvfp4_m32"},
                                     {"resident_mxfp4_m16", "resident_mxfp4_m32"}};
   *name = names[FMT][MT - 1];
-  const int64_t lds = resident_lds_bytes(FMT, MT, p.K);
+  const int64_t lds = resident_lds_bytes(FMT, MT, KSPLIT, p.K);
   static bool attr_set = false;  // once per instantiation (idempotent)
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&resident_gemm<FMT, MT, RING>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kResidentMaxLds);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&resident_gemm<FMT, MT, RING, KSPLIT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kResidentMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((resident_gemm<FMT, MT, RING>), dim3((unsigned)grid), dim3(256),
+  hipLaunchKernelGGL((resident_gemm<FMT, MT, RING, KSPLIT>), dim3((unsigned)grid), dim3(256),
                      (size_t)lds, s, p);
   return hipGetLastError();
 }
 
-template <int FMT, int MT>
+// ring depth: the steps of one wave's K range, up to 32
+template <int FMT, int MT, int KSPLIT>
 hipError_t launch_res_ring(const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ns = p.K / kRStep;
-  if (ns >= 32) return launch_res<FMT, MT, 32>(p, s, name);
-  if (ns >= 16) return launch_res<FMT, MT, 16>(p, s, name);
-  return launch_res<FMT, MT, 8>(p, s, name);
+  const int64_t ns = p.K / kRStep / KSPLIT;
+  if (ns >= 32) return launch_res<FMT, MT, 32, KSPLIT>(p, s, name);
+  if (ns >= 16) return launch_res<FMT, MT, 16, KSPLIT>(p, s, name);
+  return launch_res<FMT, MT, 8, KSPLIT>(p, s, name);
+}
+
+template <int FMT, int MT>
+hipError_t launch_res_split(int ksplit, const GemmParams& p, hipStream_t s, const char** name) {
+  if (ksplit == 4) return launch_res_ring<FMT, MT, 4>(p, s, name);
+  if (ksplit == 2) return launch_res_ring<FMT, MT, 2>(p, s, name);
+  return launch_res_ring<FMT, MT, 1>(p, s, name);
 }
 
 }  // namespace
 
-int64_t resident_lds_bytes(int fmt, int mt, int64_t K) {
+int64_t resident_lds_bytes(int fmt, int mt, int ksplit, int64_t K) {
   const int64_t G = fmt == kNV ? 16 : 32;
   const int64_t arows = 16 * mt;
-  return arows * res_astr(K) + round_kb(arows * (K / G)) + round_kb(kRRows * (K / G));
+  const int64_t rrows = 64 / ksplit;
+  return arows * res_astr(K) + round_kb(arows * (K / G)) + round_kb(rrows * (K / G)) +
+         (int64_t)(ksplit - 1) * (4 / ksplit) * mt * 1024;
 }
 
-bool resident_fits(int fmt, int mt, int64_t K) {
+int resident_ksplit(int64_t M, int64_t N, int64_t K) {
+  // split K while the workgroups would not cover every CU twice and each wave keeps
+  // at least 8 steps; four ways only for at most 4 rows (measured at N = 14336,
+  // K = 4096: four ways is best for 1 row, two ways from 8 rows on)
+  const int64_t ns = K / kRStep;
+  const int kmax = M <= 4 ? 4 : 2;
+  int ks = 1;
+  while (ks < kmax && ns / (2 * ks) >= 8 && (N + 16 * (4 / ks) - 1) / (16 * (4 / ks)) < 512)
+    ks *= 2;
+  return ks;
+}
+
+bool resident_fits(int fmt, int mt, int64_t M, int64_t N, int64_t K) {
   const int64_t G = fmt == kNV ? 16 : 32;
   const int64_t pieces = 16 * mt * (K / 32);          // 16-byte activation pieces
   return K % kRStep == 0 && (K / G) % 16 == 0 && pieces <= 256 * kResPieces &&
-         resident_lds_bytes(fmt, mt, K) <= kResidentMaxLds;
+         resident_lds_bytes(fmt, mt, resident_ksplit(M, N, K), K) <= kResidentMaxLds;
 }
 
 hipError_t launch_gemm_resident(int fmt, int mt, const GemmParams& p, hipStream_t s,
                                 const char** name) {
-  if (!resident_fits(fmt, mt, p.K)) return hipErrorInvalidValue;
+  const int64_t rows = p.mblk_expert ? 16 * mt : p.M;   // rows per block, at most
+  if (!resident_fits(fmt, mt, rows, p.N, p.K)) return hipErrorInvalidValue;
+  const int ks = resident_ksplit(rows, p.N, p.K);
   if (fmt == kNV)
-    return mt == 1 ? launch_res_ring<kNV, 1>(p, s, name) : launch_res_ring<kNV, 2>(p, s, name);
-  return mt == 1 ? launch_res_ring<kMX, 1>(p, s, name) : launch_res_ring<kMX, 2>(p, s, name);
+    return mt == 1 ? launch_res_split<kNV, 1>(ks, p, s, name) : launch_res_split<kNV, 2>(ks, p, s, name);
+  return mt == 1 ? launch_res_split<kMX, 1>(ks, p, s, name) : launch_res_split<kMX, 2>(ks, p, s, name);
 }
 
 }  // namespace fp4

@@ -154,31 +154,44 @@ def test_tiled_256_shapes(shape):
 
 # at most 64 activation rows: the resident-activation kernel whenever the scale rows
 # are whole 16-byte pieces and the activations fit in LDS (ring of 8, 16 or 32 K
-# steps; K = 6144 refills the ring once), otherwise the streaming kernel
+# steps; K = 6144 refills the ring once), otherwise the streaming kernel.  The 4 waves
+# split K 1, 2 or 4 ways depending on M, N and K: (3, 40, 1024) one way, (16, 100,
+# 2048) two ways, (1, 300, 6144) four ways with 12 steps a wave, and (5, 72, 4352) and
+# (4, 72, 4352) (NVFP4) two even and four uneven ranges (8 and 9 steps)
 RESIDENT = [(1, 300, 6144), (16, 100, 2048), (17, 64, 768), (32, 520, 4096), (50, 70, 1536),
-            (64, 33, 512)]
+            (64, 33, 512), (3, 40, 1024), (5, 72, 4352), (4, 72, 4352)]
 
 
-def resident_expected(fmt, M, K):
+def resident_ksplit(M, N, K):
+    ns, ks, kmax = K // 128, 1, 4 if M <= 4 else 2
+    while ks < kmax and ns // (2 * ks) >= 8 and -(-N // (16 * (4 // ks))) < 512:
+        ks *= 2
+    return ks
+
+
+def resident_expected(fmt, M, N, K):
     G = 16 if fmt == "nvfp4" else 32
     if M > 16:
         return False    # two-tile blocks take the streaming kernel
-    mt = 1
+    mt, ks = 1, resident_ksplit(M, N, K)
     kb = lambda b: (b + 1023) // 1024 * 1024
-    lds = 16 * mt * K // 2 + kb(16 * mt * (K // G)) + kb(64 * (K // G))
-    return (K // G) % 16 == 0 and lds <= 160 * 1024
+    lds = (16 * mt * (kb(K // 2) + 16) + kb(16 * mt * (K // G)) + kb(64 // ks * (K // G))
+           + (ks - 1) * (4 // ks) * mt * 1024)
+    return K % 128 == 0 and (K // G) % 16 == 0 and lds <= 160 * 1024
 
 
 @pytest.mark.parametrize("shape", RESIDENT)
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_resident_shapes(fmt, shape):
     M, N, K = shape
+    if K % OQ.GROUP[fmt]:
+        pytest.skip("K not a multiple of the block size")
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 7)
     name = F.fp4_last_kernel()
-    if resident_expected(fmt, M, K):
+    if resident_expected(fmt, M, N, K):
         assert name == f"resident_{fmt}_m16", name
     else:
-        assert name.startswith("stream_"), name
+        assert name.startswith(("stream_", "rowblock_")), name
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 8, out_dtype=torch.float32,
                   prequant=True)
 
