@@ -56,6 +56,9 @@ struct ResCfg {
   static constexpr int AROWS = 16 * MT;
   static constexpr int RG = 4 / KSPLIT;      // 16-row weight groups per workgroup
   static constexpr int RROWS = 16 * RG;      // weight rows per workgroup
+  // activation rows staged in LDS: the four-way split serves at most 4 rows, which
+  // keeps its LDS small enough for all of its workgroups to be resident at once
+  static constexpr int ALDS = KSPLIT == 4 ? 4 : AROWS;
   static_assert(KSPLIT == 1 || KSPLIT == 2 || KSPLIT == 4, "4 waves split K evenly");
 };
 
@@ -91,7 +94,7 @@ struct StepOps {
 // padded LDS row stride of the activation codes
 __host__ __device__ constexpr int64_t res_astr(int64_t K) { return round_kb(K / 2) + 16; }
 
-template <int FMT, int MT, int RROWS>
+template <int FMT, int MT, int RROWS, int ALDS>
 __device__ __forceinline__ StepOps<MT> res_fetch(const uint8_t* __restrict__ a_lds,
                                                  const uint8_t* __restrict__ as_lds,
                                                  const uint8_t* __restrict__ ws_lds, int KS,
@@ -105,9 +108,10 @@ __device__ __forceinline__ StepOps<MT> res_fetch(const uint8_t* __restrict__ a_l
   const int sgrp = sb >> 4, sbyte = sb & 15;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    const int ar = 16 * t + r;
+    // operand rows past the staged ones re-read the last (outputs never stored)
+    const int ar = 16 * t + r < ALDS ? 16 * t + r : ALDS - 1;
     o.aq[t] = *reinterpret_cast<const u32x4*>(a_lds + ar * astr + jc * 64 + gq * 16);
-    const uint8_t* ap = as_lds + (sgrp * C::AROWS + ar) * 16 + sbyte;
+    const uint8_t* ap = as_lds + (sgrp * ALDS + ar) * 16 + sbyte;
     o.asb[t] = FMT == kMX ? (uint32_t)*ap : (uint32_t)*reinterpret_cast<const uint16_t*>(ap);
   }
   const uint8_t* wp = ws_lds + (sgrp * RROWS + wrow) * 16 + sbyte;
@@ -149,8 +153,11 @@ __device__ __forceinline__ void res_mma(const StepOps<MT>& o, uint32_t keep, u32
   }
 }
 
+// A four-way split has four times the workgroups of the unsplit kernel (896 for
+// N = 14336); asking for four workgroups per CU (at most 128 registers) keeps them all
+// resident at once instead of leaving a second, partial round.
 template <int FMT, int MT, int RING, int KSPLIT>
-__global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
+__global__ __launch_bounds__(256, KSPLIT == 4 ? 4 : 1) void resident_gemm(GemmParams p) {
   using C = ResCfg<FMT, MT, KSPLIT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t res_smem[];
   const int tid = threadIdx.x;
@@ -175,9 +182,9 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
   const int KS = (int)(K / C::G);
   const int64_t NS = K / kRStep;
   const int astr = (int)res_astr(K);
-  uint8_t* a_lds = res_smem;                                            // AROWS * astr
-  uint8_t* as_lds = a_lds + (size_t)C::AROWS * astr;                    // AROWS * KS
-  uint8_t* ws_lds = as_lds + round_kb((int64_t)C::AROWS * KS);          // RROWS * KS
+  uint8_t* a_lds = res_smem;                                            // ALDS * astr
+  uint8_t* as_lds = a_lds + (size_t)C::ALDS * astr;                     // ALDS * KS
+  uint8_t* ws_lds = as_lds + round_kb((int64_t)C::ALDS * KS);           // RROWS * KS
   uint8_t* red_lds = ws_lds + round_kb((int64_t)C::RROWS * KS);         // partial tiles
   const uint8_t* wcodes = p.w_codes + grp * p.w_estride_codes;
   const uint8_t* wscales = p.w_scales + grp * p.w_estride_scales;
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
   // are in flight): the rows_valid * K/32 16-byte pieces of the existing rows,
   // piece u * 256 + tid of this thread, rotated by the workgroup index (every
   // workgroup reads the same rows).  nper is uniform over the workgroup.
-  const uint32_t rows_valid = (uint32_t)(row_end - row0 < C::AROWS ? row_end - row0 : C::AROWS);
+  const uint32_t rows_valid = (uint32_t)(row_end - row0 < C::ALDS ? row_end - row0 : C::ALDS);
   const uint32_t ppr = (uint32_t)(KB / 16);       // pieces per row
   const uint32_t apieces = rows_valid * ppr;      // <= 256 * kResPieces (resident_fits)
   const int nper = (int)((apieces + 255) / 256);
@@ -233,12 +240,12 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
   // act scales and weight scales: 16-byte piece P = 64 c + lane of copy c is group
   // P / rows, row P % rows (KS % 16 == 0, so a row has KS / 16 whole groups)
   {
-    const int64_t apieces = (int64_t)C::AROWS * (KS / 16);
+    const int64_t apieces = (int64_t)C::ALDS * (KS / 16);
     for (int64_t c = wave; c * 64 < apieces; c += 4) {
       int64_t pc = c * 64 + lane;
       if (pc >= apieces) pc = apieces - 1;       // surplus lanes re-copy the last piece
-      const int rr = (int)(pc % C::AROWS);
-      const int64_t g = pc / C::AROWS;
+      const int rr = (int)(pc % C::ALDS);
+      const int64_t g = pc / C::ALDS;
       lds_copy16(p.a_scales + act_src(rr) * KS + g * 16, as_lds + c * 1024);
     }
     const int64_t wpieces = (int64_t)C::RROWS * (KS / 16);
@@ -304,14 +311,14 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
   // scheduling barrier closes every step: the lookahead stays at one step, which
   // keeps the ring, the operands and the accumulators in ordinary registers.
   int64_t base = s0;
-  StepOps<MT> cur = res_fetch<FMT, MT, C::RROWS>(a_lds, as_lds, ws_lds, KS, astr, s0, wrow, r, gq);
+  StepOps<MT> cur = res_fetch<FMT, MT, C::RROWS, C::ALDS>(a_lds, as_lds, ws_lds, KS, astr, s0, wrow, r, gq);
   // full ring passes that refill: step base + i, then load step base + i + RING
   for (; base + RING < s1; base += RING) {
 #pragma unroll
     for (int i = 0; i < RING; ++i) {
       const int64_t j = base + i;
       const StepOps<MT> nxt =
-          res_fetch<FMT, MT, C::RROWS>(a_lds, as_lds, ws_lds, KS, astr, j + 1, wrow, r, gq);
+          res_fetch<FMT, MT, C::RROWS, C::ALDS>(a_lds, as_lds, ws_lds, KS, astr, j + 1, wrow, r, gq);
       res_mma<FMT, MT>(cur, 0xFFFFFFFFu, wq[i], acc, i % kNAcc);
       const int64_t jn = j + RING < s1 ? j + RING : s1 - 1;
       wq[i] = *reinterpret_cast<const u32x4*>(wsrc + jn * 64);
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(256) void resident_gemm(GemmParams p) {
     const int64_t j = base + i;
     const int64_t jn = j + 1 < s1 ? j + 1 : s1 - 1;
     const StepOps<MT> nxt =
-        res_fetch<FMT, MT, C::RROWS>(a_lds, as_lds, ws_lds, KS, astr, jn, wrow, r, gq);
+        res_fetch<FMT, MT, C::RROWS, C::ALDS>(a_lds, as_lds, ws_lds, KS, astr, jn, wrow, r, gq);
     res_mma<FMT, MT>(cur, j < s1 ? 0xFFFFFFFFu : 0u, wq[i], acc, i % kNAcc);
     cur = nxt;
     __builtin_amdgcn_sched_barrier(0);
@@ -413,6 +420,7 @@ hipError_t launch_res(const GemmParams& p, hipStream_t s, const char** name) {
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (p.K / kRStep < KSPLIT) return hipErrorInvalidValue;
+  if (C::ALDS < C::AROWS && (p.mblk_expert || p.M > C::ALDS)) return hipErrorInvalidValue;
   static const char* names[2][2] = {{"resident_nvfp4_m16", "resident_nvfp4_m32"},
                                     {"resident_mxfp4_m16", "resident_mxfp4_m32"}};
   *name = names[FMT][MT - 1];
@@ -430,18 +438,24 @@ hipError_t launch_res(const GemmParams& p, hipStream_t s, const char** name) {
   return hipGetLastError();
 }
 
-// ring depth: the steps of one wave's K range, up to 32
+// ring depth: the steps of one wave's K range, up to 32 (8 for the four-way split,
+// whose 128-register budget holds no deeper ring)
 template <int FMT, int MT, int KSPLIT>
 hipError_t launch_res_ring(const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ns = p.K / kRStep / KSPLIT;
-  if (ns >= 32) return launch_res<FMT, MT, 32, KSPLIT>(p, s, name);
-  if (ns >= 16) return launch_res<FMT, MT, 16, KSPLIT>(p, s, name);
-  return launch_res<FMT, MT, 8, KSPLIT>(p, s, name);
+  if constexpr (KSPLIT == 4) {
+    return launch_res<FMT, MT, 8, KSPLIT>(p, s, name);
+  } else {
+    const int64_t ns = p.K / kRStep / KSPLIT;
+    if (ns >= 32) return launch_res<FMT, MT, 32, KSPLIT>(p, s, name);
+    if (ns >= 16) return launch_res<FMT, MT, 16, KSPLIT>(p, s, name);
+    return launch_res<FMT, MT, 8, KSPLIT>(p, s, name);
+  }
 }
 
 template <int FMT, int MT>
 hipError_t launch_res_split(int ksplit, const GemmParams& p, hipStream_t s, const char** name) {
-  if (ksplit == 4) return launch_res_ring<FMT, MT, 4>(p, s, name);
+  if constexpr (MT == 1)
+    if (ksplit == 4) return launch_res_ring<FMT, MT, 4>(p, s, name);
   if (ksplit == 2) return launch_res_ring<FMT, MT, 2>(p, s, name);
   return launch_res_ring<FMT, MT, 1>(p, s, name);
 }
@@ -450,7 +464,7 @@ hipError_t launch_res_split(int ksplit, const GemmParams& p, hipStream_t s, cons
 
 int64_t resident_lds_bytes(int fmt, int mt, int ksplit, int64_t K) {
   const int64_t G = fmt == kNV ? 16 : 32;
-  const int64_t arows = 16 * mt;
+  const int64_t arows = ksplit == 4 ? 4 : 16 * mt;   // staged activation rows
   const int64_t rrows = 64 / ksplit;
   return arows * res_astr(K) + round_kb(arows * (K / G)) + round_kb(rrows * (K / G)) +
          (int64_t)(ksplit - 1) * (4 / ksplit) * mt * 1024;
@@ -461,7 +475,7 @@ int resident_ksplit(int64_t M, int64_t N, int64_t K) {
   // at least 8 steps; four ways only for at most 4 rows (measured at N = 14336,
   // K = 4096: four ways is best for 1 row, two ways from 8 rows on)
   const int64_t ns = K / kRStep;
-  const int kmax = M <= 4 ? 4 : 2;
+  const int kmax = M <= 4 ? 4 : 2;   // (so two-tile blocks never split four ways)
   int ks = 1;
   while (ks < kmax && ns / (2 * ks) >= 8 && (N + 16 * (4 / ks) - 1) / (16 * (4 / ks)) < 512)
     ks *= 2;

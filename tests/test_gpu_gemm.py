@@ -175,7 +175,8 @@ def resident_expected(fmt, M, N, K):
         return False    # two-tile blocks take the streaming kernel
     mt, ks = 1, resident_ksplit(M, N, K)
     kb = lambda b: (b + 1023) // 1024 * 1024
-    lds = (16 * mt * (kb(K // 2) + 16) + kb(16 * mt * (K // G)) + kb(64 // ks * (K // G))
+    arows = 4 if ks == 4 else 16 * mt
+    lds = (arows * (kb(K // 2) + 16) + kb(arows * (K // G)) + kb(64 // ks * (K // G))
            + (ks - 1) * (4 // ks) * mt * 1024)
     return K % 128 == 0 and (K // G) % 16 == 0 and lds <= 160 * 1024
 
