@@ -550,489 +550,6 @@ hipError_t launch_stream(const GemmParams& p, hipStream_t s, const char** name) 
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------------
-// Split-K kernel for few activation rows, fp4 activations, K a multiple of 128.  A
-// workgroup owns 16 weight rows and 16*MT activation rows; its 4 waves take
-// contiguous quarters of K and reduce through LDS in wave order.  Each wave issues
-// the loads of up to 8 K-steps at once (weights, activations and their scales, all
-// unpredicated from clamped addresses), so with ~14 waves per CU the whole weight
-// matrix of a decode GEMM is requested within the first microseconds.
-// ---------------------------------------------------------------------------------
-constexpr int kBatch = 8;
-
-template <int FMT, int MT>
-struct SplitBatch {
-  uint4 w[kBatch];
-  uint32_t ws[kBatch];
-  uint4 a[kBatch][MT];
-  uint32_t as[kBatch][MT];
-};
-
-template <int FMT>
-__device__ __forceinline__ uint32_t load_scale_bytes(const uint8_t* srow, int64_t k0) {
-  if (FMT == kMX) return srow[k0 >> 5];
-  return *reinterpret_cast<const uint16_t*>(srow + (k0 >> 4));  // 2 e4m3 bytes, 2-aligned
-}
-
-template <int FMT, int MT>
-__device__ __forceinline__ void split_load(SplitBatch<FMT, MT>& b, const uint8_t* wrow,
-                                           const uint8_t* wsrow, const uint8_t* const (&arow)[MT],
-                                           const uint8_t* const (&asrow)[MT], int64_t s_begin,
-                                           int64_t s_end, int gq) {
-#pragma unroll
-  for (int j = 0; j < kBatch; ++j) {
-    int64_t s = s_begin + j;
-    if (s >= s_end) s = s_begin;  // clamp to a step of this batch (not computed)
-    const int64_t k0 = s * kKStep + gq * 32;
-    b.w[j] = *reinterpret_cast<const uint4*>(wrow + (k0 >> 1));
-    b.ws[j] = load_scale_bytes<FMT>(wsrow, k0);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      b.a[j][t] = *reinterpret_cast<const uint4*>(arow[t] + (k0 >> 1));
-      b.as[j][t] = load_scale_bytes<FMT>(asrow[t], k0);
-    }
-  }
-}
-
-// All kBatch steps are computed without branches (a branch per step lets the
-// compiler sink each step's loads into it, serializing them); steps at or past n
-// get an all-zero weight operand, which contributes exactly zero.
-template <int FMT, int MT>
-__device__ __forceinline__ void split_compute(const SplitBatch<FMT, MT>& b, int n, v4f (&acc)[MT]) {
-#pragma unroll
-  for (int j = 0; j < kBatch; ++j) {
-    const uint32_t keep = j < n ? 0xFFFFFFFFu : 0u;
-    const uint4 wj = make_uint4(b.w[j].x & keep, b.w[j].y & keep, b.w[j].z & keep, b.w[j].w & keep);
-    if (FMT == kMX) {
-      const v8i wop = {(int)wj.x, (int)wj.y, (int)wj.z, (int)wj.w, 0, 0, 0, 0};
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const v8i aop = {(int)b.a[j][t].x, (int)b.a[j][t].y, (int)b.a[j][t].z, (int)b.a[j][t].w,
-                         0, 0, 0, 0};
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop, aop, acc[t], 4, 4, 0,
-                                                                   (int)b.ws[j], 0, (int)b.as[j][t]);
-      }
-    } else {
-      const f16x2 ws_lo = f16_pair(e4m3_value_pos(b.ws[j] & 0xFFu));
-      const f16x2 ws_hi = f16_pair(e4m3_value_pos((b.ws[j] >> 8) & 0xFFu));
-      f16x2 as_lo[MT], as_hi[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        as_lo[t] = f16_pair(e4m3_value_pos(b.as[j][t] & 0xFFu));
-        as_hi[t] = f16_pair(e4m3_value_pos((b.as[j][t] >> 8) & 0xFFu));
-      }
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const f16x8 wop = decode8_f16(dword_of(wj, sub), sub < 2 ? ws_lo : ws_hi);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const f16x8 aop = decode8_f16(dword_of(b.a[j][t], sub), sub < 2 ? as_lo[t] : as_hi[t]);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t], 0, 0, 0);
-        }
-      }
-    }
-  }
-}
-
-template <int FMT, int MT>
-__global__ __launch_bounds__(256) void splitk_gemm(GemmParams p) {
-  constexpr int G = FMT == kNV ? 16 : 32;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int64_t ntiles = (p.N + 15) >> 4;
-  const int64_t mb = (int64_t)blockIdx.x / ntiles;
-  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
-  int grp = 0;
-  int64_t row0, row_end;
-  if (p.mblk_expert) {
-    grp = p.mblk_expert[mb];
-    if (grp < 0) return;  // uniform over the workgroup
-    row0 = p.mblk_row0[mb];
-    row_end = p.group_end[grp];
-  } else {
-    row0 = mb * (16 * MT);
-    row_end = p.M;
-  }
-  const int64_t K = p.K;
-  const int64_t KB = K >> 1;
-  const int64_t KS = K / G;
-  const int r = lane & 15;
-  const int gq = lane >> 4;
-  // padded rows are clamped to the last valid one (their outputs are not stored)
-  const int64_t wn_raw = nt * 16 + r;
-  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;
-  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
-  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
-  const uint8_t* arow[MT];
-  const uint8_t* asrow[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    int64_t pv = row0 + t * 16 + r;
-    if (pv >= row_end) pv = row_end - 1;
-    const int64_t src = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
-    arow[t] = p.a_codes + src * KB;
-    asrow[t] = p.a_scales + src * KS;
-  }
-
-  const int64_t nsteps = K / kKStep;
-  const int64_t per = (nsteps + 3) / 4;
-  const int64_t s0 = wave * per;
-  const int64_t s1 = s0 + per < nsteps ? s0 + per : nsteps;
-
-  v4f acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // one batch of up to 8 steps in registers at a time (K <= 4096 is one batch per
-  // wave); a single buffer keeps the register count low enough for ~4 waves per SIMD
-  for (int64_t s = s0; s < s1; s += kBatch) {
-    SplitBatch<FMT, MT> b;
-    split_load<FMT, MT>(b, wrow, wsrow, arow, asrow, s, s1, gq);
-    // all of the batch's loads are issued before the first MFMA waits for data
-    __builtin_amdgcn_sched_barrier(0);
-    split_compute<FMT, MT>(b, (int)((s1 - s) < kBatch ? (s1 - s) : kBatch), acc);
-  }
-
-  __shared__ float red[3][MT][64][4];
-  if (wave > 0) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave - 1][t][lane][v] = acc[t][v];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int64_t m = row0 + t * 16 + (lane & 15);
-    if (m >= row_end) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t n = nt * 16 + 4 * (lane >> 4) + v;
-      if (n >= p.N) continue;
-      float x = acc[t][v];
-      x += red[0][t][lane][v];
-      x += red[1][t][lane][v];
-      x += red[2][t][lane][v];
-      x *= alpha;
-      if (p.out_f32)
-        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
-    }
-  }
-}
-
-template <int FMT, int MT>
-hipError_t launch_splitk(const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ntiles = (p.N + 15) / 16;
-  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
-  const int64_t grid = ntiles * mblocks;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  *name = FMT == kNV ? (MT == 1 ? "splitk_nvfp4_m16" : "splitk_nvfp4_m32")
-                     : (MT == 1 ? "splitk_mxfp4_m16" : "splitk_mxfp4_m32");
-  hipLaunchKernelGGL((splitk_gemm<FMT, MT>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------------
-// Wide streaming kernel: the stream kernel's tiling (64 weight rows, activations
-// staged once per workgroup in LDS) with a 4096-wide K chunk, so each wave has all
-// 32 of its 16-byte weight loads per lane (and the scales) in flight at once and a
-// decode GEMM with K <= 4096 takes a single memory round trip.  Longer K loops
-// over 4096-wide chunks.
-// ---------------------------------------------------------------------------------
-constexpr int kWKC = 4096;
-constexpr int kWSteps = kWKC / kKStep;   // 32
-
-template <int FMT, int MT>
-struct WideCfg {
-  static constexpr int G = FMT == kNV ? 16 : 32;
-  static constexpr int AROWS = 16 * MT;
-  static constexpr int ASTR = kWKC / 2 + 16;    // padded LDS row stride of staged codes
-  static constexpr int SSTR = kWKC / G;         // scale bytes per staged row (128 / 256)
-  static constexpr int SDW = SSTR / 16;         // 16-byte scale loads per lane (8 / 16)
-  static constexpr int TPR = 256 / AROWS;       // staging threads per row (8 / 16)
-  static constexpr int CBT = (kWKC / 2) / TPR;  // code bytes staged per thread (256 / 128)
-  static constexpr int NCL = CBT / 16;          // 16-byte loads per staging thread (16 / 8)
-  static constexpr int SBT = SSTR / TPR;        // scale bytes staged per thread
-  static constexpr int NSW = SBT / 4;           // dwords (SBT is 8, 16 or 32)
-};
-
-template <int FMT, int MT>
-__global__ __launch_bounds__(256) void wide_gemm(GemmParams p) {
-  using C = WideCfg<FMT, MT>;
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[C::AROWS * C::ASTR];
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[C::AROWS * C::SSTR];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int64_t ntiles = (p.N + 63) >> 6;
-  const int64_t mb = (int64_t)blockIdx.x / ntiles;
-  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
-  int grp = 0;
-  int64_t row0, row_end;
-  if (p.mblk_expert) {
-    grp = p.mblk_expert[mb];
-    if (grp < 0) return;  // uniform over the workgroup
-    row0 = p.mblk_row0[mb];
-    row_end = p.group_end[grp];
-  } else {
-    row0 = mb * C::AROWS;
-    row_end = p.M;
-  }
-  const int64_t K = p.K;
-  const int64_t KB = K >> 1;
-  const int64_t KS = K / C::G;
-  const int r = lane & 15;
-  const int gq = lane >> 4;
-  const int64_t wn_raw = nt * 64 + wave * 16 + r;
-  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;   // padded rows: outputs not stored
-  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
-  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
-
-  const int srow = tid / C::TPR;
-  const int sseg = tid % C::TPR;
-  int64_t pv = row0 + srow;
-  if (pv >= row_end) pv = row_end - 1;  // row0 < row_end for every block
-  const int64_t s_src = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
-  const uint8_t* s_codes = p.a_codes + s_src * KB;
-  const uint8_t* s_scales = p.a_scales + s_src * KS;
-  const int64_t nchunks = (K + kWKC - 1) / kWKC;
-
-  v4f acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t c = 0; c < nchunks; ++c) {
-    if (c > 0) __syncthreads();  // every wave is done with the previous chunk's LDS
-    // 1. activation staging loads (issued first, so waiting for them leaves the
-    //    weight loads in flight)
-    uint4 stc[C::NCL];
-    uint32_t sts[C::NSW];
-    {
-      const int64_t kb0 = c * (kWKC / 2) + sseg * C::CBT;
-#pragma unroll
-      for (int i = 0; i < C::NCL; ++i) {
-        const int64_t off = kb0 + i * 16;
-        stc[i] = *reinterpret_cast<const uint4*>(s_codes + (off < KB ? off : 0));
-      }
-      const int64_t so = c * C::SSTR + sseg * C::SBT;
-#pragma unroll
-      for (int i = 0; i < C::NSW; ++i) {
-        const int64_t o = so + 4 * i;
-        sts[i] = *reinterpret_cast<const uint32_t*>(s_scales + (o < KS ? o : 0));
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // 2. all weight loads of the chunk (steps past K are clamped, not computed)
-    uint4 wq[kWSteps];
-    uint4 wsc[C::SDW];
-    {
-      const int64_t k0 = c * kWKC;
-#pragma unroll
-      for (int j = 0; j < kWSteps; ++j) {
-        const int64_t kk = k0 + j * kKStep + gq * 32;
-        wq[j] = *reinterpret_cast<const uint4*>(wrow + (kk < K ? (kk >> 1) : 0));
-      }
-      // scale rows are a multiple of 4 bytes; 16-byte loads where the row allows
-#pragma unroll
-      for (int i = 0; i < C::SDW; ++i) {
-        const int64_t so = c * C::SSTR + i * 16;
-        uint32_t d[4];
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int64_t o = so + 4 * q2;
-          d[q2] = *reinterpret_cast<const uint32_t*>(wsrow + (o < KS ? o : 0));
-        }
-        wsc[i] = make_uint4(d[0], d[1], d[2], d[3]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // 3. publish the activation chunk
-    {
-#pragma unroll
-      for (int i = 0; i < C::NCL; ++i)
-        *reinterpret_cast<uint4*>(a_lds + srow * C::ASTR + sseg * C::CBT + i * 16) = stc[i];
-#pragma unroll
-      for (int i = 0; i < C::NSW; ++i)
-        *reinterpret_cast<uint32_t*>(s_lds + srow * C::SSTR + sseg * C::SBT + 4 * i) = sts[i];
-    }
-    __syncthreads();
-    // 4. compute (steps past K get a zero weight operand: no branches)
-    const int64_t rem = (K - c * kWKC) / kKStep;
-    const uint32_t* wsd = reinterpret_cast<const uint32_t*>(wsc);
-#pragma unroll
-    for (int j = 0; j < kWSteps; ++j) {
-      const uint32_t keep = j < rem ? 0xFFFFFFFFu : 0u;
-      const uint4 wj = make_uint4(wq[j].x & keep, wq[j].y & keep, wq[j].z & keep, wq[j].w & keep);
-      if (FMT == kMX) {
-        const uint32_t wsb = (wsd[j] >> (8 * gq)) & 0xFFu;
-        const v8i wop = {(int)wj.x, (int)wj.y, (int)wj.z, (int)wj.w, 0, 0, 0, 0};
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const int ar = t * 16 + r;
-          const uint4 aq = *reinterpret_cast<const uint4*>(a_lds + ar * C::ASTR + j * 64 + gq * 16);
-          const uint32_t asb = s_lds[ar * C::SSTR + j * 4 + gq];
-          const v8i aop = {(int)aq.x, (int)aq.y, (int)aq.z, (int)aq.w, 0, 0, 0, 0};
-          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop, aop, acc[t], 4, 4, 0,
-                                                                     (int)wsb, 0, (int)asb);
-        }
-      } else {
-        const uint32_t wsd2 = (gq >> 1) ? wsd[2 * j + 1] : wsd[2 * j];
-        const uint32_t wsb = (wsd2 >> (16 * (gq & 1))) & 0xFFFFu;
-        const f16x2 ws_lo = f16_pair(e4m3_value_pos(wsb & 0xFFu));
-        const f16x2 ws_hi = f16_pair(e4m3_value_pos(wsb >> 8));
-        uint4 aq[MT];
-        f16x2 as_lo[MT], as_hi[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const int ar = t * 16 + r;
-          aq[t] = *reinterpret_cast<const uint4*>(a_lds + ar * C::ASTR + j * 64 + gq * 16);
-          const uint32_t asb = *reinterpret_cast<const uint16_t*>(s_lds + ar * C::SSTR + j * 8 + gq * 2);
-          as_lo[t] = f16_pair(e4m3_value_pos(asb & 0xFFu));
-          as_hi[t] = f16_pair(e4m3_value_pos(asb >> 8));
-        }
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-          const f16x8 wop = decode8_f16(dword_of(wj, sub), sub < 2 ? ws_lo : ws_hi);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            const f16x8 aop = decode8_f16(dword_of(aq[t], sub), sub < 2 ? as_lo[t] : as_hi[t]);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
-
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int64_t m = row0 + t * 16 + (lane & 15);
-    if (m >= row_end) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t n = nt * 64 + wave * 16 + 4 * (lane >> 4) + v;
-      if (n >= p.N) continue;
-      const float x = acc[t][v] * alpha;
-      if (p.out_f32)
-        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
-    }
-  }
-}
-
-template <int FMT, int MT>
-hipError_t launch_wide(const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ntiles = (p.N + 63) / 64;
-  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
-  const int64_t grid = ntiles * mblocks;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  *name = FMT == kNV ? (MT == 1 ? "wide_nvfp4_m16" : "wide_nvfp4_m32")
-                     : (MT == 1 ? "wide_mxfp4_m16" : "wide_mxfp4_m32");
-  hipLaunchKernelGGL((wide_gemm<FMT, MT>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------------
-// Direct streaming kernel (decode, fp4 activations, K a multiple of 128): 64 weight
-// rows per workgroup, 16 per wave over the full K, no LDS and no barriers.  Each
-// wave loads its activation fragments straight from global memory next to the
-// weights (the 4 waves of a workgroup read the same activation bytes, which the
-// caches absorb); batches of 8 K-steps with the next batch in flight.
-// ---------------------------------------------------------------------------------
-template <int FMT, int MT>
-__global__ __launch_bounds__(256) void direct_gemm(GemmParams p) {
-  constexpr int G = FMT == kNV ? 16 : 32;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int64_t ntiles = (p.N + 63) >> 6;
-  const int64_t mb = (int64_t)blockIdx.x / ntiles;
-  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
-  int grp = 0;
-  int64_t row0, row_end;
-  if (p.mblk_expert) {
-    grp = p.mblk_expert[mb];
-    if (grp < 0) return;  // uniform over the workgroup
-    row0 = p.mblk_row0[mb];
-    row_end = p.group_end[grp];
-  } else {
-    row0 = mb * (16 * MT);
-    row_end = p.M;
-  }
-  const int64_t K = p.K;
-  const int64_t KB = K >> 1;
-  const int64_t KS = K / G;
-  const int r = lane & 15;
-  const int gq = lane >> 4;
-  const int64_t wn_raw = nt * 64 + wave * 16 + r;
-  const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;   // padded rows: outputs not stored
-  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
-  const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
-  const uint8_t* arow[MT];
-  const uint8_t* asrow[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    int64_t pv = row0 + t * 16 + r;
-    if (pv >= row_end) pv = row_end - 1;
-    const int64_t src = p.a_gather ? (int64_t)p.a_gather[pv] : pv;
-    arow[t] = p.a_codes + src * KB;
-    asrow[t] = p.a_scales + src * KS;
-  }
-  const int64_t nsteps = K / kKStep;
-  v4f acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  SplitBatch<FMT, MT> bA, bB;
-  split_load<FMT, MT>(bA, wrow, wsrow, arow, asrow, 0, nsteps, gq);
-  for (int64_t s = 0; s < nsteps; s += 2 * kBatch) {
-    const int64_t s1 = s + kBatch;
-    split_load<FMT, MT>(bB, wrow, wsrow, arow, asrow, s1 < nsteps ? s1 : s, nsteps, gq);
-    __builtin_amdgcn_sched_barrier(0);
-    split_compute<FMT, MT>(bA, (int)((nsteps - s) < kBatch ? (nsteps - s) : kBatch), acc);
-    if (s1 >= nsteps) break;
-    const int64_t s2 = s1 + kBatch;
-    split_load<FMT, MT>(bA, wrow, wsrow, arow, asrow, s2 < nsteps ? s2 : s1, nsteps, gq);
-    __builtin_amdgcn_sched_barrier(0);
-    split_compute<FMT, MT>(bB, (int)((nsteps - s1) < kBatch ? (nsteps - s1) : kBatch), acc);
-  }
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int64_t m = row0 + t * 16 + (lane & 15);
-    if (m >= row_end) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t n = nt * 64 + wave * 16 + 4 * (lane >> 4) + v;
-      if (n >= p.N) continue;
-      const float x = acc[t][v] * alpha;
-      if (p.out_f32)
-        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
-    }
-  }
-}
-
-template <int FMT, int MT>
-hipError_t launch_direct(const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ntiles = (p.N + 63) / 64;
-  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
-  const int64_t grid = ntiles * mblocks;
-  if (grid == 0) return hipSuccess;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  *name = FMT == kNV ? (MT == 1 ? "direct_nvfp4_m16" : "direct_nvfp4_m32")
-                     : (MT == 1 ? "direct_mxfp4_m16" : "direct_mxfp4_m32");
-  hipLaunchKernelGGL((direct_gemm<FMT, MT>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
 template <int FMT, int AK, int MT>
 hipError_t launch_rowblock(const GemmParams& p, hipStream_t s, const char** name) {
   const int64_t ntiles = (p.N + 15) / 16;
@@ -1082,30 +599,13 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
     if (p.bm != 128 || !fast) return hipErrorInvalidValue;
     return launch_gemm_tiled(fmt, p, s, name);
   }
-  // measurement switch between the fp4-activation kernels (default: stream)
-  const char* sel = getenv("FP4_GEMM_KERNEL");
-  const char c0 = (fast && sel) ? sel[0] : 0, c1 = c0 ? sel[1] : 0;
-  if (fast && !sel && !p.mblk_expert && p.M > 64)
-    return launch_gemm_tiled(fmt, p, s, name);
+  if (fast && !p.mblk_expert && p.M > 64) return launch_gemm_tiled(fmt, p, s, name);
   // at most 16 rows (one 16-row activation tile): activations resident in LDS with
   // a deep weight stream, when they fit; two-tile blocks measure faster on the
   // streaming kernel below
-  if (fast && (!sel || c0 == 'r') && (one || c0 == 'r') &&
-      resident_fits(fmt, one ? 1 : 2, p.mblk_expert ? 32 : p.M, p.N, p.K))
-    return launch_gemm_resident(fmt, one ? 1 : 2, p, s, name);
+  if (fast && one && resident_fits(fmt, 1, p.M, p.N, p.K))
+    return launch_gemm_resident(fmt, 1, p, s, name);
   if (fast) {
-    if (c0 == 's' && c1 == 'p') {
-      if (fmt == kNV) return one ? launch_splitk<kNV, 1>(p, s, name) : launch_splitk<kNV, 2>(p, s, name);
-      return one ? launch_splitk<kMX, 1>(p, s, name) : launch_splitk<kMX, 2>(p, s, name);
-    }
-    if (c0 == 'w') {
-      if (fmt == kNV) return one ? launch_wide<kNV, 1>(p, s, name) : launch_wide<kNV, 2>(p, s, name);
-      return one ? launch_wide<kMX, 1>(p, s, name) : launch_wide<kMX, 2>(p, s, name);
-    }
-    if (c0 == 'd') {
-      if (fmt == kNV) return one ? launch_direct<kNV, 1>(p, s, name) : launch_direct<kNV, 2>(p, s, name);
-      return one ? launch_direct<kMX, 1>(p, s, name) : launch_direct<kMX, 2>(p, s, name);
-    }
     if (fmt == kNV) return one ? launch_stream<kNV, 1>(p, s, name) : launch_stream<kNV, 2>(p, s, name);
     return one ? launch_stream<kMX, 1>(p, s, name) : launch_stream<kMX, 2>(p, s, name);
   }

@@ -1,4 +1,4 @@
-// Decode-shaped block-scaled FP4 GEMM: few activation rows (at most 32 per
+// Decode-shaped block-scaled FP4 GEMM: few activation rows (one 16-row tile per
 // workgroup), fp4 activations, K a multiple of 128.  The weights are read exactly
 // once, so the kernel is bound by HBM bandwidth and its job is to keep as many
 // weight bytes in flight as the register file allows.
@@ -491,12 +491,14 @@ bool resident_fits(int fmt, int mt, int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_resident(int fmt, int mt, const GemmParams& p, hipStream_t s,
                                 const char** name) {
-  const int64_t rows = p.mblk_expert ? 16 * mt : p.M;   // rows per block, at most
-  if (!resident_fits(fmt, mt, rows, p.N, p.K)) return hipErrorInvalidValue;
+  // one 16-row activation tile per workgroup (two-tile blocks measured faster on the
+  // streaming kernel, so only MT = 1 is built)
+  if (mt != 1) return hipErrorInvalidValue;
+  const int64_t rows = p.mblk_expert ? 16 : p.M;   // rows per block, at most
+  if (!resident_fits(fmt, 1, rows, p.N, p.K)) return hipErrorInvalidValue;
   const int ks = resident_ksplit(rows, p.N, p.K);
-  if (fmt == kNV)
-    return mt == 1 ? launch_res_split<kNV, 1>(ks, p, s, name) : launch_res_split<kNV, 2>(ks, p, s, name);
-  return mt == 1 ? launch_res_split<kMX, 1>(ks, p, s, name) : launch_res_split<kMX, 2>(ks, p, s, name);
+  return fmt == kNV ? launch_res_split<kNV, 1>(ks, p, s, name)
+                    : launch_res_split<kMX, 1>(ks, p, s, name);
 }
 
 }  // namespace fp4

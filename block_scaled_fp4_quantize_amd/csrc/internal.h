@@ -68,8 +68,8 @@ bool gemm_can_fuse_swiglu(int akind, int64_t M, int64_t K, int64_t I, bool group
 int gemm_block_rows(int fmt, int akind, int64_t rows_per_group, int64_t H, int64_t I);
 hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
                        const char** name);
-// decode kernel with the activations resident in LDS (fp4 activations, 16*mt rows
-// per workgroup); usable when resident_fits()
+// decode kernel with the activations resident in LDS (fp4 activations, one 16-row
+// tile per workgroup: mt must be 1); usable when resident_fits()
 constexpr int64_t kResidentMaxLds = 160 * 1024;
 int64_t resident_lds_bytes(int fmt, int mt, int ksplit, int64_t K);
 int resident_ksplit(int64_t M, int64_t N, int64_t K);   // waves that split K: 1, 2 or 4
