@@ -25,7 +25,6 @@ namespace fp4 {
 namespace {
 
 constexpr int kTBK = 128;        // K per stage
-constexpr int kTBN = 256;        // weight rows per workgroup
 
 // Staged LDS layout of one K stage (no staging registers: global -> LDS copies).
 // Codes: unpadded 64-byte rows; the 16-byte column c of row x is stored at column
@@ -49,7 +48,10 @@ __device__ __forceinline__ int tile_srow(int slot) {   // inverse of tile_sslot
   return (slot & ~63) | ((slot & 3) << 4) | ((slot >> 2) & 15);
 }
 
-template <int FMT, int BM>
+// BM activation rows x BN weight rows per workgroup.  NVFP4 128 x 128 tiles take half
+// the registers of 128 x 256 ones, so two workgroups share a CU (as for MXFP4 at 128 x
+// 256) and one computes while the other waits.
+template <int FMT, int BM, int BN>
 struct TileCfg {
   static constexpr int G = FMT == kNV ? 16 : 32;
   static constexpr int SB = kTBK / G;                  // scale bytes per row per stage
@@ -57,8 +59,8 @@ struct TileCfg {
   static constexpr int WAVES = 2 * WM;                 // (two along the weight rows)
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int MI = 4;                         // 16-row activation tiles per wave
-  static constexpr int NJ = 8;                         // 16-row weight tiles per wave
-  static constexpr int ROWS = BM + kTBN;               // staged rows: activations, then weights
+  static constexpr int NJ = BN / 32;                   // 16-row weight tiles per wave
+  static constexpr int ROWS = BM + BN;                 // staged rows: activations, then weights
   static constexpr int CCOP = ROWS / 16;               // 1 KB code copies per stage
   static constexpr int CPW = CCOP / WAVES;             // ... per wave
   static constexpr int SDW = ROWS * SB / 4;            // scale words per stage
@@ -67,12 +69,13 @@ struct TileCfg {
   static constexpr int OPS = CPW + SPW;                // copies per wave per stage
   static constexpr int CODES = ROWS * 64;
   static constexpr int STAGE = CODES + WAVES * SPW * 256;  // bytes per LDS stage
-  // MXFP4 128-row tiles: two workgroups per CU (3 stages each); otherwise one
-  static constexpr int NBUF = (FMT == kMX && BM == 128) ? 3 : 4;
-  static constexpr int PER_CU = (FMT == kMX && BM == 128) ? 2 : 1;
+  // two workgroups per CU for the 4-wave tiles that fit in 256 registers: MXFP4 128 x
+  // 256 (3 stages each) and NVFP4 128 x 128 (4 stages each); otherwise one
+  static constexpr int PER_CU = (BM == 128 && (FMT == kMX || BN == 128)) ? 2 : 1;
+  static constexpr int NBUF = (PER_CU == 2 && BN == 256) ? 3 : 4;
   static constexpr int LDS = NBUF * STAGE;
   static_assert(CCOP % WAVES == 0, "code copies split evenly over the waves");
-  static_assert(BM % 128 == 0 && ROWS % 64 == 0, "64-row scale blocks, 128-row weight halves");
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "64-row scale blocks, 4-tile weight groups");
   static_assert(NBUF >= 3 && NBUF <= 4, "the stage waits cover up to two stages in flight");
   static_assert(PER_CU * LDS <= 160 * 1024, "LDS per CU");
   static_assert(THREADS == 2 * BM, "launch bounds of tile_gemm");
@@ -100,10 +103,11 @@ constexpr int tile_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4);
 
 // The MFMA work of one staged K step: fragment reads (codes at row * 64 + ccol, scales
 // at CODES + row * SB) and the MFMAs into acc.
-template <int FMT, int BM>
-__device__ __forceinline__ void tile_step(const uint8_t* cur, int ccol, int r, int gq, int wm, int wn,
-                                          v4f (&acc)[TileCfg<FMT, BM>::NJ][TileCfg<FMT, BM>::MI]) {
-  using C = TileCfg<FMT, BM>;
+template <int FMT, int BM, int BN>
+__device__ __forceinline__ void tile_step(
+    const uint8_t* cur, int ccol, int r, int gq, int wm, int wn,
+    v4f (&acc)[TileCfg<FMT, BM, BN>::NJ][TileCfg<FMT, BM, BN>::MI]) {
+  using C = TileCfg<FMT, BM, BN>;
   // fragments of this stage: weights (A operand) and activations (B operand).  The
   // scale word of tile j of this lane's row holds its 4 (MXFP4) or 2 (NVFP4 plane
   // gq / 2) block scales; the lane's own block starts at bit 8 gq or 16 (gq & 1).
@@ -115,10 +119,10 @@ __device__ __forceinline__ void tile_step(const uint8_t* cur, int ccol, int r, i
   const int ssh = FMT == kNV ? 16 * (gq & 1) : 8 * gq;
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j)
-    wf[j] = *reinterpret_cast<const uint4*>(cur + (BM + wn * 128 + 16 * j + r) * 64 + ccol);
+    wf[j] = *reinterpret_cast<const uint4*>(cur + (BM + wn * (BN / 2) + 16 * j + r) * 64 + ccol);
 #pragma unroll
   for (int k = 0; k < C::NJ / 4; ++k) {
-    const uint4 w4 = *reinterpret_cast<const uint4*>(sc + (BM + wn * 128 + 64 * k) * 4);
+    const uint4 w4 = *reinterpret_cast<const uint4*>(sc + (BM + wn * (BN / 2) + 64 * k) * 4);
     wsb[4 * k + 0] = w4.x >> ssh;
     wsb[4 * k + 1] = w4.y >> ssh;
     wsb[4 * k + 2] = w4.z >> ssh;
@@ -170,26 +174,27 @@ __device__ __forceinline__ void tile_step(const uint8_t* cur, int ccol, int r, i
 
 }
 
-// Each wave holds a 128 (weight rows) x 64 (activation rows) accumulator tile.  MXFP4
-// 128-row tiles fit in 256 registers, so two workgroups share a CU and one computes
-// while the other waits at a barrier; MXFP4 256-row tiles use 8 waves (two per SIMD)
-// on one CU, sharing each staged weight row between twice as many activation rows;
-// NVFP4 runs one 4-wave workgroup per CU (its decode needs more registers).
+// Each wave holds a BN/2 (weight rows) x 64 (activation rows) accumulator tile.
+// MXFP4 128 x 256 and NVFP4 128 x 128 tiles fit in 256 registers, so two workgroups
+// share a CU and one computes while the other waits at a barrier; MXFP4 256 x 256
+// tiles use 8 waves (two per SIMD) on one CU, sharing each staged weight row between
+// twice as many activation rows.
 // FUSE: the gate/up GEMM of an MoE expert with SwiGLU + requant in the epilogue.  The
-// workgroup's 256 weight rows are then 128 gate rows and the matching 128 up rows of
-// h columns [128 nt, 128 nt + 128): wave column wn takes h columns 64 wn + [0, 64),
-// its weight tiles 0-3 being the gate rows and 4-7 the up rows of the same columns,
-// so a lane holds gate and up of the same (m, h column) in registers.
-template <int FMT, int BM, bool FUSE>
-__global__ __launch_bounds__(2 * BM, (FMT == kMX && BM == 128) ? 2 : 1) void tile_gemm(GemmParams p) {
-  using C = TileCfg<FMT, BM>;
+// workgroup's BN weight rows are then BN/2 gate rows and the matching BN/2 up rows of
+// h columns [BN/2 nt, BN/2 nt + BN/2): wave column wn takes h columns BN/4 wn + [0,
+// BN/4), its weight tiles 0 .. NJ/2-1 being the gate rows and NJ/2 .. NJ-1 the up rows
+// of the same columns, so a lane holds gate and up of the same (m, h column).
+template <int FMT, int BM, int BN, bool FUSE>
+__global__ __launch_bounds__(2 * BM, (BM == 128 && (FMT == kMX || BN == 128)) ? 2 : 1) void
+tile_gemm(GemmParams p) {
+  using C = TileCfg<FMT, BM, BN>;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave % C::WM;
   const int wn = wave / C::WM;
-  const int64_t ntiles = (p.N + kTBN - 1) / kTBN;
+  const int64_t ntiles = (p.N + BN - 1) / BN;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
   int grp = 0;
@@ -219,11 +224,11 @@ __global__ __launch_bounds__(2 * BM, (FMT == kMX && BM == 128) ? 2 : 1) void til
     }
     int64_t n;
     if (FUSE) {
-      const int w = rr - BM, within = w & 127;
-      const int64_t col = nt * 128 + (w >> 7) * 64 + (within & 63);
-      n = within < 64 ? col : p.I + col;
+      const int w = rr - BM, within = w % (BN / 2);
+      const int64_t col = nt * (BN / 2) + (w / (BN / 2)) * (BN / 4) + within % (BN / 4);
+      n = within < BN / 4 ? col : p.I + col;
     } else {
-      n = nt * kTBN + (rr - BM);
+      n = nt * BN + (rr - BM);
     }
     return n < p.N ? n : p.N - 1;
   };
@@ -294,32 +299,35 @@ __global__ __launch_bounds__(2 * BM, (FMT == kMX && BM == 128) ? 2 : 1) void til
   for (int64_t st = 0; st < nstages; ++st) {
     const int64_t t = st + C::NBUF - 1;
     if (t < nstages) issue(t);
-    tile_step<FMT, BM>(tsm + (int)(st % C::NBUF) * C::STAGE, gcol, r, gq, wm, wn, acc);
+    tile_step<FMT, BM, BN>(tsm + (int)(st % C::NBUF) * C::STAGE, gcol, r, gq, wm, wn, acc);
     sync((t < nstages ? t : nstages - 1) - (st + 1));
   }
 
   const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
   if (FUSE) {
     // h = SiLU(alpha g) * (alpha u) for this lane's 4 consecutive h columns of each
-    // gate tile j; a quantization block (16 or 32 columns of one row) spans the lanes
-    // r, r + 16, r + 32, r + 48 (and, for MXFP4, gate tiles j and j + 1), so its amax is
-    // two lane exchanges away.  Every lane takes part in the exchanges; only rows
-    // that exist are stored.
+    // gate tile j (up tile j + NJ/2); a quantization block (16 or 32 columns of one
+    // row) spans the lanes r, r + 16, r + 32, r + 48 (and, for MXFP4, gate tiles j and
+    // j + 1), so its amax is two lane exchanges away.  Every lane takes part in the
+    // exchanges; only rows that exist are stored.
+    constexpr int NG = C::NJ / 2;   // gate tiles per wave
+    static_assert(NG % 2 == 0, "MXFP4 blocks pair gate tiles");
     const float g = p.h_grp_g ? p.h_grp_g[grp] : p.h_g;
     const int64_t hrow = p.I / 2;
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) {
       const int64_t m = row0 + wm * 64 + 16 * i + r;
       const bool store = m < row_end;
-      float h[4][4];
+      float h[NG][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NG; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) h[j][v] = swiglu1(acc[j][i][v] * alpha, acc[j + 4][i][v] * alpha);
-      const int64_t hc0 = nt * 128 + wn * 64 + 4 * gq;   // + 16 j: this lane's first column
+        for (int v = 0; v < 4; ++v) h[j][v] = swiglu1(acc[j][i][v] * alpha, acc[j + NG][i][v] * alpha);
+      // + 16 j: this lane's first column
+      const int64_t hc0 = nt * (BN / 2) + wn * (BN / 4) + 4 * gq;
       if (FMT == kNV) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NG; ++j) {
           float amax = fmaxf(fmaxf(fabsf(h[j][0]), fabsf(h[j][1])), fmaxf(fabsf(h[j][2]), fabsf(h[j][3])));
           amax = fmaxf(amax, __shfl_xor(amax, 16));
           amax = fmaxf(amax, __shfl_xor(amax, 32));
@@ -336,7 +344,7 @@ __global__ __launch_bounds__(2 * BM, (FMT == kMX && BM == 128) ? 2 : 1) void til
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
+        for (int j = 0; j < NG; j += 2) {
           float amax = 0.0f;
 #pragma unroll
           for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fmaxf(fabsf(h[j][v]), fabsf(h[j + 1][v])));
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(2 * BM, (FMT == kMX && BM == 128) ? 2 : 1) void til
     if (m >= row_end) continue;
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
-      const int64_t n = nt * kTBN + wn * 128 + 16 * j + 4 * gq;
+      const int64_t n = nt * BN + wn * (BN / 2) + 16 * j + 4 * gq;
       if (n >= p.N) continue;
       const float x0 = acc[j][i][0] * alpha, x1 = acc[j][i][1] * alpha;
       const float x2 = acc[j][i][2] * alpha, x3 = acc[j][i][3] * alpha;
@@ -403,43 +411,50 @@ __global__ __launch_bounds__(2 * BM, (FMT == kMX && BM == 128) ? 2 : 1) void til
   }
 }
 
-template <int FMT, int BM, bool FUSE>
+template <int FMT, int BM, int BN, bool FUSE>
 hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
-  using C = TileCfg<FMT, BM>;
-  const int64_t ntiles = (p.N + kTBN - 1) / kTBN;
+  using C = TileCfg<FMT, BM, BN>;
+  const int64_t ntiles = (p.N + BN - 1) / BN;
   const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + BM - 1) / BM;
   const int64_t grid = ntiles * mblocks;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  *name = FUSE ? (FMT == kNV ? "tile_nvfp4_m128_swiglu" : "tile_mxfp4_m128_swiglu")
-        : BM == 256 ? "tile_mxfp4_m256"
-                    : (FMT == kNV ? "tile_nvfp4_m128" : "tile_mxfp4_m128");
+  if (FMT == kNV)
+    *name = FUSE ? (BN == 128 ? "tile_nvfp4_m128_n128_swiglu" : "tile_nvfp4_m128_swiglu")
+                 : (BN == 128 ? "tile_nvfp4_m128_n128" : "tile_nvfp4_m128");
+  else
+    *name = FUSE ? "tile_mxfp4_m128_swiglu" : (BM == 256 ? "tile_mxfp4_m256" : "tile_mxfp4_m128");
   if (p.K % kTBK != 0 || p.K <= 0) return hipErrorInvalidValue;
   if (FUSE && (p.I <= 0 || p.I % 128 != 0 || p.N != 2 * p.I || !p.h_codes || !p.h_scales))
     return hipErrorInvalidValue;
   const size_t lds = C::LDS;
   static bool attr_set = false;  // once per instantiation (idempotent, so races are harmless)
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm<FMT, BM, FUSE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm<FMT, BM, BN, FUSE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tile_gemm<FMT, BM, FUSE>), dim3((unsigned)grid), dim3(C::THREADS), lds, s, p);
+  hipLaunchKernelGGL((tile_gemm<FMT, BM, BN, FUSE>), dim3((unsigned)grid), dim3(C::THREADS), lds,
+                     s, p);
   return hipGetLastError();
 }
+
+// NVFP4 weight-tile width (128: two workgroups per CU)
+constexpr int kNvTileN = 128;
 
 }  // namespace
 
 hipError_t launch_gemm_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name) {
-  if (p.fuse_swiglu)
-    return fmt == kNV ? launch_tile<kNV, 128, true>(p, s, name) : launch_tile<kMX, 128, true>(p, s, name);
-  if (fmt == kNV) return launch_tile<kNV, 128, false>(p, s, name);
+  if (fmt == kNV)
+    return p.fuse_swiglu ? launch_tile<kNV, 128, kNvTileN, true>(p, s, name)
+                         : launch_tile<kNV, 128, kNvTileN, false>(p, s, name);
+  if (p.fuse_swiglu) return launch_tile<kMX, 128, 256, true>(p, s, name);
   // dense MXFP4 with enough 256 x 256 tiles to give every CU one: the 8-wave tile
-  const int64_t ntiles = (p.N + kTBN - 1) / kTBN;
+  const int64_t ntiles = (p.N + 255) / 256;
   if (!p.mblk_expert && ((p.M + 255) / 256) * ntiles >= 256)
-    return launch_tile<kMX, 256, false>(p, s, name);
-  return launch_tile<kMX, 128, false>(p, s, name);
+    return launch_tile<kMX, 256, 256, false>(p, s, name);
+  return launch_tile<kMX, 128, 256, false>(p, s, name);
 }
 
 }  // namespace fp4

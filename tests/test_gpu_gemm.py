@@ -118,7 +118,7 @@ def test_mxfp4_w4a4_decode_full_size(decode_problem, M):
 
 
 # more than 64 activation rows and K % 128 == 0: the LDS-tiled kernel (128-row
-# tiles), with ragged rows and columns
+# tiles; 128 x 128 for NVFP4, 128 x 256 for MXFP4), with ragged rows and columns
 TILED = [(65, 40, 128), (130, 256, 1024), (200, 300, 512), (257, 513, 384), (64 + 128 + 1, 17, 256)]
 
 
@@ -129,7 +129,7 @@ def test_tiled_shapes(fmt, shape):
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape))
     name = F.fp4_last_kernel()
     assert name.startswith("tile_" + fmt), name
-    assert name.endswith("m128") or name.endswith("m128_k256"), name
+    assert name == {"nvfp4": "tile_nvfp4_m128_n128", "mxfp4": "tile_mxfp4_m128"}[fmt], name
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32,
                   prequant=True)
 
