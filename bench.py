@@ -329,16 +329,41 @@ def bench_moe(args, torch, F, fmt):
     wbytes_expert = 3 * H * I // 2 + 3 * H * I // G
     bytes_ = (touched + (1 if shared else 0)) * wbytes_expert + T_ * H * 2 * 2
     flops = 2.0 * 3 * H * I * (T_ * k + (T_ if shared else 0))
-    return {
+    # Roofline of the whole fp4_moe_grouped_gemm call (all of its launches on one
+    # stream, timed by the step graph's events): weight-streaming decode token counts
+    # against HBM, large token counts against the MFMA peak of the format's
+    # instruction (NVFP4: fp16 MFMA on the exact decode; MXFP4: FP4 MFMA).
+    if T_ * k >= 32 * E:
+        peak = 2500.0 if fmt == "nvfp4" else 10100.0
+        achieved = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "fp4_moe_grouped_gemm (whole call)",
+                "algorithmic_flops_per_call": flops, "avg_call_us": round(ms * 1e3, 2)}
+    else:
+        achieved = bytes_ / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                "frac": round(achieved / 8000.0, 4), "traffic": None,
+                "kernel": "fp4_moe_grouped_gemm (whole call)",
+                "algorithmic_bytes_per_call": bytes_, "avg_call_us": round(ms * 1e3, 2)}
+    res_cpu = None
+    if not args.no_cpu_baseline:
+        res_cpu = cpu_baseline_moe(fmt, hv, ids, w, w13c, w13s, w2c, w2s, s13, s2, sh, kw,
+                                   E, k, H, I)
+    out_line = {
         "metric": f"{fmt.upper()} MoE tokens/s (T={T_})", "value": round(T_ / (ms * 1e-3), 1),
         "unit": "tokens/s", "ms_per_step": ms, "steps_override": steps,
         "config": {"workload": f"{fmt.upper()} W4A4 MoE E={E} top-{k} H={H} I={I} T={T_}"
                                + (" + shared, Zipf(1.1)" if shared else ""),
                    "experts_touched": touched},
+        "roofline": roof,
         "achieved_GBps": round(bytes_ / (ms * 1e-3) / 1e9, 1),
         "achieved_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
         "wall_s_timed": wall,
     }
+    if res_cpu is not None:
+        out_line["cpu_baseline"] = res_cpu
+    return out_line
 
 
 # ---------------------------------------------------------------------------------
@@ -380,20 +405,20 @@ def cpu_baseline_decode(target_s=10.0, rows=2048):
                       f"{el:.1f} s: activation QDQ + float64 weight dequant + float64 matmul"}
 
 
-def cpu_baseline_prefill(target_s=10.0, rows=64):
+def cpu_baseline_prefill(target_s=10.0, rows=64, fmt="nvfp4"):
     import numpy as np
     import synth
     from oracle import gemm as OG
     from oracle import quant as OQ
     M, N, K = 8192, 4096, 4096
     w = synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT)
-    wc, ws, ws2 = OQ.quantize_weight("nvfp4", w)
+    wc, ws, ws2 = OQ.quantize_weight(fmt, w)
     _, av = synth.bf16_bits(synth.normal((M, K), seed=0, role=synth.ACT, index=3))
-    s = float(np.float32(np.abs(av).max()) / np.float32(2688.0))
+    s = float(np.float32(np.abs(av).max()) / np.float32(2688.0)) if fmt == "nvfp4" else 1.0
     n = 0
     t0 = time.perf_counter()
     while True:
-        OG.gemm_fused("nvfp4", av[n * rows % M:(n * rows % M) + rows], wc, ws, ws2, s)
+        OG.gemm_fused(fmt, av[n * rows % M:(n * rows % M) + rows], wc, ws, ws2, s)
         n += 1
         el = time.perf_counter() - t0
         if el >= target_s:
@@ -403,6 +428,49 @@ def cpu_baseline_prefill(target_s=10.0, rows=64):
             "kind": "oracle",
             "sample": f"{rows}-row slices of the 8192 activation rows against the full weight, "
                       f"{n} repetitions in {el:.1f} s"}
+
+
+def cpu_baseline_moe(fmt, hv, ids, w, w13c, w13s, w2c, w2s, s13, s2, sh, kw, E, k, H, I,
+                     target_s=10.0):
+    """The oracle MoE layer over the first tokens of the same problem (same routing,
+    the same expert codes and scales copied to the host), token by token, for about
+    target_s seconds."""
+    import numpy as np
+    from oracle import moe as OM
+    ids_h = ids.cpu().numpy()
+    w_h = w.cpu().numpy().astype(np.float64)
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            kwe = {}
+            if fmt == "nvfp4":
+                kwe = dict(w13_scale_2=float(s13[e]), w2_scale_2=float(s2[e]),
+                           a13_scale=float(kw["a13_scale"][e]), a2_scale=float(kw["a2_scale"][e]))
+            cache[e] = OM.Expert(w13c[e].cpu().numpy(), w13s[e].cpu().numpy(),
+                                 w2c[e].cpu().numpy(), w2s[e].cpu().numpy(), **kwe)
+        return cache[e]
+
+    # experts the sampled token does not reach carry no weights, only valid scales
+    idle = OM.Expert(None, None, None, None, a13_scale=1.0, a2_scale=1.0)
+    shared = None
+    if sh is not None:
+        shared = OM.Expert(sh["w13_codes"].cpu().numpy(), sh["w13_scales"].cpu().numpy(),
+                           sh["w2_codes"].cpu().numpy(), sh["w2_scales"].cpu().numpy())
+    n = 0
+    el = 0.0
+    while el < target_s and n < hv.shape[0]:
+        experts = {int(e): expert(int(e)) for e in ids_h[n]}      # host copies, untimed
+        full = [experts.get(e, idle) for e in range(E)]
+        t0 = time.perf_counter()
+        OM.moe(fmt, "w4a4", hv[n:n + 1], ids_h[n:n + 1], w_h[n:n + 1], full, shared)
+        el += time.perf_counter() - t0
+        n += 1
+    return {"value": round(n / el, 4), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"the first {n} tokens one at a time ({n} x {k} routed experts"
+                      + (" + the shared expert" if sh is not None else "")
+                      + f", H={H}, I={I}) in {el:.1f} s of oracle time"}
 
 
 def main():
@@ -444,8 +512,9 @@ def main():
     if not args.no_cpu_baseline:
         if args.workload == "decode":
             line["cpu_baseline"] = cpu_baseline_decode()
-        elif args.workload == "prefill":
-            line["cpu_baseline"] = cpu_baseline_prefill()
+        elif args.workload in ("prefill", "prefill-mxfp4"):
+            line["cpu_baseline"] = cpu_baseline_prefill(
+                fmt="nvfp4" if args.workload == "prefill" else "mxfp4")
     print(json.dumps(line), flush=True)
 
 
