@@ -573,8 +573,11 @@ hipError_t launch_rowblock(const GemmParams& p, hipStream_t s, const char** name
 }  // namespace
 
 int gemm_block_rows(int /*fmt*/, int akind, int64_t rows_per_group, int64_t H, int64_t I) {
+  // experts averaging at least 48 rows: 128-row tiles; at most 16: one 16-row tile per
+  // block (half the activation decode and MFMA work of a 32-row block); else 32
   const bool tiled = akind == kA_FP4 && H % kKStep == 0 && I % kKStep == 0;
-  return (tiled && rows_per_group >= 48) ? 128 : 32;
+  if (tiled && rows_per_group >= 48) return 128;
+  return rows_per_group <= 16 ? 16 : 32;
 }
 
 bool gemm_can_fuse_swiglu(int akind, int64_t M, int64_t K, int64_t I, bool grouped, int bm) {
@@ -590,12 +593,12 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
     return launch_gemm_tiled(fmt, p, s, name);
   }
   // row blocks of 32 (two 16-row activation tiles); dense problems of at most 16
-  // rows use one tile
-  const bool one = !p.mblk_expert && p.M <= 16;
+  // rows, and expert tables of 16-row blocks, use one tile
+  const bool one = p.mblk_expert ? p.bm == 16 : p.M <= 16;
   // fp4 activations with K a multiple of 128 take the streaming kernel, or the
   // LDS-tiled one when there are many activation rows
   const bool fast = akind == kA_FP4 && p.K % kKStep == 0;
-  if (p.mblk_expert && p.bm != 32) {
+  if (p.mblk_expert && p.bm != 32 && p.bm != 16) {
     if (p.bm != 128 || !fast) return hipErrorInvalidValue;
     return launch_gemm_tiled(fmt, p, s, name);
   }

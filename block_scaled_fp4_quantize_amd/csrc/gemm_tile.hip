@@ -69,10 +69,13 @@ struct TileCfg {
   static constexpr int OPS = CPW + SPW;                // copies per wave per stage
   static constexpr int CODES = ROWS * 64;
   static constexpr int STAGE = CODES + WAVES * SPW * 256;  // bytes per LDS stage
-  // two workgroups per CU for the 4-wave tiles that fit in 256 registers: MXFP4 128 x
-  // 256 (3 stages each) and NVFP4 128 x 128 (4 stages each); otherwise one
-  static constexpr int PER_CU = (BM == 128 && (FMT == kMX || BN == 128)) ? 2 : 1;
-  static constexpr int NBUF = (PER_CU == 2 && BN == 256) ? 3 : 4;
+  // workgroups per CU (the register budget follows from it: 512 / (PER_CU * WAVES /
+  // 4) per lane): 4-wave tiles that fit in 256 registers run two per CU (MXFP4 128 x
+  // 256, NVFP4 128 x 128), MXFP4 128 x 128 three; 8-wave tiles one.  Four stages
+  // in LDS when they fit next to the other workgroups, else three.
+  static constexpr int PER_CU =
+      BM == 128 ? (BN == 128 ? (FMT == kMX ? 3 : 2) : (FMT == kMX ? 2 : 1)) : 1;
+  static constexpr int NBUF = PER_CU * 4 * STAGE <= 160 * 1024 ? 4 : 3;
   static constexpr int LDS = NBUF * STAGE;
   static_assert(CCOP % WAVES == 0, "code copies split evenly over the waves");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "64-row scale blocks, 4-tile weight groups");
@@ -185,8 +188,7 @@ __device__ __forceinline__ void tile_step(
 // BN/4), its weight tiles 0 .. NJ/2-1 being the gate rows and NJ/2 .. NJ-1 the up rows
 // of the same columns, so a lane holds gate and up of the same (m, h column).
 template <int FMT, int BM, int BN, bool FUSE>
-__global__ __launch_bounds__(2 * BM, (BM == 128 && (FMT == kMX || BN == 128)) ? 2 : 1) void
-tile_gemm(GemmParams p) {
+__global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_gemm(GemmParams p) {
   using C = TileCfg<FMT, BM, BN>;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   const int tid = threadIdx.x;
