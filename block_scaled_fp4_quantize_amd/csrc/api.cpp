@@ -426,7 +426,7 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
   float* alpha13 = scal + E;
   float* g2 = scal + 2 * E;
   float* alpha2 = scal + 3 * E;
-  {
+  if (nv) {   // (MXFP4 reads none of them: alpha and the block-scale rule are fixed)
     std::vector<float> h(4 * (size_t)E, 1.0f);
     for (int64_t x = 0; x < E; ++x) {
       if (nv) {

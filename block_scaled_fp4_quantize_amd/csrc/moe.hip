@@ -240,6 +240,70 @@ __global__ __launch_bounds__(kPermuteChunk) void permute_scatter_kernel(PermuteP
   p.src_token[pos] = (int32_t)(i / p.k);
 }
 
+// ---- dispatch for at most kScanThreads slots (decode token counts): counts,
+// offsets, the row-block table and the scatter in one workgroup, the same results
+// as the three kernels above --------------------------------------------------------
+__global__ __launch_bounds__(kScanThreads) void permute_small_kernel(PermuteParams p) {
+  __shared__ int buf[kScanThreads];
+  __shared__ __attribute__((aligned(16))) int ids[kScanThreads];
+  __shared__ int cnt[1024];
+  __shared__ int ebase[1024];
+  __shared__ int total_mb;
+  const int tid = threadIdx.x;
+  const int n = (int)(p.T * p.k);   // <= kScanThreads
+  const int E = (int)p.E;           // <= 1024
+  int e = -1;
+  if (tid < n) {
+    e = p.ids[tid];
+    if (e < 0 || e >= E) e = -1;
+  }
+  ids[tid] = e;
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+  if (e >= 0) atomicAdd(&cnt[e], 1);
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  const int off = block_exclusive_scan(c, buf);
+  if (tid < E) {
+    p.expert_offsets[tid] = off;
+    p.group_end[tid] = off + c;
+    ebase[tid] = off;
+  }
+  if (tid == E - 1) p.expert_offsets[E] = off + c;
+  const int nmb = (c + p.bm - 1) / p.bm;
+  const int mbo = block_exclusive_scan(nmb, buf);
+  if (tid == kScanThreads - 1) total_mb = mbo + nmb;
+  if (tid < E) {
+    for (int j = 0; j < nmb; ++j) {
+      p.mblk_expert[mbo + j] = tid;
+      p.mblk_row0[mbo + j] = off + j * p.bm;
+    }
+  }
+  __syncthreads();
+  for (int64_t i = total_mb + tid; i < p.n_mblocks; i += kScanThreads) {
+    p.mblk_expert[i] = -1;
+    p.mblk_row0[i] = 0;
+  }
+  if (tid >= n) return;
+  if (e < 0) {
+    p.inverse[tid] = -1;
+    return;
+  }
+  // earlier slots routed to the same expert, four at a time
+  int rank = 0;
+  const int4* ids4 = reinterpret_cast<const int4*>(ids);
+  for (int q = 0; q < (tid >> 2); ++q) {
+    const int4 v = ids4[q];
+    rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+  }
+  for (int s2 = tid & ~3; s2 < tid; ++s2) rank += ids[s2] == e;
+  const int pos = ebase[e] + rank;
+  p.sorted_rows[pos] = tid;
+  p.inverse[tid] = pos;
+  p.row_expert[pos] = e;
+  p.src_token[pos] = (int32_t)(tid / p.k);
+}
+
 // ---- SwiGLU + requant: one lane = 8 consecutive intermediate columns -----------
 template <int FMT, bool W4A16>
 __global__ __launch_bounds__(256) void swiglu_kernel(SwigluParams p) {
@@ -356,6 +420,11 @@ hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,
 hipError_t launch_permute(const PermuteParams& p, hipStream_t s, const char** name) {
   *name = "permute";
   const int64_t n = p.T * p.k;
+  if (p.E > 1024) return hipErrorInvalidValue;
+  if (n <= kScanThreads) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kScanThreads), 0, s, p);
+    return hipGetLastError();
+  }
   const int64_t nchunks = (n + kPermuteChunk - 1) / kPermuteChunk;
   if (nchunks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (nchunks > 0) {
