@@ -35,17 +35,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Magnitude code (0..7) of the e2m1 value nearest to y >= 0, ties to the even code,
-// values above 6 saturating to code 7.  The thresholds are the midpoints between
-// neighbouring e2m1 values {0, .5, 1, 1.5, 2, 3, 4, 6}; a midpoint goes to the
-// neighbour whose mantissa bit is 0 (strict '>' where that is the lower one,
-// '>=' where it is the upper one).
-__device__ __forceinline__ uint32_t e2m1_mag_code(float y) {
-  return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
-         (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
-         (uint32_t)(y > 5.0f);
-}
-
 // e4m3fn code of sf >= 0 (finite or +inf): round to nearest even, saturating at 448
 // (code 0x7E).  Normal range: keep 3 mantissa bits of the fp32 pattern with
 // round-half-even at bit 20 and rebias the exponent (127 -> 7).  Below 2^-6 the
@@ -73,13 +62,14 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
 // ---- one quantization block, given its amax ---------------------------------------
 // NVFP4 (activation quantizer order): sf = fp32(fp32(amax * g) / 6) -> e4m3 code sc
 // (RNE, saturating); elements are scaled by r = fp32(g / scale).  A zero scale gives
-// r = 0, for which q_nv_code returns magnitude 0 with the sign kept (e2m1 of 0).
+// r = 0, for which q_nv_pack2 gives magnitude 0 with the sign kept (e2m1 of 0).
 __device__ __forceinline__ uint32_t q_nv_scale(float amax, float g, float* r);
-__device__ __forceinline__ uint32_t q_nv_code(float v, float r);
+__device__ __forceinline__ uint32_t q_nv_pack2(float v0, float v1, float r);
 // MXFP4 (OCP MX): E = clamp(floor(log2 amax) - 2, -127, 127), code E + 127, read off
 // the exponent field (zero and subnormal amax give code 0); elements are v * 2^-E.
 __device__ __forceinline__ uint32_t q_mx_scale(float amax, int* E);
-__device__ __forceinline__ uint32_t q_mx_code(float v, int E);
+__device__ __forceinline__ uint32_t q_mx_pack2(float v0, float v1, int E);
+// (q_*_pack2: the codes of two elements in one byte, the first in the low nibble)
 
 // Value 2^(c-127) of an e8m0 code (c = 0 gives the fp32 subnormal 2^-127).
 __device__ __forceinline__ float e8m0_value(uint32_t c) {
@@ -170,8 +160,19 @@ __device__ __forceinline__ uint32_t q_nv_scale(float amax, float g, float* r) {
   *r = sd != 0.0f ? g / sd : 0.0f;
   return sc;
 }
-__device__ __forceinline__ uint32_t q_nv_code(float v, float r) {
-  return e2m1_mag_code(fabsf(v) * r) | ((__float_as_uint(v) >> 31) << 3);
+// Two e2m1 codes in one byte (low nibble y0), by gfx950's fp32 -> fp4 conversion at
+// unit scale: the magnitude is the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, a midpoint
+// going to the neighbour with mantissa bit 0, values above 6 saturating to 6; the sign
+// bit is y's (so -0 and small negatives give 0x8).  Checked on the device against
+// that rule for every midpoint and its neighbouring floats, both signs, zeros,
+// infinities and subnormals; NaN, outside the quantizers' contract, comes out as 6.
+// The upper bytes of the result are zero.
+__device__ __forceinline__ uint32_t e2m1_pack2(float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0);
+}
+// elements times r (r >= 0: the product keeps the element's sign)
+__device__ __forceinline__ uint32_t q_nv_pack2(float v0, float v1, float r) {
+  return e2m1_pack2(v0 * r, v1 * r);
 }
 __device__ __forceinline__ uint32_t q_mx_scale(float amax, int* E) {
   const uint32_t eb = (__float_as_uint(amax) >> 23) & 0xFFu;
@@ -179,7 +180,8 @@ __device__ __forceinline__ uint32_t q_mx_scale(float amax, int* E) {
   *E = code - 127;
   return (uint32_t)code;
 }
-__device__ __forceinline__ uint32_t q_mx_code(float v, int E) {
-  return e2m1_mag_code(ldexpf(fabsf(v), -E)) | ((__float_as_uint(v) >> 31) << 3);
+// elements times 2^-E, exactly (|v| * 2^-E < 8 for the block's E)
+__device__ __forceinline__ uint32_t q_mx_pack2(float v0, float v1, int E) {
+  return e2m1_pack2(ldexpf(v0, -E), ldexpf(v1, -E));
 }
 }  // namespace fp4

@@ -335,9 +335,7 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           float rs;
           const uint32_t sc = q_nv_scale(amax, g, &rs);
-          uint32_t q = 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) q |= q_nv_code(h[j][v], rs) << (4 * v);
+          const uint32_t q = q_nv_pack2(h[j][0], h[j][1], rs) | (q_nv_pack2(h[j][2], h[j][3], rs) << 8);
           if (store) {
             const int64_t hc = hc0 + 16 * j;
             *reinterpret_cast<uint16_t*>(p.h_codes + m * hrow + hc / 2) = (uint16_t)q;
@@ -354,12 +352,9 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           int E;
           const uint32_t sc = q_mx_scale(amax, &E);
-          uint32_t q0 = 0, q1 = 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            q0 |= q_mx_code(h[j][v], E) << (4 * v);
-            q1 |= q_mx_code(h[j + 1][v], E) << (4 * v);
-          }
+          const uint32_t q0 = q_mx_pack2(h[j][0], h[j][1], E) | (q_mx_pack2(h[j][2], h[j][3], E) << 8);
+          const uint32_t q1 =
+              q_mx_pack2(h[j + 1][0], h[j + 1][1], E) | (q_mx_pack2(h[j + 1][2], h[j + 1][3], E) << 8);
           if (store) {
             const int64_t hc = hc0 + 16 * j;
             *reinterpret_cast<uint16_t*>(p.h_codes + m * hrow + hc / 2) = (uint16_t)q0;

@@ -347,12 +347,12 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluParams p) {
     float r;
     sc = q_nv_scale(amax, g, &r);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= q_nv_code(h[i], r) << (4 * i);
+    for (int i = 0; i < 4; ++i) packed |= q_nv_pack2(h[2 * i], h[2 * i + 1], r) << (8 * i);
   } else {
     int E;
     sc = q_mx_scale(amax, &E);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= q_mx_code(h[i], E) << (4 * i);
+    for (int i = 0; i < 4; ++i) packed |= q_mx_pack2(h[2 * i], h[2 * i + 1], E) << (8 * i);
   }
   *reinterpret_cast<uint32_t*>(p.h_codes + row * (p.I / 2) + kc * 4) = packed;
   if ((kc & (LPG - 1)) == 0) {
