@@ -58,6 +58,10 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
   const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
   return e == 0 ? sub : nrm;
 }
+// Value of an e4m3 code of either sign (0x7F / 0xFF, NaN, are outside the contract)
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  return __uint_as_float(__float_as_uint(e4m3_value_pos(c & 0x7Fu)) | ((c & 0x80u) << 24));
+}
 
 // ---- one quantization block, given its amax ---------------------------------------
 // NVFP4 (activation quantizer order): sf = fp32(fp32(amax * g) / 6) -> e4m3 code sc
@@ -106,6 +110,22 @@ __device__ __forceinline__ f16x8 decode8_f16(uint32_t packed, f16x2 scale2) {
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
+}
+
+// The two e4m3 scale codes in bytes 0 and 1 of w -> their values as an fp16 pair
+// {value(byte 0), value(byte 1)}, by gfx950's fp8 -> fp16 pair conversion at unit
+// scale (exact: every e4m3 value is an fp16 number).  A device probe of all 256 codes
+// in both bytes of both words matched the e4m3fn definition (bias 7, subnormals,
+// sign; 0x7F / 0xFF give NaN).  Issued as inline asm: this compiler's builtin for the
+// conversion hands back the low half in both halves of its result.
+__device__ __forceinline__ f16x2 e4m3_pair_f16(uint32_t w) {
+  uint32_t r;
+  asm("v_cvt_scalef32_pk_f16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  return __builtin_bit_cast(f16x2, r);
+}
+// {p.x, p.x} or {p.y, p.y}
+__device__ __forceinline__ f16x2 f16_bcast(f16x2 p, int hi) {
+  return hi ? f16x2{p.y, p.y} : f16x2{p.x, p.x};
 }
 
 // 8 e2m1 codes times an arbitrary fp32 scale -> bf16x8 (for bf16 MFMA against bf16

@@ -87,7 +87,7 @@ __device__ __forceinline__ void load_bf16x32(const uint16_t* row, int64_t k0, in
 template <int FMT>
 __device__ __forceinline__ float scale_value(uint32_t sb, int sub) {
   if (FMT == kMX) return e8m0_value(sb & 0xFFu);
-  return e4m3_value_pos((sb >> (8 * (sub >> 1))) & 0xFFu);
+  return e4m3_value((sb >> (8 * (sub >> 1))) & 0xFFu);
 }
 
 
@@ -183,13 +183,15 @@ __global__ __launch_bounds__(256) void rowblock_gemm(GemmParams p) {
         }
       } else if (FMT == kNV && AK == kA_FP4) {
         // NVFP4 W4A4: both operands decoded exactly to fp16, fp16 MFMA
-        const f16x2 ws_lo = f16_pair(scale_value<FMT>(wsb[u], 0));
-        const f16x2 ws_hi = f16_pair(scale_value<FMT>(wsb[u], 2));
+        const f16x2 wsp = e4m3_pair_f16(wsb[u]);
+        const f16x2 ws_lo = f16_bcast(wsp, 0);
+        const f16x2 ws_hi = f16_bcast(wsp, 1);
         f16x2 as_lo[MT], as_hi[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          as_lo[t] = f16_pair(scale_value<FMT>(asb[u][t], 0));
-          as_hi[t] = f16_pair(scale_value<FMT>(asb[u][t], 2));
+          const f16x2 asp = e4m3_pair_f16(asb[u][t]);
+          as_lo[t] = f16_bcast(asp, 0);
+          as_hi[t] = f16_bcast(asp, 1);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -405,8 +407,9 @@ __device__ __forceinline__ void stream_compute(
       const uint32_t d1 = dword_of(wsc[(2 * j + 1) >> 2], (2 * j + 1) & 3);
       const uint32_t wsd2 = (gq >> 1) ? d1 : d0;
       const uint32_t wsb = (wsd2 >> (16 * (gq & 1))) & 0xFFFFu;
-      const f16x2 ws_lo = f16_pair(e4m3_value_pos(wsb & 0xFFu));
-      const f16x2 ws_hi = f16_pair(e4m3_value_pos(wsb >> 8));
+      const f16x2 wsp = e4m3_pair_f16(wsb);
+      const f16x2 ws_lo = f16_bcast(wsp, 0);
+      const f16x2 ws_hi = f16_bcast(wsp, 1);
       uint4 aq[MT];
       f16x2 as_lo[MT], as_hi[MT];
 #pragma unroll
@@ -414,8 +417,9 @@ __device__ __forceinline__ void stream_compute(
         const int ar = t * 16 + r;
         aq[t] = *reinterpret_cast<const uint4*>(a_lds + ar * C::ASTR + j * 64 + gq * 16);
         const uint32_t asb = *reinterpret_cast<const uint16_t*>(s_lds + ar * C::SSTR + j * 8 + gq * 2);
-        as_lo[t] = f16_pair(e4m3_value_pos(asb & 0xFFu));
-        as_hi[t] = f16_pair(e4m3_value_pos(asb >> 8));
+        const f16x2 asp = e4m3_pair_f16(asb);
+        as_lo[t] = f16_bcast(asp, 0);
+        as_hi[t] = f16_bcast(asp, 1);
       }
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {

@@ -138,15 +138,18 @@ __device__ __forceinline__ void res_mma(const StepOps<MT>& o, uint32_t keep, u32
           wop, aop, acc[t][chain], 4, 4, 0, (int)o.wsb, 0, (int)o.asb[t]);
     }
   } else {
-    const f16x2 ws_lo = f16_pair(e4m3_value_pos(o.wsb & 0xFFu));
-    const f16x2 ws_hi = f16_pair(e4m3_value_pos(o.wsb >> 8));
+    const f16x2 wsp = e4m3_pair_f16(o.wsb);
+    const f16x2 ws_lo = f16_bcast(wsp, 0);
+    const f16x2 ws_hi = f16_bcast(wsp, 1);
+    f16x2 asp[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) asp[t] = e4m3_pair_f16(o.asb[t]);
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
       const f16x8 wop = decode8_f16(w[sub], sub < 2 ? ws_lo : ws_hi);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        const uint32_t sb = sub < 2 ? (o.asb[t] & 0xFFu) : (o.asb[t] >> 8);
-        const f16x8 aop = decode8_f16(o.aq[t][sub], f16_pair(e4m3_value_pos(sb)));
+        const f16x8 aop = decode8_f16(o.aq[t][sub], f16_bcast(asp[t], sub >> 1));
         acc[t][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[t][sub], 0, 0, 0);
       }
     }

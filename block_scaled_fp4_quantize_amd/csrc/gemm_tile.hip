@@ -66,9 +66,21 @@ struct TileCfg {
   static constexpr int SDW = ROWS * SB / 4;            // scale words per stage
   static constexpr int SCOP = (SDW + 63) / 64;         // 256-byte scale copies
   static constexpr int SPW = (SCOP + WAVES - 1) / WAVES;  // ... per wave (padded)
-  static constexpr int OPS = CPW + SPW;                // copies per wave per stage
+  static constexpr int PLANES = SB / 4;                // scale words per row per stage
+  // Grouped scales (the 8-wave tile, whose LDS has room for them): a copy moves the
+  // words of 16 rows for 4 consecutive stages (16 bytes of each row), so each scale
+  // line is fetched once per 4 stages instead of once per stage.  A group (4 stages)
+  // takes SGI copies, issued a quarter per stage, into one of 3 group buffers.
+  static constexpr bool SGRP = BM == 256;
+  static constexpr int SGI = ROWS / 16 * PLANES;       // 256-byte copies per group
+  static constexpr int SGW = SGI / 4 / WAVES;          // ... per wave per stage
+  static constexpr int ISTR = 320;                     // LDS stride of those copies
+  static constexpr int SGBYTES = SGI * ISTR;           // one group buffer
+  static constexpr int OPS = CPW + (SGRP ? SGW : SPW);  // copies per wave per stage
   static constexpr int CODES = ROWS * 64;
-  static constexpr int STAGE = CODES + WAVES * SPW * 256;  // bytes per LDS stage
+  static constexpr int STAGE = CODES + (SGRP ? 0 : WAVES * SPW * 256);  // bytes per LDS stage
+  // LDS stride between the scale words of consecutive 64-row blocks (as seen by a lane)
+  static constexpr int SBLK = SGRP ? 4 * ISTR : 256;
   // workgroups per CU (the register budget follows from it: 512 / (PER_CU * WAVES /
   // 4) per lane): 4-wave tiles that fit in 256 registers run two per CU (MXFP4 128 x
   // 256, NVFP4 128 x 128), MXFP4 128 x 128 three; 8-wave tiles one.  Four stages
@@ -76,7 +88,9 @@ struct TileCfg {
   static constexpr int PER_CU =
       BM == 128 ? (BN == 128 ? (FMT == kMX ? 3 : 2) : (FMT == kMX ? 2 : 1)) : 1;
   static constexpr int NBUF = PER_CU * 4 * STAGE <= 160 * 1024 ? 4 : 3;
-  static constexpr int LDS = NBUF * STAGE;
+  static constexpr int SGOFF = NBUF * STAGE;           // group buffers follow the stages
+  static constexpr int LDS = NBUF * STAGE + (SGRP ? 3 * SGBYTES : 0);
+  static_assert(!SGRP || SGI % (4 * WAVES) == 0, "group copies split evenly over stages and waves");
   static_assert(CCOP % WAVES == 0, "code copies split evenly over the waves");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "64-row scale blocks, 4-tile weight groups");
   static_assert(NBUF >= 3 && NBUF <= 4, "the stage waits cover up to two stages in flight");
@@ -104,11 +118,12 @@ __device__ __forceinline__ void tile_copy4(const void* g, uint8_t* lds) {
 // buffer just read may be overwritten
 constexpr int tile_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-// The MFMA work of one staged K step: fragment reads (codes at row * 64 + ccol, scales
-// at CODES + row * SB) and the MFMAs into acc.
+// The MFMA work of one staged K step: fragment reads (codes at row * 64 + ccol; the
+// 16 scale bytes of this lane's row in the 4 tiles of 64-row block b at sc + b * SBLK)
+// and the MFMAs into acc.
 template <int FMT, int BM, int BN>
 __device__ __forceinline__ void tile_step(
-    const uint8_t* cur, int ccol, int r, int gq, int wm, int wn,
+    const uint8_t* cur, const uint8_t* sc, int ccol, int r, int gq, int wm, int wn,
     v4f (&acc)[TileCfg<FMT, BM, BN>::NJ][TileCfg<FMT, BM, BN>::MI]) {
   using C = TileCfg<FMT, BM, BN>;
   // fragments of this stage: weights (A operand) and activations (B operand).  The
@@ -118,14 +133,13 @@ __device__ __forceinline__ void tile_step(
   uint32_t wsb[C::NJ];
   uint4 af[C::MI];
   uint32_t asb[C::MI];
-  const uint8_t* sc = cur + C::CODES + (FMT == kNV ? (gq >> 1) * C::ROWS * 4 : 0) + r * 16;
   const int ssh = FMT == kNV ? 16 * (gq & 1) : 8 * gq;
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j)
     wf[j] = *reinterpret_cast<const uint4*>(cur + (BM + wn * (BN / 2) + 16 * j + r) * 64 + ccol);
 #pragma unroll
   for (int k = 0; k < C::NJ / 4; ++k) {
-    const uint4 w4 = *reinterpret_cast<const uint4*>(sc + (BM + wn * (BN / 2) + 64 * k) * 4);
+    const uint4 w4 = *reinterpret_cast<const uint4*>(sc + ((BM + wn * (BN / 2)) / 64 + k) * C::SBLK);
     wsb[4 * k + 0] = w4.x >> ssh;
     wsb[4 * k + 1] = w4.y >> ssh;
     wsb[4 * k + 2] = w4.z >> ssh;
@@ -135,7 +149,7 @@ __device__ __forceinline__ void tile_step(
   for (int i = 0; i < C::MI; ++i)
     af[i] = *reinterpret_cast<const uint4*>(cur + (wm * 64 + 16 * i + r) * 64 + ccol);
   {
-    const uint4 a4 = *reinterpret_cast<const uint4*>(sc + wm * 64 * 4);
+    const uint4 a4 = *reinterpret_cast<const uint4*>(sc + wm * C::SBLK);
     asb[0] = a4.x >> ssh;
     asb[1] = a4.y >> ssh;
     asb[2] = a4.z >> ssh;
@@ -157,17 +171,21 @@ __device__ __forceinline__ void tile_step(
   } else {
     // lane group gq holds elements [32 gq, 32 gq + 32) of the stage; k-step s uses
     // its dword s (block 2 gq + s/2), the same k slots for both operands
+    // the lane's two block scales of each tile (bytes 0 and 1 of its scale word)
+    f16x2 asc[C::MI], wsc[C::NJ];
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) asc[i] = e4m3_pair_f16(asb[i]);
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) wsc[j] = e4m3_pair_f16(wsb[j]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       f16x8 aop[C::MI];
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
-        aop[i] = decode8_f16(dword_of(af[i], s),
-                             f16_pair(e4m3_value_pos((asb[i] >> (8 * (s >> 1))) & 0xFFu)));
+        aop[i] = decode8_f16(dword_of(af[i], s), f16_bcast(asc[i], s >> 1));
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j) {
-        const f16x8 wop = decode8_f16(dword_of(wf[j], s),
-                                      f16_pair(e4m3_value_pos((wsb[j] >> (8 * (s >> 1))) & 0xFFu)));
+        const f16x8 wop = decode8_f16(dword_of(wf[j], s), f16_bcast(wsc[j], s >> 1));
 #pragma unroll
         for (int i = 0; i < C::MI; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop[i], acc[j][i], 0, 0, 0);
@@ -258,6 +276,23 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
     dscale[q] = (rr < BM ? p.a_scales : wscales) + src_row(rr) * KS + plane * 4;
   }
 
+  // Grouped scales: copy c of a group (c = SGI/4 q + wave + WAVES w for quarter q) is
+  // plane c / (ROWS/16), 64-row block b = (c % (ROWS/16)) / 4 and rows 4 (c % 4) ..
+  // +3 of each of the block's 4 tiles; lane l fetches stage 4 g + l / 16 of tile l % 4,
+  // row 4 (c % 4) + (l / 4) % 4, so the 256 bytes land as [stage][row][tile] words and
+  // a lane reads its row's 4 tile words of one stage with one 16-byte read.
+  const uint8_t* gsrc[4][C::SGW > 0 ? C::SGW : 1];
+  if constexpr (C::SGRP) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int w = 0; w < C::SGW; ++w) {
+        const int c = (C::SGI / 4) * q + wave + C::WAVES * w;
+        const int plane = c / (C::ROWS / 16), rem = c % (C::ROWS / 16);
+        const int rr = (rem / 4) * 64 + (lane & 3) * 16 + 4 * (rem % 4) + ((lane >> 2) & 3);
+        gsrc[q][w] = (rr < BM ? p.a_scales : wscales) + src_row(rr) * KS + plane * 4;
+      }
+  }
   v4f acc[C::NJ][C::MI];
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j)
@@ -272,17 +307,33 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
   // exists) into the buffer computed at st - 1, computes stage st, then waits until
   // stage st + 1 has landed -- the stages after it may stay in flight -- and syncs.
   // The last iteration waits for everything, so no copy is outstanding after the loop.
-  auto issue = [&](int64_t t) {
+  // quarter q of scale group gi into group buffer gi % 3 (stages past the end re-read
+  // the last one: a group past the end is padding, its buffer free like any other)
+  auto issue_grp = [&](int64_t gi, int q, int w) {
+    uint8_t* gb = tsm + C::SGOFF + (int)(gi % 3) * C::SGBYTES;
+    int64_t stg = 4 * gi + (lane >> 4);
+    if (stg >= nstages) stg = nstages - 1;
+    tile_copy4(gsrc[q][w] + stg * C::SB, gb + ((C::SGI / 4) * q + wave + C::WAVES * w) * C::ISTR);
+  };
+  // copy u (0 .. OPS-1) of stage t: the code copies, then the scale copies
+  auto issue_part = [&](int64_t t, int u) {
     uint8_t* buf = tsm + (int)(t % C::NBUF) * C::STAGE;
+    if (u < C::CPW) {
+      tile_copy16(dcode[u] + t * 64, buf + (wave + C::WAVES * u) * 1024);
+    } else if constexpr (C::SGRP) {
+      issue_grp(t / 4 + 1, (int)(t % 4), u - C::CPW);
+    } else {
+      tile_copy4(dscale[u - C::CPW] + t * C::SB, buf + C::CODES + (wave + C::WAVES * (u - C::CPW)) * 256);
+    }
+  };
+  auto issue = [&](int64_t t) {
 #pragma unroll
-    for (int q = 0; q < C::CPW; ++q)
-      tile_copy16(dcode[q] + t * 64, buf + (wave + C::WAVES * q) * 1024);
-#pragma unroll
-    for (int q = 0; q < C::SPW; ++q)
-      tile_copy4(dscale[q] + t * C::SB, buf + C::CODES + (wave + C::WAVES * q) * 256);
+    for (int u = 0; u < C::OPS; ++u) issue_part(t, u);
   };
   auto sync = [&](int64_t ahead) {   // stages issued after the one needed next
-    if (C::NBUF >= 4 && ahead >= 2)
+    if (ahead >= 3)
+      __builtin_amdgcn_s_waitcnt(tile_vmcnt(3 * C::OPS));
+    else if (ahead >= 2)
       __builtin_amdgcn_s_waitcnt(tile_vmcnt(2 * C::OPS));
     else if (ahead >= 1)
       __builtin_amdgcn_s_waitcnt(tile_vmcnt(C::OPS));
@@ -294,15 +345,133 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
   };
   // fragment rows are 16-row tile starts + r, so their swizzle is tile_swz(r)
   const int gcol = (gq ^ tile_swz(r)) << 4;
+  // this lane's scale words: plane gq / 2 (NVFP4), row r
+  const int splane = FMT == kNV ? (gq >> 1) : 0;
+  const int srd = C::SGRP ? splane * (C::ROWS / 16) * C::ISTR + (r >> 2) * C::ISTR + (r & 3) * 16
+                          : C::CODES + splane * C::ROWS * 4 + r * 16;
+  auto stage_scales = [&](int64_t s, const uint8_t* cur) -> const uint8_t* {
+    return C::SGRP ? tsm + C::SGOFF + (int)((s / 4) % 3) * C::SGBYTES + (int)(s % 4) * 64 + srd
+                   : cur + srd;
+  };
+  // Scale group g is issued with code stages 4 g - 4 .. 4 g - 1 (group 0 up front) and
+  // read by stages 4 g .. 4 g + 3; its buffer last held group g - 3, whose reads all
+  // ended before the barrier that precedes the first of those issues.
+  if constexpr (C::SGRP) {
 #pragma unroll
-  for (int t = 0; t < C::NBUF - 1; ++t)
-    if (t < nstages) issue(t);
-  sync(nstages - 1 < C::NBUF - 2 ? nstages - 1 : C::NBUF - 2);
-  for (int64_t st = 0; st < nstages; ++st) {
-    const int64_t t = st + C::NBUF - 1;
-    if (t < nstages) issue(t);
-    tile_step<FMT, BM, BN>(tsm + (int)(st % C::NBUF) * C::STAGE, gcol, r, gq, wm, wn, acc);
-    sync((t < nstages ? t : nstages - 1) - (st + 1));
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int w = 0; w < C::SGW; ++w) issue_grp(0, q, w);
+  }
+
+  if constexpr (FMT == kMX) {
+    // Software-pipelined: the LDS operands of stage st + 1 are read while the MFMAs of
+    // stage st run, each into the registers of an operand right after its last MFMA
+    // (weight tile j after tile j's MFMAs, activation tile i during the last weight
+    // tile's), so a stage's MFMAs never wait on LDS.  Stage st's buffer is free once
+    // its operands are in registers: iteration st refills it with stage st + NBUF, and
+    // waits (before its barrier) until stage st + 2 has landed.
+    const int wrow0 = BM + wn * (BN / 2);
+    u32x4 wf[C::NJ];
+    uint32_t wsb[C::NJ];
+    u32x4 af[C::MI];
+    uint32_t asb[C::MI];
+    const int ssh = 8 * gq;
+    auto rd_w = [&](const uint8_t* cur, int j) {
+      return *reinterpret_cast<const u32x4*>(cur + (wrow0 + 16 * j + r) * 64 + gcol);
+    };
+    auto rd_ws = [&](const uint8_t* sc, int k) {   // weight tiles 4 k .. 4 k + 3
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(sc + (wrow0 / 64 + k) * C::SBLK);
+      wsb[4 * k + 0] = w4.x >> ssh;
+      wsb[4 * k + 1] = w4.y >> ssh;
+      wsb[4 * k + 2] = w4.z >> ssh;
+      wsb[4 * k + 3] = w4.w >> ssh;
+    };
+    auto rd_a = [&](const uint8_t* cur, int i) {
+      return *reinterpret_cast<const u32x4*>(cur + (wm * 64 + 16 * i + r) * 64 + gcol);
+    };
+    auto rd_as = [&](const uint8_t* sc) {
+      const u32x4 a4 = *reinterpret_cast<const u32x4*>(sc + wm * C::SBLK);
+      asb[0] = a4.x >> ssh;
+      asb[1] = a4.y >> ssh;
+      asb[2] = a4.z >> ssh;
+      asb[3] = a4.w >> ssh;
+    };
+    auto mma = [&](int j, int i) {
+      const v8i wop = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
+      const v8i aop = {(int)af[i].x, (int)af[i].y, (int)af[i].z, (int)af[i].w, 0, 0, 0, 0};
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          wop, aop, acc[j][i], 4, 4, 0, (int)wsb[j], 0, (int)asb[i]);
+    };
+    static_assert(C::MI == 4 && C::NJ % 4 == 0, "scale words are read 4 tiles at a time");
+#pragma unroll
+    for (int t = 0; t < C::NBUF; ++t)
+      if (t < nstages) issue(t);
+    sync(nstages - 1 < C::NBUF - 1 ? nstages - 1 : C::NBUF - 1);   // stage 0 landed
+    {
+      const uint8_t* sc = stage_scales(0, tsm);
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) wf[j] = rd_w(tsm, j);
+#pragma unroll
+      for (int k = 0; k < C::NJ / 4; ++k) rd_ws(sc, k);
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) af[i] = rd_a(tsm, i);
+      rd_as(sc);
+    }
+    // stage 1 landed; every wave's reads of buffer 0 done
+    sync(nstages - 1 < C::NBUF - 1 ? (nstages - 1 > 0 ? nstages - 2 : 0) : C::NBUF - 2);
+    // copy u goes after MFMA group u (NJ - 1) / OPS <= NJ - 2: every copy is issued
+    static_assert(C::NJ >= 2, "at least two weight tiles per wave");
+    for (int64_t st = 0; st < nstages; ++st) {
+      // stage st + NBUF refills this stage's buffer; its OPS copies are spread over
+      // the MFMA groups below (issued in one burst, the copies of the 8 waves queue
+      // up in the texture unit and stall the waves behind them)
+      const bool refill = st + C::NBUF < nstages;
+      // operands of stage st + 1 (or stage st again after the last: its buffer is not
+      // refilled then, and the values go unused)
+      const int64_t sn = st + 1 < nstages ? st + 1 : st;
+      const uint8_t* cur = tsm + (int)(sn % C::NBUF) * C::STAGE;
+      const uint8_t* sc = stage_scales(sn, cur);
+#pragma unroll
+      for (int j = 0; j < C::NJ - 1; ++j) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) mma(j, i);
+        // pins the order: the MFMAs above (their results pass through here), then the
+        // reads below (the memory clobber keeps them from being hoisted)
+        asm volatile("" : "+v"(acc[j][0]), "+v"(acc[j][1]), "+v"(acc[j][2]), "+v"(acc[j][3])
+                     :: "memory");
+#pragma unroll
+        for (int u = 0; u < C::OPS; ++u)
+          if (u * (C::NJ - 1) / C::OPS == j && refill) issue_part(st + C::NBUF, u);
+        wf[j] = rd_w(cur, j);
+        if (j % 4 == 3) rd_ws(sc, j / 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        mma(C::NJ - 1, i);
+        asm volatile("" : "+v"(acc[C::NJ - 1][i]) :: "memory");
+        af[i] = rd_a(cur, i);
+      }
+      wf[C::NJ - 1] = rd_w(cur, C::NJ - 1);
+      rd_ws(sc, C::NJ / 4 - 1);
+      rd_as(sc);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage st + 2 landed (the stages issued after it may stay in flight)
+      const int64_t last = st + C::NBUF < nstages ? st + C::NBUF : nstages - 1;
+      sync(st + 2 <= nstages - 1 ? last - (st + 2) : 0);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < C::NBUF - 1; ++t)
+      if (t < nstages) issue(t);
+    sync(nstages - 1 < C::NBUF - 2 ? nstages - 1 : C::NBUF - 2);
+    for (int64_t st = 0; st < nstages; ++st) {
+      const int64_t t = st + C::NBUF - 1;
+      if (t < nstages) issue(t);
+      const uint8_t* cur = tsm + (int)(st % C::NBUF) * C::STAGE;
+      tile_step<FMT, BM, BN>(cur, stage_scales(st, cur), gcol, r, gq, wm, wn, acc);
+      sync((t < nstages ? t : nstages - 1) - (st + 1));
+    }
   }
 
   const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;

@@ -134,10 +134,46 @@ def test_tiled_shapes(fmt, shape):
                   prequant=True)
 
 
+# Uniformly drawn bytes: every e2m1 code, and block scales over the whole finite range
+# (NVFP4: e4m3 codes of either sign, subnormals included, only the NaN codes 0x7F /
+# 0xFF left out; MXFP4: e8m0 2^-20 .. 2^20), through each kernel family -- resident
+# (1 row), streaming (32 rows), LDS tile (more than 64 rows), generic (K not a
+# multiple of 128) -- against the oracle's dequantization of the same bytes.
+RAW = [(1, 272, 1024), (32, 200, 1024), (96, 384, 512), (20, 72, 96)]
+
+
+@pytest.mark.parametrize("shape", RAW)
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_raw_codes(fmt, shape):
+    M, N, K = shape
+    G = OQ.GROUP[fmt]
+    rng = np.random.default_rng(sum(shape) + (fmt == "nvfp4"))
+
+    def scales(rows):
+        if fmt == "nvfp4":
+            c = rng.integers(0, 256, (rows, K // G), dtype=np.uint8)
+            c[(c & 0x7F) == 0x7F] ^= 1
+            return c
+        return rng.integers(107, 148, (rows, K // G), dtype=np.uint8)
+
+    wc, ws = rng.integers(0, 256, (N, K // 2), dtype=np.uint8), scales(N)
+    ac, asc = rng.integers(0, 256, (M, K // 2), dtype=np.uint8), scales(M)
+    out, st = T.gemm(fmt, "w4a4", to_dev(wc), to_dev(ws), a_codes=to_dev(ac),
+                     a_scales=to_dev(asc), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert st == F.FP4_OK
+    a_hat, w_hat = dequant(fmt, ac, asc), dequant(fmt, wc, ws)
+    check_gemm(out.cpu().numpy().astype(np.float64), a_hat @ w_hat.T, a_hat, w_hat, 1.0,
+               False, what=f"raw {fmt} M={M} N={N} K={K} ({F.fp4_last_kernel()})")
+
+
 # dense MXFP4 with at least 256 tiles of 256 x 256: the 8-wave 256-row tile, with K of
 # one and three stages (fewer than the copy pipeline holds) and of eight, ragged rows
 # and columns; the oracle checks the first and last 300 rows and 200 sampled ones
-TILED_256 = [(2300, 7324, 128), (2049, 7324, 384), (4096, 4096, 1024)]
+# K of 1, 3, 5, 8 and 17 stages of 128: the 256-row tile copies the block scales of 4
+# stages at a time, so these cover a group cut short at 1, 3 and 1 stages and whole ones
+TILED_256 = [(2300, 7324, 128), (2049, 7324, 384), (4096, 4096, 1024), (4096, 4096, 640),
+             (4352, 4096, 2176)]
 
 
 @pytest.mark.parametrize("shape", TILED_256)
