@@ -71,7 +71,7 @@ struct TileCfg {
   // words of 16 rows for 4 consecutive stages (16 bytes of each row), so each scale
   // line is fetched once per 4 stages instead of once per stage.  A group (4 stages)
   // takes SGI copies, issued a quarter per stage, into one of 3 group buffers.
-  static constexpr bool SGRP = BM == 256;
+  static constexpr bool SGRP = BM == 256 && FMT == kMX;
   static constexpr int SGI = ROWS / 16 * PLANES;       // 256-byte copies per group
   static constexpr int SGW = SGI / 4 / WAVES;          // ... per wave per stage
   static constexpr int ISTR = 320;                     // LDS stride of those copies
@@ -587,7 +587,7 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (FMT == kNV)
     *name = FUSE ? (BN == 128 ? "tile_nvfp4_m128_n128_swiglu" : "tile_nvfp4_m128_swiglu")
-                 : (BN == 128 ? "tile_nvfp4_m128_n128" : "tile_nvfp4_m128");
+                 : (BM == 256 ? "tile_nvfp4_m256" : (BN == 128 ? "tile_nvfp4_m128_n128" : "tile_nvfp4_m128"));
   else
     *name = FUSE ? "tile_mxfp4_m128_swiglu" : (BM == 256 ? "tile_mxfp4_m256" : "tile_mxfp4_m128");
   if (p.K % kTBK != 0 || p.K <= 0) return hipErrorInvalidValue;
@@ -612,14 +612,16 @@ constexpr int kNvTileN = 128;
 }  // namespace
 
 hipError_t launch_gemm_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name) {
-  if (fmt == kNV)
-    return p.fuse_swiglu ? launch_tile<kNV, 128, kNvTileN, true>(p, s, name)
-                         : launch_tile<kNV, 128, kNvTileN, false>(p, s, name);
+  const int64_t ntiles256 = (p.N + 255) / 256;
+  const bool big = !p.mblk_expert && ((p.M + 255) / 256) * ntiles256 >= 256;
+  if (fmt == kNV) {
+    if (p.fuse_swiglu) return launch_tile<kNV, 128, kNvTileN, true>(p, s, name);
+    if (big) return launch_tile<kNV, 256, 256, false>(p, s, name);
+    return launch_tile<kNV, 128, kNvTileN, false>(p, s, name);
+  }
   if (p.fuse_swiglu) return launch_tile<kMX, 128, 256, true>(p, s, name);
   // dense MXFP4 with enough 256 x 256 tiles to give every CU one: the 8-wave tile
-  const int64_t ntiles = (p.N + 255) / 256;
-  if (!p.mblk_expert && ((p.M + 255) / 256) * ntiles >= 256)
-    return launch_tile<kMX, 256, 256, false>(p, s, name);
+  if (big) return launch_tile<kMX, 256, 256, false>(p, s, name);
   return launch_tile<kMX, 128, 256, false>(p, s, name);
 }
 

@@ -167,7 +167,7 @@ def test_raw_codes(fmt, shape):
                False, what=f"raw {fmt} M={M} N={N} K={K} ({F.fp4_last_kernel()})")
 
 
-# dense MXFP4 with at least 256 tiles of 256 x 256: the 8-wave 256-row tile, with K of
+# dense problems with at least 256 tiles of 256 x 256: the 8-wave 256-row tile, with K of
 # one and three stages (fewer than the copy pipeline holds) and of eight, ragged rows
 # and columns; the oracle checks the first and last 300 rows and 200 sampled ones
 # K of 1, 3, 5, 8 and 17 stages of 128: the 256-row tile copies the block scales of 4
@@ -177,14 +177,15 @@ TILED_256 = [(2300, 7324, 128), (2049, 7324, 384), (4096, 4096, 1024), (4096, 40
 
 
 @pytest.mark.parametrize("shape", TILED_256)
-def test_tiled_256_shapes(shape):
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_tiled_256_shapes(fmt, shape):
     M, N, K = shape
     rng = np.random.default_rng(sum(shape))
     rows = np.unique(np.concatenate([np.arange(300), np.arange(M - 300, M),
                                      rng.choice(M, 200, replace=False)]))
-    run_and_check("mxfp4", "w4a4", M, N, K, seed=sum(shape), rows=rows)
-    assert F.fp4_last_kernel() == "tile_mxfp4_m256"
-    run_and_check("mxfp4", "w4a4", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32,
+    run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape), rows=rows)
+    assert F.fp4_last_kernel() == f"tile_{fmt}_m256"
+    run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32,
                   prequant=True, rows=rows)
 
 
