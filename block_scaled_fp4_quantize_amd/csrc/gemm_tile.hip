@@ -363,13 +363,15 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
       for (int w = 0; w < C::SGW; ++w) issue_grp(0, q, w);
   }
 
-  if constexpr (FMT == kMX) {
+  if constexpr (FMT == kMX && C::NBUF == 4) {
     // Software-pipelined: the LDS operands of stage st + 1 are read while the MFMAs of
     // stage st run, each into the registers of an operand right after its last MFMA
     // (weight tile j after tile j's MFMAs, activation tile i during the last weight
     // tile's), so a stage's MFMAs never wait on LDS.  Stage st's buffer is free once
     // its operands are in registers: iteration st refills it with stage st + NBUF, and
-    // waits (before its barrier) until stage st + 2 has landed.
+    // waits (before its barrier) until stage st + 2 has landed.  Only with four stage
+    // buffers: with three, the copies would get one stage less to land than in the
+    // plain loop below, which measured faster there (MoE 128-row tiles).
     const int wrow0 = BM + wn * (BN / 2);
     u32x4 wf[C::NJ];
     uint32_t wsb[C::NJ];
