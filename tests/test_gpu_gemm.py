@@ -234,6 +234,21 @@ def test_resident_shapes(fmt, shape):
                   prequant=True)
 
 
+# 17..64 rows: the streaming kernel over many weight tiles with a ragged last one, one
+# 32-row block and two
+STREAM = [(20, 9990, 512), (40, 5000, 256)]
+
+
+@pytest.mark.parametrize("shape", STREAM)
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_stream_wide(fmt, shape):
+    M, N, K = shape
+    run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 3)
+    assert F.fp4_last_kernel() == f"stream_{fmt}_m32", F.fp4_last_kernel()
+    run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 4, out_dtype=torch.float32,
+                  prequant=True)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_tiled_strided_output_canaries(fmt):
     # output rows with a stride that is not a multiple of 4 take the scalar stores;
