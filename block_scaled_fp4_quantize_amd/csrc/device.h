@@ -29,10 +29,15 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two fp32 values -> bf16 pair (a in the low half), round to nearest even, by gfx950's
+// pair conversion.  A device probe over 2^24 random bit patterns plus ties at every
+// exponent, denormals, infinities and NaNs matched rounding the bit pattern to nearest
+// even (NaNs stay NaN).
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
 }
 
 // e4m3fn code of sf >= 0 (finite or +inf): round to nearest even, saturating at 448

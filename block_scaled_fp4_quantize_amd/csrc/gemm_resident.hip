@@ -399,11 +399,11 @@ __global__ __launch_bounds__(256, KSPLIT == 4 ? 4 : 1) void resident_gemm(GemmPa
       }
     } else {
       uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + n;
-      const uint16_t b0 = f32_to_bf16_rne(x0), b1 = f32_to_bf16_rne(x1);
-      const uint16_t b2 = f32_to_bf16_rne(x2), b3 = f32_to_bf16_rne(x3);
+      const uint32_t b01 = bf16_pack2(x0, x1), b23 = bf16_pack2(x2, x3);
+      const uint16_t b0 = (uint16_t)b01, b1 = (uint16_t)(b01 >> 16);
+      const uint16_t b2 = (uint16_t)b23, b3 = (uint16_t)(b23 >> 16);
       if (vec && n + 3 < p.N) {
-        *reinterpret_cast<uint2*>(o) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
-                                                  (uint32_t)b2 | ((uint32_t)b3 << 16));
+        *reinterpret_cast<uint2*>(o) = make_uint2(b01, b23);
       } else {
         o[0] = b0;
         if (n + 1 < p.N) o[1] = b1;

@@ -541,6 +541,29 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
   // epilogue: lane holds out[m][n .. n+3], m = rows of activation tile i,
   // n = 4 consecutive columns of weight tile j
   const bool vec = (p.ldo & 3) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+  // the wave's whole 64 x BN/2 block inside the output and aligned: stores without
+  // per-element checks (the decision is uniform over the wave)
+  {
+    const int64_t m_lo = row0 + wm * 64, n_lo = nt * BN + wn * (BN / 2);
+    if (vec && m_lo + 64 <= row_end && n_lo + BN / 2 <= p.N) {
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        const int64_t off = (m_lo + 16 * i + r) * p.ldo + n_lo + 4 * gq;
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j) {
+          const float x0 = acc[j][i][0] * alpha, x1 = acc[j][i][1] * alpha;
+          const float x2 = acc[j][i][2] * alpha, x3 = acc[j][i][3] * alpha;
+          if (p.out_f32)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off + 16 * j) =
+                make_float4(x0, x1, x2, x3);
+          else
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + off + 16 * j) =
+                make_uint2(bf16_pack2(x0, x1), bf16_pack2(x2, x3));
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
     const int64_t m = row0 + wm * 64 + 16 * i + r;
@@ -563,11 +586,11 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
         }
       } else {
         uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + n;
-        const uint16_t b0 = f32_to_bf16_rne(x0), b1 = f32_to_bf16_rne(x1);
-        const uint16_t b2 = f32_to_bf16_rne(x2), b3 = f32_to_bf16_rne(x3);
+        const uint32_t b01 = bf16_pack2(x0, x1), b23 = bf16_pack2(x2, x3);
+        const uint16_t b0 = (uint16_t)b01, b1 = (uint16_t)(b01 >> 16);
+        const uint16_t b2 = (uint16_t)b23, b3 = (uint16_t)(b23 >> 16);
         if (vec && n + 3 < p.N) {
-          *reinterpret_cast<uint2*>(o) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
-                                                    (uint32_t)b2 | ((uint32_t)b3 << 16));
+          *reinterpret_cast<uint2*>(o) = make_uint2(b01, b23);
         } else {
           o[0] = b0;
           if (n + 1 < p.N) o[1] = b1;

@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluParams p) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16_rne(h[2 * i]) | ((uint32_t)f32_to_bf16_rne(h[2 * i + 1]) << 16);
+      w[i] = bf16_pack2(h[2 * i], h[2 * i + 1]);
     *reinterpret_cast<uint4*>(p.h_bf16 + row * p.I + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
     return;
   }
@@ -391,18 +391,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i]) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+    w[i] = bf16_pack2(acc[2 * i], acc[2 * i + 1]);
   *reinterpret_cast<uint4*>(p.out + t * p.H + col) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// ---- per-expert host scalars -> device, passed by value ------------------------
+// ---- per-expert host scalars -> device, passed by value (3 KB of kernel arguments,
+// under the 4 KB limit: the four scalars of up to 192 experts in one launch) ---------
+constexpr int kPackFloats = 768;
 struct FloatPack {
-  float v[256];
+  float v[kPackFloats];
 };
 
-__global__ void upload_kernel(float* dst, int n, FloatPack pk) {
-  const int i = threadIdx.x;
-  if (i < n) dst[i] = pk.v[i];
+__global__ __launch_bounds__(256) void upload_kernel(float* dst, int n, FloatPack pk) {
+  for (int i = threadIdx.x; i < n; i += 256) dst[i] = pk.v[i];
 }
 
 }  // namespace
@@ -465,10 +466,10 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s, const char** na
 }
 
 hipError_t launch_upload_floats(float* dst, const float* host_vals, int64_t n, hipStream_t s) {
-  for (int64_t base = 0; base < n; base += 256) {
+  for (int64_t base = 0; base < n; base += kPackFloats) {
     FloatPack pk;
-    const int cnt = (int)((n - base) < 256 ? (n - base) : 256);
-    for (int i = 0; i < 256; ++i) pk.v[i] = i < cnt ? host_vals[base + i] : 0.f;
+    const int cnt = (int)((n - base) < kPackFloats ? (n - base) : kPackFloats);
+    for (int i = 0; i < kPackFloats; ++i) pk.v[i] = i < cnt ? host_vals[base + i] : 0.f;
     hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, dst + base, cnt, pk);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
