@@ -541,13 +541,15 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
   // epilogue: lane holds out[m][n .. n+3], m = rows of activation tile i,
   // n = 4 consecutive columns of weight tile j
   const bool vec = (p.ldo & 3) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
-  // the wave's whole 64 x BN/2 block inside the output and aligned: stores without
-  // per-element checks (the decision is uniform over the wave)
+  // the wave's BN/2 columns inside the output and aligned: stores without per-column
+  // checks (uniform decision), rows checked per lane only if the block is cut short
   {
     const int64_t m_lo = row0 + wm * 64, n_lo = nt * BN + wn * (BN / 2);
-    if (vec && m_lo + 64 <= row_end && n_lo + BN / 2 <= p.N) {
+    if (vec && n_lo + BN / 2 <= p.N) {
+      const bool rows_full = m_lo + 64 <= row_end;
 #pragma unroll
       for (int i = 0; i < C::MI; ++i) {
+        if (!rows_full && m_lo + 16 * i + r >= row_end) continue;
         const int64_t off = (m_lo + 16 * i + r) * p.ldo + n_lo + 4 * gq;
 #pragma unroll
         for (int j = 0; j < C::NJ; ++j) {
