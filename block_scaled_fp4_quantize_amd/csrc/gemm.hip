@@ -520,19 +520,35 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
   }
 
   const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+  // a lane holds out[m][n0 .. n0+3]: one 8-byte (bf16) or 16-byte (fp32) store when the
+  // four columns exist and the row stride and base allow it
+  const bool vec = (p.ldo & 3) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.out) & (p.out_f32 ? 15 : 7)) == 0;
+  const int64_t n0 = nt * 64 + wave * 16 + 4 * (lane >> 4);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int64_t m = row0 + t * 16 + (lane & 15);
     if (m >= row_end) continue;
+    const float x0 = acc[t][0] * alpha, x1 = acc[t][1] * alpha;
+    const float x2 = acc[t][2] * alpha, x3 = acc[t][3] * alpha;
+    if (vec && n0 + 3 < p.N) {
+      if (p.out_f32)
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + m * p.ldo + n0) =
+            make_float4(x0, x1, x2, x3);
+      else
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + n0) =
+            make_uint2(bf16_pack2(x0, x1), bf16_pack2(x2, x3));
+      continue;
+    }
+    const float xs[4] = {x0, x1, x2, x3};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t n = nt * 64 + wave * 16 + 4 * (lane >> 4) + v;
+      const int64_t n = n0 + v;
       if (n >= p.N) continue;
-      const float x = acc[t][v] * alpha;
       if (p.out_f32)
-        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = x;
+        reinterpret_cast<float*>(p.out)[m * p.ldo + n] = xs[v];
       else
-        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(x);
+        reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(xs[v]);
     }
   }
 }
