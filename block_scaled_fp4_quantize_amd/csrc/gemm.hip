@@ -114,6 +114,8 @@ __global__ __launch_bounds__(256) void rowblock_gemm(GemmParams p) {
     row0 = mb * (16 * MT);
     row_end = p.M;
   }
+  // per-group scalars fetched up front, not after the main loop
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
 
   const int64_t K = p.K;
   const int r = lane & 15;
@@ -228,7 +230,6 @@ __global__ __launch_bounds__(256) void rowblock_gemm(GemmParams p) {
   }
   __syncthreads();
   if (wave != 0) return;
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     // lane holds out[m = row0 + 16t + (lane & 15)][n = 16 nt + 4 (lane >> 4) + v]
@@ -457,6 +458,8 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
     row0 = mb * C::AROWS;
     row_end = p.M;
   }
+  // per-group scalars fetched up front, not after the main loop
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
   const int64_t K = p.K;
   const int64_t KB = K >> 1;
   const int64_t KS = K / C::G;
@@ -519,7 +522,6 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
     }
   }
 
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
   // a lane holds out[m][n0 .. n0+3]: one 8-byte (bf16) or 16-byte (fp32) store when the
   // four columns exist and the row stride and base allow it
   const bool vec = (p.ldo & 3) == 0 &&

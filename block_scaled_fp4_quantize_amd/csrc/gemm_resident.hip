@@ -180,6 +180,8 @@ __global__ __launch_bounds__(256, KSPLIT == 4 ? 4 : 1) void resident_gemm(GemmPa
     row0 = mb * C::AROWS;
     row_end = p.M;
   }
+  // per-group scalars fetched up front, not after the main loop
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
   const int64_t K = p.K;
   const int64_t KB = K >> 1;
   const int KS = (int)(K / C::G);
@@ -377,7 +379,6 @@ __global__ __launch_bounds__(256, KSPLIT == 4 ? 4 : 1) void resident_gemm(GemmPa
 
   // a lane holds out[m][n .. n+3]: one 8-byte (bf16) or 16-byte (fp32) store when
   // the row stride and base allow it
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
   const bool vec = (p.ldo & 3) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.out) & (p.out_f32 ? 15 : 7)) == 0;
   const int64_t n = nt * C::RROWS + rg * 16 + 4 * gq;

@@ -228,6 +228,9 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
     row0 = mb * BM;
     row_end = p.M;
   }
+  // per-group scalars fetched up front, not after the main loop
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+  const float hg = FUSE ? (p.h_grp_g ? p.h_grp_g[grp] : p.h_g) : 0.0f;
   const int64_t K = p.K;
   const int64_t KB = K >> 1;
   const int64_t KS = K / C::G;
@@ -476,7 +479,6 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
     }
   }
 
-  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
   if (FUSE) {
     // h = SiLU(alpha g) * (alpha u) for this lane's 4 consecutive h columns of each
     // gate tile j (up tile j + NJ/2); a quantization block (16 or 32 columns of one
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
     // exchanges; only rows that exist are stored.
     constexpr int NG = C::NJ / 2;   // gate tiles per wave
     static_assert(NG % 2 == 0, "MXFP4 blocks pair gate tiles");
-    const float g = p.h_grp_g ? p.h_grp_g[grp] : p.h_g;
+    const float g = hg;
     const int64_t hrow = p.I / 2;
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) {
