@@ -429,14 +429,10 @@ hipError_t launch_res(const GemmParams& p, hipStream_t s, const char** name) {
                                     {"resident_mxfp4_m16", "resident_mxfp4_m32"}};
   *name = names[FMT][MT - 1];
   const int64_t lds = resident_lds_bytes(FMT, MT, KSPLIT, p.K);
-  static bool attr_set = false;  // once per instantiation (idempotent)
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&resident_gemm<FMT, MT, RING, KSPLIT>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kResidentMaxLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};   // devices done, per instantiation
+  hipError_t e = ensure_dynamic_lds(
+      reinterpret_cast<const void*>(&resident_gemm<FMT, MT, RING, KSPLIT>), (int)kResidentMaxLds, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((resident_gemm<FMT, MT, RING, KSPLIT>), dim3((unsigned)grid), dim3(256),
                      (size_t)lds, s, p);
   return hipGetLastError();

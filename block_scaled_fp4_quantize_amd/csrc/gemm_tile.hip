@@ -623,13 +623,10 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
   if (FUSE && (p.I <= 0 || p.I % 128 != 0 || p.N != 2 * p.I || !p.h_codes || !p.h_scales))
     return hipErrorInvalidValue;
   const size_t lds = C::LDS;
-  static bool attr_set = false;  // once per instantiation (idempotent, so races are harmless)
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm<FMT, BM, BN, FUSE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};   // devices done, per instantiation
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&tile_gemm<FMT, BM, BN, FUSE>),
+                                    (int)lds, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((tile_gemm<FMT, BM, BN, FUSE>), dim3((unsigned)grid), dim3(C::THREADS), lds,
                      s, p);
   return hipGetLastError();

@@ -3,10 +3,26 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace fp4 {
+
+// Raise a kernel's dynamic-LDS limit on the current device, once per device (the
+// attribute belongs to the device the call is made on).  Concurrent first calls both
+// set it, which is harmless.
+inline hipError_t ensure_dynamic_lds(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  if (bit) done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 enum Fmt : int { kNV = 0, kMX = 1 };
 
