@@ -17,6 +17,8 @@
 // bits per element all the way into registers; NVFP4 is decoded to fp16 right before
 // the MFMA (unit-scale convert, then one packed fp16 multiply by the e4m3 scale --
 // exact), MXFP4 needs no decode at all.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -121,10 +123,13 @@ constexpr int tile_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4);
 // The MFMA work of one staged K step: fragment reads (codes at row * 64 + ccol; the
 // 16 scale bytes of this lane's row in the 4 tiles of 64-row block b at sc + b * SBLK)
 // and the MFMAs into acc.
-template <int FMT, int BM, int BN>
+// PART: only the first nv (wave-uniform) 16-row activation tiles of the wave hold
+// rows that exist (a row block cut short, as an MoE expert's last one is); the others
+// are neither read nor multiplied, and their accumulators stay zero (never stored).
+template <int FMT, int BM, int BN, bool PART = false>
 __device__ __forceinline__ void tile_step(
     const uint8_t* cur, const uint8_t* sc, int ccol, int r, int gq, int wm, int wn,
-    v4f (&acc)[TileCfg<FMT, BM, BN>::NJ][TileCfg<FMT, BM, BN>::MI]) {
+    v4f (&acc)[TileCfg<FMT, BM, BN>::NJ][TileCfg<FMT, BM, BN>::MI], int nv = TileCfg<FMT, BM, BN>::MI) {
   using C = TileCfg<FMT, BM, BN>;
   // fragments of this stage: weights (A operand) and activations (B operand).  The
   // scale word of tile j of this lane's row holds its 4 (MXFP4) or 2 (NVFP4 plane
@@ -147,7 +152,8 @@ __device__ __forceinline__ void tile_step(
   }
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
-    af[i] = *reinterpret_cast<const uint4*>(cur + (wm * 64 + 16 * i + r) * 64 + ccol);
+    if (!PART || i < nv)
+      af[i] = *reinterpret_cast<const uint4*>(cur + (wm * 64 + 16 * i + r) * 64 + ccol);
   {
     const uint4 a4 = *reinterpret_cast<const uint4*>(sc + wm * C::SBLK);
     asb[0] = a4.x >> ssh;
@@ -158,6 +164,20 @@ __device__ __forceinline__ void tile_step(
   static_assert(C::MI == 4 && C::NJ % 4 == 0, "scale words are read 4 tiles at a time");
 
   if (FMT == kMX) {
+    if (PART) {   // activation tile outermost: one uniform branch per tile
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        if (i >= nv) break;
+        const v8i aop = {(int)af[i].x, (int)af[i].y, (int)af[i].z, (int)af[i].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j) {
+          const v8i wop = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wop, aop, acc[j][i], 4, 4, 0, (int)wsb[j], 0, (int)asb[i]);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
       const v8i wop = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
@@ -177,6 +197,22 @@ __device__ __forceinline__ void tile_step(
     for (int i = 0; i < C::MI; ++i) asc[i] = e4m3_pair_f16(asb[i]);
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) wsc[j] = e4m3_pair_f16(wsb[j]);
+    if (PART) {   // activation tile outermost: one uniform branch per tile
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        if (i >= nv) break;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f16x8 aop = decode8_f16(dword_of(af[i], s), f16_bcast(asc[i], s >> 1));
+#pragma unroll
+          for (int j = 0; j < C::NJ; ++j) {
+            const f16x8 wop = decode8_f16(dword_of(wf[j], s), f16_bcast(wsc[j], s >> 1));
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[j][i], 0, 0, 0);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       f16x8 aop[C::MI];
@@ -348,6 +384,13 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
   };
   // fragment rows are 16-row tile starts + r, so their swizzle is tile_swz(r)
   const int gcol = (gq ^ tile_swz(r)) << 4;
+  // 16-row activation tiles of this wave that hold existing rows (uniform per wave)
+  int nvt;
+  {
+    const int64_t left = row_end - (row0 + wm * 64);
+    nvt = left >= 64 ? 4 : (left <= 0 ? 0 : (int)((left + 15) / 16));
+    nvt = __builtin_amdgcn_readfirstlane(nvt);
+  }
   // this lane's scale words: plane gq / 2 (NVFP4), row r
   const int splane = FMT == kNV ? (gq >> 1) : 0;
   const int srd = C::SGRP ? splane * (C::ROWS / 16) * C::ISTR + (r >> 2) * C::ISTR + (r & 3) * 16
@@ -466,16 +509,30 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
       sync(st + 2 <= nstages - 1 ? last - (st + 2) : 0);
     }
   } else {
+    // Row blocks cut short take the per-tile form of the step through their own copy
+    // of the loop (two forms in one loop would double the live registers)
+    auto plain = [&](auto partial) {
+      constexpr bool PART = decltype(partial)::value;
 #pragma unroll
-    for (int t = 0; t < C::NBUF - 1; ++t)
-      if (t < nstages) issue(t);
-    sync(nstages - 1 < C::NBUF - 2 ? nstages - 1 : C::NBUF - 2);
-    for (int64_t st = 0; st < nstages; ++st) {
-      const int64_t t = st + C::NBUF - 1;
-      if (t < nstages) issue(t);
-      const uint8_t* cur = tsm + (int)(st % C::NBUF) * C::STAGE;
-      tile_step<FMT, BM, BN>(cur, stage_scales(st, cur), gcol, r, gq, wm, wn, acc);
-      sync((t < nstages ? t : nstages - 1) - (st + 1));
+      for (int t = 0; t < C::NBUF - 1; ++t)
+        if (t < nstages) issue(t);
+      sync(nstages - 1 < C::NBUF - 2 ? nstages - 1 : C::NBUF - 2);
+      for (int64_t st = 0; st < nstages; ++st) {
+        const int64_t t = st + C::NBUF - 1;
+        if (t < nstages) issue(t);
+        const uint8_t* cur = tsm + (int)(st % C::NBUF) * C::STAGE;
+        tile_step<FMT, BM, BN, PART>(cur, stage_scales(st, cur), gcol, r, gq, wm, wn, acc, nvt);
+        sync((t < nstages ? t : nstages - 1) - (st + 1));
+      }
+    };
+    if constexpr (BM == 128) {   // (the 256-row tile: dense only, no copy)
+      if (nvt < C::MI) {
+        plain(std::true_type{});
+      } else {
+        plain(std::false_type{});
+      }
+    } else {
+      plain(std::false_type{});
     }
   }
 
