@@ -497,28 +497,33 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
   stream_w_load<FMT, SVEC>(wrow, wsrow, 0, K, KS, gq, wA, sA);
   stage_store<FMT, MT>(a_lds[0], s_lds[0], srow, sseg, st);
   __syncthreads();
+  // (the prefetch of the chunk after the last one is skipped: it would only make the
+  // last waves wait for loads nothing uses)
   for (int64_t c = 0; c < nchunks; c += 2) {
-    // chunk c from (buffer 0, wA); prefetch chunk c+1 (clamped) into (buffer 1, wB)
-    {
-      const int64_t cn = c + 1 < nchunks ? c + 1 : c;
+    // chunk c from (buffer 0, wA); prefetch chunk c+1 into (buffer 1, wB)
+    if (c + 1 < nchunks) {
       // issued before the weight loads, so waiting for it leaves those in flight
-      st = stage_load<FMT, MT>(s_codes, s_scales, cn, KB, KS, sseg);
+      st = stage_load<FMT, MT>(s_codes, s_scales, c + 1, KB, KS, sseg);
       __builtin_amdgcn_sched_barrier(0);  // keep the staging loads ahead of the weight loads
-      stream_w_load<FMT, SVEC>(wrow, wsrow, cn, K, KS, gq, wB, sB);
+      stream_w_load<FMT, SVEC>(wrow, wsrow, c + 1, K, KS, gq, wB, sB);
       stream_compute<FMT, MT>(a_lds[0], s_lds[0], wA, sA, steps_of(c), r, gq, acc);
       stage_store<FMT, MT>(a_lds[1], s_lds[1], srow, sseg, st);
       __syncthreads();
+    } else {
+      stream_compute<FMT, MT>(a_lds[0], s_lds[0], wA, sA, steps_of(c), r, gq, acc);
+      break;
     }
-    if (c + 1 >= nchunks) break;
-    // chunk c+1 from (buffer 1, wB); prefetch chunk c+2 (clamped) into (buffer 0, wA)
-    {
-      const int64_t cn = c + 2 < nchunks ? c + 2 : c + 1;
-      st = stage_load<FMT, MT>(s_codes, s_scales, cn, KB, KS, sseg);
+    // chunk c+1 from (buffer 1, wB); prefetch chunk c+2 into (buffer 0, wA)
+    if (c + 2 < nchunks) {
+      st = stage_load<FMT, MT>(s_codes, s_scales, c + 2, KB, KS, sseg);
       __builtin_amdgcn_sched_barrier(0);
-      stream_w_load<FMT, SVEC>(wrow, wsrow, cn, K, KS, gq, wA, sA);
+      stream_w_load<FMT, SVEC>(wrow, wsrow, c + 2, K, KS, gq, wA, sA);
       stream_compute<FMT, MT>(a_lds[1], s_lds[1], wB, sB, steps_of(c + 1), r, gq, acc);
       stage_store<FMT, MT>(a_lds[0], s_lds[0], srow, sseg, st);
       __syncthreads();
+    } else {
+      stream_compute<FMT, MT>(a_lds[1], s_lds[1], wB, sB, steps_of(c + 1), r, gq, acc);
+      break;
     }
   }
 
