@@ -96,7 +96,11 @@ void moe_plan(const fp4_moe_args* a, bool w4a4, bool may_w4a16, MoePlan* pl) {
   const int64_t R = P + (sh ? a->T : 0);
   const int bm = fp4::gemm_block_rows(a->fmt, w4a4 ? fp4::kA_FP4 : fp4::kA_BF16,
                                       a->E > 0 ? P / a->E : P, a->H, a->I);
-  const int64_t nmb = (P + bm - 1) / bm + a->E;
+  // row-block table capacity: an expert with c > 0 rows takes ceil(c / bm) < c / bm + 1
+  // blocks, and at most min(E, P) experts have rows, so fewer than P / bm + min(E, P)
+  // blocks are ever used (every grouped GEMM launches this many row blocks, so the
+  // bound matters when few tokens are routed)
+  const int64_t nmb = (P + bm - 1) / bm + (a->E < P ? a->E : P);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -426,8 +430,9 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
   float* alpha13 = scal + E;
   float* g2 = scal + 2 * E;
   float* alpha2 = scal + 3 * E;
+  std::vector<float> h;
   if (nv) {   // (MXFP4 reads none of them: alpha and the block-scale rule are fixed)
-    std::vector<float> h(4 * (size_t)E, 1.0f);
+    h.assign(4 * (size_t)E, 1.0f);
     for (int64_t x = 0; x < E; ++x) {
       if (nv) {
         const float w13 = a->w13_scale_2[x], w2 = a->w2_scale_2[x];
@@ -442,8 +447,6 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
         }
       }
     }
-    name = "upload_scalars";
-    FP4_TRY(fp4::launch_upload_floats(scal, h.data(), 4 * E, s));
   }
   const float sh_g13 = (nv && w4a4) ? 1.0f / a->sh_a13_scale : 1.0f;
   const float sh_g2 = (nv && w4a4) ? 1.0f / a->sh_a2_scale : 1.0f;
@@ -451,6 +454,7 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
   const float sh_alpha2 = nv ? (w4a4 ? a->sh_w2_scale_2 * a->sh_a2_scale : a->sh_w2_scale_2) : 1.0f;
 
   // 2. dispatch bookkeeping
+  bool act_quantized = false;
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + pl.L.expert_offsets);
   int32_t* group_end = reinterpret_cast<int32_t*>(ws + pl.group_end);
   int32_t* sorted_rows = reinterpret_cast<int32_t*>(ws + pl.L.sorted_rows);
@@ -476,7 +480,23 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
     pp.mblk_row0 = mblk_row0;
     pp.group_end = group_end;
     pp.chunk_base = reinterpret_cast<int32_t*>(ws + pl.chunk_base);
-    FP4_TRY(fp4::launch_permute(pp, s, &name));
+    // the scalar upload travels with the dispatch launch (its own launch only when
+    // the dispatch takes several), and so may the GEMM1 activation quantization
+    pp.up_dst = nv ? scal : nullptr;
+    pp.up_n = nv ? (int)(4 * E) : 0;
+    pp.q_fmt = -1;
+    if (w4a4) {
+      pp.q_fmt = fmt;
+      pp.q_x = static_cast<const uint16_t*>(a->hidden_bf16);
+      pp.q_K = H;
+      pp.q_codes = ws + pl.L.x_codes;
+      pp.q_scales = ws + pl.L.x_scales;
+      pp.q_routed = nv ? 1 : 0;      // NVFP4: each routed row under its expert's scale
+      pp.q_rows = nv ? P : T;        // MXFP4: each token once
+      pp.q_g_off = 0;                // 1/a13_scale[e] are the first E uploaded values
+      pp.q_g = 1.0f;
+    }
+    FP4_TRY(fp4::launch_permute(pp, nv ? h.data() : nullptr, s, &name, &act_quantized));
   }
 
   // 3. GEMM1 input
@@ -493,13 +513,13 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
     if (!nv) {  // MXFP4: each token once, shared by all its experts
       q.M = T;
       q.g = 1.0f;
-      FP4_TRY(fp4::launch_quant(fmt, q, s, &name));
+      if (!act_quantized) FP4_TRY(fp4::launch_quant(fmt, q, s, &name));
     } else {    // NVFP4: each routed row under its expert's activation scale
       q.M = P;
       q.row_src = src_token;
       q.row_grp = row_expert;
       q.grp_g = g13;
-      FP4_TRY(fp4::launch_quant(fmt, q, s, &name));
+      if (!act_quantized) FP4_TRY(fp4::launch_quant(fmt, q, s, &name));
       if (pl.shared) {
         fp4::QuantParams qs{};
         qs.x = a->hidden_bf16;

@@ -117,9 +117,31 @@ struct PermuteParams {
   int32_t* mblk_row0;      // [n_mblocks]
   int32_t* group_end;      // [E]
   int32_t* chunk_base;     // [ceil(T*k / kPermuteChunk)][E] scratch
+  // Work folded into the one-workgroup dispatch of small slot counts (optional):
+  //  * up_n floats (the host values passed to launch_permute) stored to up_dst;
+  //  * quantization of the GEMM1 activations when they are few (q_fmt >= 0): output
+  //    row j is hidden row src(j) under multiplier g(j), with, for q_routed, src(j) =
+  //    the token of sorted slot j and g(j) = host value q_g_off + its expert (routed
+  //    NVFP4 rows; slots past the routed count are not written), else src(j) = j and
+  //    g = q_g (one row per token).
+  float* up_dst;
+  int up_n;
+  int q_fmt;
+  int q_routed;
+  int q_g_off;
+  float q_g;
+  const uint16_t* q_x;     // bf16 [., q_K]
+  int64_t q_K, q_rows;
+  uint8_t* q_codes;        // [q_rows, q_K/2]
+  uint8_t* q_scales;       // [q_rows, q_K/G]
 };
 constexpr int kPermuteChunk = 256;   // routed slots per histogram / scatter chunk
-hipError_t launch_permute(const PermuteParams& p, hipStream_t s, const char** name);
+// Activation elements up to which the one-workgroup dispatch also quantizes them.
+constexpr int64_t kPermuteQuantMax = 65536;
+// Dispatch; *quantized tells whether the activation quantization was done in it (when
+// it was not, the caller runs the quantization pass).  up_host: the up_n floats.
+hipError_t launch_permute(const PermuteParams& p, const float* up_host, hipStream_t s,
+                          const char** name, bool* quantized);
 
 struct SwigluParams {
   const float* gu;          // [R, 2I] fp32

@@ -240,16 +240,78 @@ __global__ __launch_bounds__(kPermuteChunk) void permute_scatter_kernel(PermuteP
   p.src_token[pos] = (int32_t)(i / p.k);
 }
 
+// ---- per-expert host scalars -> device, passed by value (3 KB of kernel arguments,
+// under the 4 KB limit: the four scalars of up to 192 experts in one launch) ---------
+constexpr int kPackFloats = 768;
+struct FloatPack {
+  float v[kPackFloats];
+};
+
+// One quantization block (G elements of one row) for the folded activation
+// quantization: the quantization pass's rules and helpers, one thread per block.
+template <int FMT>
+__device__ __forceinline__ void quant_block(const uint16_t* x, float g, uint8_t* codes,
+                                            uint8_t* scale) {
+  constexpr int G = FMT == kNV ? 16 : 32;
+  float v[G];
+#pragma unroll
+  for (int q = 0; q < G / 8; ++q) {
+    const uint4 d = *reinterpret_cast<const uint4*>(x + 8 * q);
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * q + 2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+      v[8 * q + 2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < G; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t out[G / 8];
+  uint32_t sc;
+  if (FMT == kNV) {
+    float r;
+    sc = q_nv_scale(amax, g, &r);
+#pragma unroll
+    for (int q = 0; q < G / 8; ++q) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pk |= q_nv_pack2(v[8 * q + 2 * i], v[8 * q + 2 * i + 1], r) << (8 * i);
+      out[q] = pk;
+    }
+    *reinterpret_cast<uint2*>(codes) = make_uint2(out[0], out[1]);
+  } else {
+    int E;
+    sc = q_mx_scale(amax, &E);
+#pragma unroll
+    for (int q = 0; q < G / 8; ++q) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pk |= q_mx_pack2(v[8 * q + 2 * i], v[8 * q + 2 * i + 1], E) << (8 * i);
+      out[q] = pk;
+    }
+    *reinterpret_cast<uint4*>(codes) = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+  *scale = (uint8_t)sc;
+}
+
 // ---- dispatch for at most kScanThreads slots (decode token counts): counts,
 // offsets, the row-block table and the scatter in one workgroup, the same results
-// as the three kernels above --------------------------------------------------------
-__global__ __launch_bounds__(kScanThreads) void permute_small_kernel(PermuteParams p) {
+// as the three kernels above; also the per-expert scalar upload and, for few rows,
+// the GEMM1 activation quantization (saving their launches) ----------------------------
+__global__ __launch_bounds__(kScanThreads) void permute_small_kernel(PermuteParams p,
+                                                                     FloatPack pk) {
   __shared__ int buf[kScanThreads];
   __shared__ __attribute__((aligned(16))) int ids[kScanThreads];
   __shared__ int cnt[1024];
   __shared__ int ebase[1024];
+  __shared__ int q_src[kScanThreads];
+  __shared__ int q_exp[kScanThreads];
   __shared__ int total_mb;
   const int tid = threadIdx.x;
+  for (int i = tid; i < p.up_n; i += kScanThreads) p.up_dst[i] = pk.v[i];
   const int n = (int)(p.T * p.k);   // <= kScanThreads
   const int E = (int)p.E;           // <= 1024
   int e = -1;
@@ -284,24 +346,45 @@ __global__ __launch_bounds__(kScanThreads) void permute_small_kernel(PermutePara
     p.mblk_expert[i] = -1;
     p.mblk_row0[i] = 0;
   }
-  if (tid >= n) return;
-  if (e < 0) {
-    p.inverse[tid] = -1;
-    return;
+  if (tid < n) {
+    if (e < 0) {
+      p.inverse[tid] = -1;
+    } else {
+      // earlier slots routed to the same expert, four at a time
+      int rank = 0;
+      const int4* ids4 = reinterpret_cast<const int4*>(ids);
+      for (int q = 0; q < (tid >> 2); ++q) {
+        const int4 v = ids4[q];
+        rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+      }
+      for (int s2 = tid & ~3; s2 < tid; ++s2) rank += ids[s2] == e;
+      const int pos = ebase[e] + rank;
+      p.sorted_rows[pos] = tid;
+      p.inverse[tid] = pos;
+      p.row_expert[pos] = e;
+      p.src_token[pos] = (int32_t)(tid / p.k);
+      q_src[pos] = tid / p.k;
+      q_exp[pos] = e;
+    }
   }
-  // earlier slots routed to the same expert, four at a time
-  int rank = 0;
-  const int4* ids4 = reinterpret_cast<const int4*>(ids);
-  for (int q = 0; q < (tid >> 2); ++q) {
-    const int4 v = ids4[q];
-    rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+  if (p.q_fmt < 0) return;  // uniform over the workgroup
+  __syncthreads();
+  // routed rows: the slots that hold a valid expert (the routed count)
+  const int64_t rows = p.q_routed ? (int64_t)(ebase[E - 1] + cnt[E - 1]) : p.q_rows;
+  const int G = p.q_fmt == kNV ? 16 : 32;
+  const int64_t bpr = p.q_K / G;
+  for (int64_t b = tid; b < rows * bpr; b += kScanThreads) {
+    const int64_t j = b / bpr, kb = b - j * bpr;
+    const int64_t src = p.q_routed ? q_src[j] : j;
+    const float g = p.q_routed ? pk.v[p.q_g_off + q_exp[j]] : p.q_g;
+    const uint16_t* x = p.q_x + src * p.q_K + kb * G;
+    uint8_t* codes = p.q_codes + j * (p.q_K / 2) + kb * (G / 2);
+    uint8_t* scale = p.q_scales + j * bpr + kb;
+    if (p.q_fmt == kNV)
+      quant_block<kNV>(x, g, codes, scale);
+    else
+      quant_block<kMX>(x, g, codes, scale);
   }
-  for (int s2 = tid & ~3; s2 < tid; ++s2) rank += ids[s2] == e;
-  const int pos = ebase[e] + rank;
-  p.sorted_rows[pos] = tid;
-  p.inverse[tid] = pos;
-  p.row_expert[pos] = e;
-  p.src_token[pos] = (int32_t)(tid / p.k);
 }
 
 // ---- SwiGLU + requant: one lane = 8 consecutive intermediate columns -----------
@@ -395,13 +478,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   *reinterpret_cast<uint4*>(p.out + t * p.H + col) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// ---- per-expert host scalars -> device, passed by value (3 KB of kernel arguments,
-// under the 4 KB limit: the four scalars of up to 192 experts in one launch) ---------
-constexpr int kPackFloats = 768;
-struct FloatPack {
-  float v[kPackFloats];
-};
-
 __global__ __launch_bounds__(256) void upload_kernel(float* dst, int n, FloatPack pk) {
   for (int i = threadIdx.x; i < n; i += 256) dst[i] = pk.v[i];
 }
@@ -418,13 +494,27 @@ hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const PermuteParams& p, hipStream_t s, const char** name) {
+hipError_t launch_permute(const PermuteParams& p, const float* up_host, hipStream_t s,
+                          const char** name, bool* quantized) {
   *name = "permute";
+  *quantized = false;
   const int64_t n = p.T * p.k;
-  if (p.E > 1024) return hipErrorInvalidValue;
-  if (n <= kScanThreads) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kScanThreads), 0, s, p);
+  if (p.E > 1024 || p.up_n < 0) return hipErrorInvalidValue;
+  if (n <= kScanThreads && p.up_n <= kPackFloats) {
+    PermuteParams q = p;
+    const bool fold_q = p.q_fmt >= 0 && p.q_rows * p.q_K <= kPermuteQuantMax &&
+                        p.q_rows <= kScanThreads &&
+                        (!p.q_routed || p.q_g_off + p.E <= p.up_n);
+    if (!fold_q) q.q_fmt = -1;
+    FloatPack pk;
+    for (int i = 0; i < kPackFloats; ++i) pk.v[i] = i < p.up_n ? up_host[i] : 0.f;
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kScanThreads), 0, s, q, pk);
+    *quantized = fold_q;
     return hipGetLastError();
+  }
+  if (p.up_n > 0) {
+    hipError_t err = launch_upload_floats(p.up_dst, up_host, p.up_n, s);
+    if (err != hipSuccess) return err;
   }
   const int64_t nchunks = (n + kPermuteChunk - 1) / kPermuteChunk;
   if (nchunks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
