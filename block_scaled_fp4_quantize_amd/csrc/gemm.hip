@@ -632,8 +632,10 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   if (fast && !p.mblk_expert && p.M > 64) return launch_gemm_tiled(fmt, p, s, name);
   // at most 16 rows (one 16-row activation tile): activations resident in LDS with
   // a deep weight stream, when they fit; two-tile blocks measure faster on the
-  // streaming kernel below
-  if (fast && one && resident_fits(fmt, 1, p.M, p.N, p.K))
+  // streaming kernel below, and so do MXFP4 expert tables of 16-row blocks (many
+  // experts with a few rows each: 64 weight rows per workgroup amortize the staging)
+  const bool grouped_mx = p.mblk_expert && fmt == kMX;
+  if (fast && one && !grouped_mx && resident_fits(fmt, 1, p.M, p.N, p.K))
     return launch_gemm_resident(fmt, 1, p, s, name);
   if (fast) {
     if (fmt == kNV) return one ? launch_stream<kNV, 1>(p, s, name) : launch_stream<kNV, 2>(p, s, name);
