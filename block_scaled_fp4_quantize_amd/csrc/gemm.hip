@@ -635,7 +635,8 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   // streaming kernel below, and so do MXFP4 expert tables of 16-row blocks (many
   // experts with a few rows each: 64 weight rows per workgroup amortize the staging)
   const bool grouped_mx = p.mblk_expert && fmt == kMX;
-  if (fast && one && !grouped_mx && resident_fits(fmt, 1, p.M, p.N, p.K))
+  if (fast && one && !grouped_mx &&
+      resident_fits(fmt, 1, p.mblk_expert ? 16 : p.M, p.N, p.K, p.mblk_expert ? p.n_mblocks : 1))
     return launch_gemm_resident(fmt, 1, p, s, name);
   if (fast) {
     if (fmt == kNV) return one ? launch_stream<kNV, 1>(p, s, name) : launch_stream<kNV, 2>(p, s, name);

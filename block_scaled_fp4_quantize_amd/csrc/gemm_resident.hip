@@ -470,23 +470,26 @@ int64_t resident_lds_bytes(int fmt, int mt, int ksplit, int64_t K) {
          (int64_t)(ksplit - 1) * (4 / ksplit) * mt * 1024;
 }
 
-int resident_ksplit(int64_t M, int64_t N, int64_t K) {
-  // split K while the workgroups would not cover every CU twice and each wave keeps
-  // at least 8 steps; four ways only for at most 4 rows (measured at N = 14336,
-  // K = 4096: four ways is best for 1 row, two ways from 8 rows on)
+int resident_ksplit(int64_t M, int64_t N, int64_t K, int64_t nblk) {
+  // split K while the workgroups (nblk row blocks times the weight tiles) would not
+  // cover every CU twice and each wave keeps at least 8 steps; four ways only for at
+  // most 4 rows (measured at N = 14336, K = 4096: four ways is best for 1 row, two
+  // ways from 8 rows on).  Expert tables count all their row blocks: NVFP4 MoE at
+  // T = 64 (160 row blocks) runs unsplit, 117.5 -> 112 us, and at T = 1 (9) split.
   const int64_t ns = K / kRStep;
   const int kmax = M <= 4 ? 4 : 2;   // (so two-tile blocks never split four ways)
   int ks = 1;
-  while (ks < kmax && ns / (2 * ks) >= 8 && (N + 16 * (4 / ks) - 1) / (16 * (4 / ks)) < 512)
+  while (ks < kmax && ns / (2 * ks) >= 8 &&
+         nblk * ((N + 16 * (4 / ks) - 1) / (16 * (4 / ks))) < 512)
     ks *= 2;
   return ks;
 }
 
-bool resident_fits(int fmt, int mt, int64_t M, int64_t N, int64_t K) {
+bool resident_fits(int fmt, int mt, int64_t M, int64_t N, int64_t K, int64_t nblk) {
   const int64_t G = fmt == kNV ? 16 : 32;
   const int64_t pieces = 16 * mt * (K / 32);          // 16-byte activation pieces
   return K % kRStep == 0 && (K / G) % 16 == 0 && pieces <= 256 * kResPieces &&
-         resident_lds_bytes(fmt, mt, resident_ksplit(M, N, K), K) <= kResidentMaxLds;
+         resident_lds_bytes(fmt, mt, resident_ksplit(M, N, K, nblk), K) <= kResidentMaxLds;
 }
 
 hipError_t launch_gemm_resident(int fmt, int mt, const GemmParams& p, hipStream_t s,
@@ -495,8 +498,9 @@ hipError_t launch_gemm_resident(int fmt, int mt, const GemmParams& p, hipStream_
   // streaming kernel, so only MT = 1 is built)
   if (mt != 1) return hipErrorInvalidValue;
   const int64_t rows = p.mblk_expert ? 16 : p.M;   // rows per block, at most
-  if (!resident_fits(fmt, 1, rows, p.N, p.K)) return hipErrorInvalidValue;
-  const int ks = resident_ksplit(rows, p.N, p.K);
+  const int64_t nblk = p.mblk_expert ? p.n_mblocks : 1;
+  if (!resident_fits(fmt, 1, rows, p.N, p.K, nblk)) return hipErrorInvalidValue;
+  const int ks = resident_ksplit(rows, p.N, p.K, nblk);
   return fmt == kNV ? launch_res_split<kNV, 1>(ks, p, s, name)
                     : launch_res_split<kMX, 1>(ks, p, s, name);
 }

@@ -88,8 +88,9 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
 // tile per workgroup: mt must be 1); usable when resident_fits()
 constexpr int64_t kResidentMaxLds = 160 * 1024;
 int64_t resident_lds_bytes(int fmt, int mt, int ksplit, int64_t K);
-int resident_ksplit(int64_t M, int64_t N, int64_t K);   // waves that split K: 1, 2 or 4
-bool resident_fits(int fmt, int mt, int64_t M, int64_t N, int64_t K);
+// nblk: row blocks of the launch (the expert table's capacity, or 1 when dense)
+int resident_ksplit(int64_t M, int64_t N, int64_t K, int64_t nblk);   // 1, 2 or 4 waves split K
+bool resident_fits(int fmt, int mt, int64_t M, int64_t N, int64_t K, int64_t nblk);
 hipError_t launch_gemm_resident(int fmt, int mt, const GemmParams& p, hipStream_t s,
                                 const char** name);
 // tiled kernel for many activation rows (fp4 activations, K % 128 == 0, 128-row
