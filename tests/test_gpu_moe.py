@@ -283,6 +283,12 @@ SMALL = [
     ("nvfp4", "w4a4", dict(T=40, H=256, I=96, E=16, k=4, shared=False)),
     ("mxfp4", "w4a4", dict(T=33, H=256, I=96, E=16, k=4, shared=True)),
     ("nvfp4", "w4a4", dict(T=1, H=64, I=48, E=4, k=1, shared=False)),
+    # more NVFP4 experts than one by-value scalar pack holds (4 scalars each, 192
+    # experts at most): the scalars take their own launch and the dispatch runs as three
+    # kernels even at this token count; and a token count whose activations are too
+    # many to quantize inside the one-workgroup dispatch
+    ("nvfp4", "w4a4", dict(T=3, H=64, I=32, E=200, k=2, shared=False)),
+    ("nvfp4", "w4a4", dict(T=100, H=1024, I=64, E=8, k=2, shared=True)),
     # >= 48 routed rows per expert on average, H and I multiples of 128: the grouped
     # GEMMs run on 128-row tiles, with ragged expert row counts
     ("nvfp4", "w4a4", dict(T=150, H=256, I=128, E=4, k=2, shared=True)),
