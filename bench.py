@@ -477,7 +477,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X)", file=sys.stderr)
+              "(the kernels run on a single MI355X; sharding is not implemented)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
