@@ -96,18 +96,31 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 constexpr int kScanThreads = 1024;
 
 __device__ int block_exclusive_scan(int x, int* buf) {
-  // Hillis-Steele inclusive scan over kScanThreads values, then shift
-  const int tid = threadIdx.x;
-  buf[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+  // exclusive scan over kScanThreads values: an inclusive scan within each wave by
+  // lane shuffles, a scan of the wave totals by wave 0, then the earlier waves' total
+  // added (integer sums: the same result as any other order); three barriers
+  constexpr int kWaves = kScanThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int v = x;
+#pragma unroll 1
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
   }
-  const int incl = buf[tid];
+  if (lane == 63) buf[w] = v;
   __syncthreads();
+  if (w == 0) {
+    int t = lane < kWaves ? buf[lane] : 0;
+#pragma unroll 1
+    for (int off = 1; off < kWaves; off <<= 1) {
+      const int y = __shfl_up(t, off, 64);
+      if (lane >= off) t += y;
+    }
+    if (lane < kWaves) buf[kWaves + lane] = t;
+  }
+  __syncthreads();
+  const int incl = v + (w > 0 ? buf[kWaves + w - 1] : 0);
+  __syncthreads();  // (buf is reused by the next scan)
   return incl - x;
 }
 
@@ -240,6 +253,8 @@ __global__ __launch_bounds__(kPermuteChunk) void permute_scatter_kernel(PermuteP
   p.src_token[pos] = (int32_t)(i / p.k);
 }
 
+constexpr int kRankE = 256;  // experts up to which the dispatch ranks by wave histograms
+
 // ---- per-expert host scalars -> device, passed by value (3 KB of kernel arguments,
 // under the 4 KB limit: the four scalars of up to 192 experts in one launch) ---------
 constexpr int kPackFloats = 768;
@@ -309,6 +324,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_small_kernel(PermutePara
   __shared__ int ebase[1024];
   __shared__ int q_src[kScanThreads];
   __shared__ int q_exp[kScanThreads];
+  __shared__ int whist[kScanThreads / 64][kRankE];
   __shared__ int total_mb;
   const int tid = threadIdx.x;
   for (int i = tid; i < p.up_n; i += kScanThreads) p.up_dst[i] = pk.v[i];
@@ -346,14 +362,34 @@ __global__ __launch_bounds__(kScanThreads) void permute_small_kernel(PermutePara
     p.mblk_expert[i] = -1;
     p.mblk_row0[i] = 0;
   }
+  // rank of a slot among the earlier slots routed to the same expert: with at most
+  // kRankE experts, the count over earlier waves comes from per-wave histograms and
+  // only the own wave's earlier lanes are compared; else all earlier slots are
+  const bool whist_ok = E <= kRankE;
+  if (whist_ok) {
+    for (int i = tid; i < (kScanThreads / 64) * kRankE; i += kScanThreads) (&whist[0][0])[i] = 0;
+    __syncthreads();
+    if (e >= 0) atomicAdd(&whist[tid >> 6][e], 1);
+    __syncthreads();
+    if (tid < E) {  // exclusive prefix over the waves, per expert
+      int run = 0;
+      for (int w = 0; w < kScanThreads / 64; ++w) {
+        const int c2 = whist[w][tid];
+        whist[w][tid] = run;
+        run += c2;
+      }
+    }
+    __syncthreads();
+  }
   if (tid < n) {
     if (e < 0) {
       p.inverse[tid] = -1;
     } else {
-      // earlier slots routed to the same expert, four at a time
       int rank = 0;
       const int4* ids4 = reinterpret_cast<const int4*>(ids);
-      for (int q = 0; q < (tid >> 2); ++q) {
+      const int q0 = whist_ok ? (tid & ~63) >> 2 : 0;   // first int4 to compare
+      if (whist_ok) rank = whist[tid >> 6][e];
+      for (int q = q0; q < (tid >> 2); ++q) {
         const int4 v = ids4[q];
         rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
       }
