@@ -215,3 +215,26 @@ def test_single_hip_runtime_in_process():
                          cwd=os.path.dirname(os.path.dirname(__file__)))
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+def test_row_block_capacity_bound_exhaustive():
+    # The MoE row-block table reserves ceil(P / bm) + min(E, P) blocks for P routed rows
+    # over E experts at bm rows per block.  Every routing must fit: over all ways of
+    # splitting P rows among at most E experts, sum_e ceil(c_e / bm) never exceeds it.
+    def partitions(n, parts, cap):
+        # non-increasing splits of n into at most `parts` positive parts <= cap
+        if n == 0:
+            yield []
+            return
+        if parts == 0:
+            return
+        for first in range(min(n, cap), 0, -1):
+            for rest in partitions(n - first, parts - 1, first):
+                yield [first] + rest
+
+    for bm in (1, 2, 3, 16):
+        for E in range(1, 7):
+            for P in range(0, 19):
+                cap = -(-P // bm) + min(E, P)
+                worst = max(sum(-(-c // bm) for c in split) for split in partitions(P, E, P))
+                assert worst <= cap, (bm, E, P, worst, cap)
