@@ -1,36 +1,48 @@
 #!/usr/bin/env python3
 """Throughput of the block-scaled FP4 hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W]
-                    [--workload decode|prefill|prefill-mxfp4|moe-nvfp4|moe-mxfp4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens T]
 
-Default workload (decode): MXFP4 W4A4 GEMM, N=14336, K=4096, activations
-[32, 4096] bf16 N(0,1) with 1% x20 outliers quantized on the fly.  One step = the
-activation quantization plus the GEMM at M=32 (the two launches the fused
-fp4_gemm call makes, issued separately so the GEMM can be timed by itself).  The
-weights rotate over enough copies that the set exceeds the 256 MB last-level
-cache, so the GEMM streams them from HBM every step.  M=1 and M=8 are measured the
-same way and reported under "per_m".
+The default run measures every workload of the metric -- FP4 GEMM TFLOP/s and GB/s
+(with roofline fractions) at decode M = 1..32 and prefill M = 8192, and MoE tokens/s
+-- and prints ONE JSON line.  Its headline is the decode GEMM at M = 32:
 
-Other workloads (one JSON line each, not the default):
-  prefill    NVFP4 W4A4 GEMM M=8192 N=4096 K=4096, fused quantization, bf16 out
+  decode   MXFP4 W4A4 GEMM, N=14336, K=4096, activations [M, 4096] bf16 N(0,1) with
+           1% x20 outliers quantized on the fly, M = 1, 8, 32 (headline M = 32).  One
+           step = the activation quantization plus the GEMM (the two launches of a
+           fused fp4_gemm call, issued separately so the GEMM is timed by itself too).
+           The weights rotate over copies that together exceed the 256 MB last-level
+           cache, so every step streams them from HBM.
+
+and the other workloads ride along as records under "workloads":
+
+  w4a16-small    NVFP4 W4A16 linear M=4 N=256 K=512 (launch-latency bound: us)
+  prefill-nvfp4  NVFP4 W4A4 GEMM M=8192 N=4096 K=4096, fused activation quant, bf16 out
   prefill-mxfp4  the same GEMM in MXFP4
-  moe-nvfp4  NVFP4 MoE, 128 experts top-8, hidden 2048, intermediate 768, T=--tokens
-  moe-mxfp4  MXFP4 MoE, 256 experts top-8 + shared, hidden 6144, intermediate 2048,
-             Zipf(1.1) routing, T=--tokens
+  moe-nvfp4      NVFP4 MoE, 128 experts top-8, hidden 2048, intermediate 768, T = 1, 64, 4096
+  moe-mxfp4      MXFP4 MoE, 256 experts top-8 + shared, hidden 6144, intermediate 2048,
+                 Zipf(1.1) routing, T = 64, 8192
 
-Timing: the launches are captured in HIP graphs so host launch overhead stays
-out of the GPU timeline.  W untimed warmup steps, then exactly K steps replayed
-between two events on the launch stream, with torch.cuda.synchronize() on both
-sides.  The dominant kernel's average duration is measured the same way from a
-graph of K back-to-back launches of that kernel alone (it includes the small gap
-between graph nodes).  The CPU baseline times the oracle (test infrastructure, the emulation
-definition in float64) on a bounded sample of the same workload.
+--workload NAME measures one of them alone (its record becomes the line; used for
+profiling runs).
+
+Timing: every measured sequence is captured in a HIP graph (host launch overhead stays
+out of the GPU timeline).  W untimed warmup steps, then the graph of exactly K steps is
+replayed in 10 timed samples between two events on the launch stream, with
+torch.cuda.synchronize() on both sides of each; the figure is the median sample.  The
+dominant kernel's average launch time comes the same way from a graph of back-to-back
+launches of that kernel alone (at least 50 per sample).  MoE records time the whole
+fp4_moe_grouped_gemm call (all its launches, from bf16 hidden states and routing to
+bf16 output); the router is timed on its own.  The CPU baseline times the oracle (test
+infrastructure: the emulation definition in float64) on a bounded sample of each
+workload, about 3 s each.
 """
 import argparse
 import hashlib
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -39,56 +51,63 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp4": 10100.0, "fp8": 5000.0}
-KERNEL_SOURCES = ["gemm.hip", "gemm_tile.hip", "gemm_resident.hip", "quant.hip", "moe.hip", "device.h",
-                  "internal.h"]
+SAMPLES = 10
+CPU_TARGET_S = 3.0
+CSRC = os.path.join(ROOT, "block_scaled_fp4_quantize_amd", "csrc")
 
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "prefill-mxfp4", "moe-nvfp4", "moe-mxfp4"])
-    p.add_argument("--tokens", type=int, default=None, help="MoE token count")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="all",
+                   choices=["all", "decode", "w4a16-small", "prefill-nvfp4", "prefill-mxfp4",
+                            "moe-nvfp4", "moe-mxfp4",
+                            "prefill"])            # (old name of prefill-nvfp4)
+    p.add_argument("--tokens", type=int, default=None, help="MoE token count (one)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain elementwise kernel over 256 MiB (counter scaling)")
     return p.parse_args()
 
 
-def kernel_source_hash():
+# ---------------------------------------------------------------------------------
+# stored counter figures
+# ---------------------------------------------------------------------------------
+
+
+def source_hash(files):
     h = hashlib.sha256()
-    for n in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_scaled_fp4_quantize_amd", "csrc", n), "rb") as f:
+    for n in files:
+        with open(os.path.join(CSRC, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(key):
-    """HBM bytes per launch from the committed counter summary, if it was taken on
-    the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current sources of that kernel; otherwise None."""
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
     e = d.get(key)
-    if not e or e.get("src_hash") != kernel_source_hash():
+    if not e or "sources" not in e or e.get("src_hash") != source_hash(e["sources"]):
         return None
     return e.get("bytes_per_launch")
 
 
 # ---------------------------------------------------------------------------------
-# GPU side
+# GPU timing
 # ---------------------------------------------------------------------------------
 
 
 def capture(torch, fn, n):
     """A HIP graph of n calls fn(0) .. fn(n-1), captured on a side stream after one
-    eager call (the library launches on torch's current stream, which during
-    capture is the capturing stream)."""
+    eager call (the library launches on torch's current stream, which during capture
+    is the capturing stream)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -103,25 +122,78 @@ def capture(torch, fn, n):
     return g
 
 
-def timed_graph(torch, fn, steps, warmup):
-    """W untimed warmup steps, then exactly K steps replayed from one graph between
-    two events, with synchronizations on both sides.  Returns (ms per step, wall s)."""
+def measure(torch, fn, steps, warmup, samples=SAMPLES):
+    """W untimed warmup steps, then `samples` timed replays of a graph of exactly
+    `steps` calls.  Returns (median ms per call, [ms per call of each sample], wall s
+    of the timed replays)."""
     if warmup > 0:
         capture(torch, fn, warmup).replay()
     g = capture(torch, fn, steps)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(samples)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps, time.perf_counter() - wall0
+    for a, b in ev:
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [a.elapsed_time(b) / steps for a, b in ev]
+    return statistics.median(per), per, wall
 
 
-def bench_decode(args, torch, F):
+def kernel_avg_us(torch, fn, steps, warmup):
+    """Average launch time (us) of one kernel from graphs of back-to-back launches."""
+    ms, _, _ = measure(torch, fn, max(steps, 50), warmup)
+    return ms * 1e3
+
+
+def copy_bandwidth(torch):
+    """Achievable HBM bandwidth: a plain device-to-device copy of 2 GiB (read + write
+    counted), graph of back-to-back copies, median sample."""
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ms, _, _ = measure(torch, lambda i: dst.copy_(src), 10, 2, samples=5)
+    gbs = 2 * 4 * n / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GBps": round(gbs, 1), "bytes_per_copy": 2 * 4 * n,
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": "torch copy_ of 2 GiB float32, read + write, graph of 10 copies, median of 5"}
+
+
+def hbm_roof(achieved_gbs, copy, traffic=None, **extra):
+    r = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    if copy:
+        r["frac_of_copy"] = round(achieved_gbs / copy["GBps"], 4)
+    r.update(extra)
+    return r
+
+
+def mfma_roof(achieved_tf, peak, traffic=None, **extra):
+    r = {"bound": "mfma", "achieved": round(achieved_tf, 1), "peak": peak, "unit": "TFLOP/s",
+         "frac": round(achieved_tf / peak, 4), "traffic": traffic}
+    r.update(extra)
+    return r
+
+
+def bf16_tensor(torch, x, dev):
     import numpy as np
+    import synth
+    bits, vals = synth.bf16_bits(x)
+    return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16), vals
+
+
+# ---------------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------------
+
+
+def bench_decode(args, torch, F, copy):
     import synth
     dev = torch.device("cuda:0")
     N, K, MMAX = 14336, 4096, 32
@@ -136,15 +208,14 @@ def bench_decode(args, torch, F):
     ws = torch.empty((copies, N, K // 32), dtype=torch.uint8, device=dev)
     wc[:] = wc0
     ws[:] = ws0
-    a32 = synth.with_outliers(synth.normal((MMAX, K), seed=0, role=synth.ACT), seed=0)
-    bits, _ = synth.bf16_bits(a32)
-    a = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    a, _ = bf16_tensor(torch, synth.with_outliers(synth.normal((MMAX, K), seed=0, role=synth.ACT),
+                                                  seed=0), dev)
     codes = torch.empty((MMAX, K // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((MMAX, K // 32), dtype=torch.uint8, device=dev)
     out = torch.empty((MMAX, N), dtype=torch.bfloat16, device=dev)
     names = {}
 
-    def run(M, steps, warmup):
+    def run(M):
         def quant(i):
             F.fp4_quantize_act(F.FP4_MXFP4, a, M, K, K, 1.0, codes, scales)
             names["quant"] = F.fp4_last_kernel()
@@ -158,51 +229,85 @@ def bench_decode(args, torch, F):
         def step(i):
             quant(i)
             gemm(i)
-        # the step: activation quantization + GEMM, K times
-        ms, wall = timed_graph(torch, step, steps, warmup)
-        # the GEMM kernel alone: K back-to-back launches (same weight rotation)
+        ms, per, wall = measure(torch, step, args.steps, args.warmup)
         quant(0)
-        kms, _ = timed_graph(torch, gemm, steps, warmup)
-        step_bytes = wbytes + M * K * 2 + M * N * 2                  # weights once, bf16 in, bf16 out
-        kern_bytes = wbytes + M * (K // 2 + K // 32) + M * N * 2    # the GEMM's own operands
+        kus = kernel_avg_us(torch, gemm, args.steps, args.warmup)
+        qus = kernel_avg_us(torch, quant, args.steps, args.warmup)
+        step_bytes = wbytes + M * K * 2 + M * N * 2                 # weights once, bf16 in, bf16 out
+        kern_bytes = wbytes + M * (K // 2 + K // 32) + M * N * 2   # the GEMM's own operands
         flops = 2.0 * M * N * K
-        return dict(M=M, ms_per_step=ms, gemm_us=kms * 1e3, wall_s=wall,
-                    step_GBps=step_bytes / (ms * 1e-3) / 1e9,
-                    gemm_GBps=kern_bytes / (kms * 1e-3) / 1e9,
-                    gemm_TFLOPs=flops / (kms * 1e-3) / 1e12,
-                    gemm_frac_hbm=kern_bytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    step_bytes=step_bytes, kern_bytes=kern_bytes, kernel=names.get("gemm"))
+        kgbs = kern_bytes / (kus * 1e-6) / 1e9
+        return {
+            "M": M, "ms_per_step": ms, "samples_ms": [round(x, 6) for x in per], "wall_s": wall,
+            "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+            "step_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 3),
+            "gemm_us": round(kus, 3), "quant_us": round(qus, 3),
+            "gemm_TFLOPs": round(flops / (kus * 1e-6) / 1e12, 3),
+            "roofline": hbm_roof(kgbs, copy, stored_traffic(f"decode_gemm_M{M}"),
+                                 kernel=names.get("gemm"), algorithmic_bytes_per_launch=kern_bytes,
+                                 avg_launch_us=round(kus, 3)),
+        }
 
-    per_m = {}
-    for M in (1, 8):
-        per_m[M] = run(M, max(20, args.steps // 2), max(5, args.warmup // 2))
-    main = run(MMAX, args.steps, args.warmup)
-    per_m[MMAX] = main
-    traffic = stored_traffic(f"decode_gemm_M{MMAX}")
-    res = {
+    per_m = {M: run(M) for M in (1, 8, MMAX)}
+    main = per_m[MMAX]
+    rec = {
         "metric": "FP4 decode GEMM GB/s (MXFP4 W4A4, M=32, N=14336, K=4096)",
-        "value": round(main["step_GBps"], 2),
-        "unit": "GB/s",
-        "ms_per_step": main["ms_per_step"],
+        "value": main["step_GBps"], "unit": "GB/s", "ms_per_step": main["ms_per_step"],
         "dtype": "fp4",
         "config": {"workload": "MXFP4 W4A4 decode GEMV/GEMM, M=32 (also M=1, 8 under per_m), "
                                "N=14336, K=4096, activations quantized on the fly",
                    "M": MMAX, "N": N, "K": K, "weight_copies_rotated": copies},
-        "roofline": {"bound": "hbm", "achieved": round(main["gemm_GBps"], 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(main["gemm_frac_hbm"], 4), "traffic": traffic,
-                     "kernel": main["kernel"], "algorithmic_bytes_per_launch": main["kern_bytes"],
-                     "avg_launch_us": round(main["gemm_us"], 3)},
-        "per_m": {str(m): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
-                           if k in ("ms_per_step", "gemm_us", "step_GBps", "gemm_GBps",
-                                    "gemm_TFLOPs", "gemm_frac_hbm", "kernel")}
+        "roofline": main["roofline"],
+        "per_m": {str(m): {k: v for k, v in r.items() if k not in ("wall_s",)}
                   for m, r in per_m.items()},
-        "wall_s_timed": main["wall_s"],
+        "samples_ms": main["samples_ms"], "wall_s_timed": main["wall_s"],
     }
-    return res
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_decode()
+    return rec
 
 
-def bench_prefill(args, torch, F, fmt="nvfp4"):
+def bench_w4a16_small(args, torch, F, copy):
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    M, N, K = 4, 256, 512
+    w = synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT)
+    ws2 = float(np.float32(np.abs(w).max()) / np.float32(2688.0))
+    wd = torch.from_numpy(w).to(dev)
+    wc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    wsc = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    F.fp4_quantize_weight(F.FP4_NVFP4, wd, N, K, K, ws2, wc, wsc)
+    a, _ = bf16_tensor(torch, synth.normal((M, K), seed=0, role=synth.ACT), dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    names = {}
+
+    def gemm(i):
+        F.fp4_gemm(F.FP4_NVFP4, F.FP4_W4A16, M, N, K, a, K, None, None, wc, wsc, ws2, 0.0,
+                   out, N, F.FP4_OUT_BF16, 0, None, 0)
+        names["gemm"] = F.fp4_last_kernel()
+
+    ms, per, wall = measure(torch, gemm, max(args.steps, 50), args.warmup)
+    nbytes = N * (K // 2 + K // 16) + M * K * 2 + M * N * 2
+    flops = 2.0 * M * N * K
+    rec = {
+        "metric": "NVFP4 W4A16 linear us per call (M=4, N=256, K=512)",
+        "value": round(ms * 1e3, 3), "unit": "us", "higher_is_better": False,
+        "ms_per_step": ms, "dtype": "bf16",
+        "config": {"workload": "NVFP4 W4A16 linear, weights [256, 512], activations [4, 512] bf16",
+                   "M": M, "N": N, "K": K},
+        "roofline": hbm_roof(nbytes / (ms * 1e-3) / 1e9, copy, None, kernel=names.get("gemm"),
+                             algorithmic_bytes_per_launch=nbytes, avg_launch_us=round(ms * 1e3, 3),
+                             note="launch-latency bound: 79,872 bytes take 10 ns at 8 TB/s"),
+        "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 4),
+        "samples_ms": [round(x, 6) for x in per], "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_w4a16_small()
+    return rec
+
+
+def bench_prefill(args, torch, F, copy, fmt):
     import numpy as np
     import synth
     dev = torch.device("cuda:0")
@@ -216,9 +321,8 @@ def bench_prefill(args, torch, F, fmt="nvfp4"):
     wsc = torch.empty((N, K // G), dtype=torch.uint8, device=dev)
     F.fp4_quantize_weight(fm, wd, N, K, K, ws2, wc, wsc)
     del wd
-    bits, av = synth.bf16_bits(synth.normal((M, K), seed=0, role=synth.ACT, index=3))
+    a, av = bf16_tensor(torch, synth.normal((M, K), seed=0, role=synth.ACT, index=3), dev)
     s = float(np.float32(np.abs(av).max()) / np.float32(2688.0)) if nv else 1.0
-    a = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((M, K // G), dtype=torch.uint8, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -236,134 +340,173 @@ def bench_prefill(args, torch, F, fmt="nvfp4"):
         quant(i)
         gemm(i)
 
-    steps = max(5, args.steps // 20)
-    ms, wall = timed_graph(torch, step, steps, max(2, args.warmup // 10))
-    kms, _ = timed_graph(torch, gemm, steps, 2)
+    ms, per, wall = measure(torch, step, args.steps, args.warmup)
+    kus = kernel_avg_us(torch, gemm, args.steps, 2)
     flops = 2.0 * M * N * K
-    tf = flops / (kms * 1e-3) / 1e12
+    tf = flops / (kus * 1e-6) / 1e12
     # NVFP4 runs its products on fp16 MFMAs (exact decode), MXFP4 on the scaled FP4 MFMA
     pk = PEAK_TFLOPS["fp16"] if nv else PEAK_TFLOPS["fp4"]
     F_ = fmt.upper()
-    return {
+    rec = {
         "metric": f"FP4 prefill GEMM TFLOP/s ({F_} W4A4, M=8192, N=4096, K=4096)",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": ms,
-        "steps_override": steps,
         "dtype": "fp16" if nv else "fp4",
         "config": {"workload": f"{F_} W4A4 prefill GEMM, fused activation quant, bf16 out",
                    "M": M, "N": N, "K": K},
-        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": pk,
-                     "unit": "TFLOP/s", "frac": round(tf / pk, 4),
-                     "frac_of_fp4_peak": round(tf / PEAK_TFLOPS["fp4"], 4),
-                     "traffic": stored_traffic("prefill_gemm_" + fmt), "kernel": names.get("gemm"),
-                     "avg_launch_us": round(kms * 1e3, 2)},
-        "wall_s_timed": wall,
+        "roofline": mfma_roof(tf, pk, stored_traffic("prefill_gemm_" + fmt),
+                              frac_of_fp4_peak=round(tf / PEAK_TFLOPS["fp4"], 4),
+                              frac_of_fp8_peak=round(tf / PEAK_TFLOPS["fp8"], 4),
+                              kernel=names.get("gemm"), algorithmic_flops_per_launch=flops,
+                              avg_launch_us=round(kus, 2)),
+        "step_GBps": round((N * K * (0.5 + 1 / G) + M * K * 2 + M * N * 2) / (ms * 1e-3) / 1e9, 1),
+        "samples_ms": [round(x, 6) for x in per], "wall_s_timed": wall,
     }
-
-
-def bench_moe(args, torch, F, fmt):
-    import numpy as np
-    from block_scaled_fp4_quantize_amd import tensors as T
-    import synth
-    dev = torch.device("cuda:0")
-    if fmt == "nvfp4":
-        E, k, H, I, T_ = 128, 8, 2048, 768, args.tokens or 64
-        shared, zipf = False, None
-    else:
-        E, k, H, I, T_ = 256, 8, 6144, 2048, args.tokens or 64
-        shared, zipf = True, 1.1
-    G = 16 if fmt == "nvfp4" else 32
-    fm = F.FP4_NVFP4 if fmt == "nvfp4" else F.FP4_MXFP4
-    n_w = E + (1 if shared else 0)
-
-    def qw(rows, cols, index, role):
-        w = torch.from_numpy(synth.normal((rows, cols), 0.02, seed=0, role=role, index=index)).to(dev)
-        ws2 = float(w.abs().max().item()) / 2688.0 if fmt == "nvfp4" else 1.0
-        ws2 = float(np.float32(ws2))
-        c = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-        s = torch.empty((rows, cols // G), dtype=torch.uint8, device=dev)
-        F.fp4_quantize_weight(fm, w, rows, cols, cols, ws2, c, s)
-        return c, s, ws2
-
-    # a few distinct experts quantized on the GPU, each further expert a row
-    # permutation of one of them (distinct memory, same value distribution)
-    n_base = 4
-    base = [(qw(2 * I, H, b, synth.W13), qw(H, I, b, synth.W2)) for b in range(n_base + 1)]
-    w13c = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
-    w13s = torch.empty((E, 2 * I, H // G), dtype=torch.uint8, device=dev)
-    w2c = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
-    w2s = torch.empty((E, H, I // G), dtype=torch.uint8, device=dev)
-    s13, s2 = np.zeros(E, np.float32), np.zeros(E, np.float32)
-    for e in range(E):
-        (c13, sc13, ws13), (c2, sc2, ws2) = base[e % n_base]
-        p13 = torch.from_numpy(synth.rows_permutation(2 * I, seed=0, index=2 * e)).to(dev)
-        p2 = torch.from_numpy(synth.rows_permutation(H, seed=0, index=2 * e + 1)).to(dev)
-        w13c[e], w13s[e], w2c[e], w2s[e] = c13[p13], sc13[p13], c2[p2], sc2[p2]
-        s13[e], s2[e] = ws13, ws2
-    sh = None
-    if shared:
-        (c13, sc13, ws13), (c2, sc2, ws2) = base[n_base]
-        sh = dict(w13_codes=c13, w13_scales=sc13, w2_codes=c2, w2_scales=sc2)
-    bits, hv = synth.bf16_bits(synth.normal((T_, H), seed=0, role=synth.HIDDEN))
-    hidden = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    if zipf:
-        logits = synth.zipf_gumbel_logits(T_, E, zipf, seed=0)
-    else:
-        logits = synth.normal((T_, E), seed=0, role=synth.LOGITS)
-    ids, w = T.topk_softmax(torch.from_numpy(logits).to(dev), k)
-    kw = {}
-    if fmt == "nvfp4":
-        a13 = np.full(E, np.float32(np.abs(hv).max() / 2688.0), np.float32)
-        a2 = np.full(E, np.float32(4.0 / 2688.0), np.float32)   # fixed calibration for timing
-        kw = dict(w13_scale_2=s13, w2_scale_2=s2, a13_scale=a13, a2_scale=a2)
-    moe = T.Moe(fmt, "w4a4", H, I, E, w13c, w13s, w2c, w2s, shared=sh, **kw)
-    out = torch.empty((T_, H), dtype=torch.bfloat16, device=dev)
-    args_c, keep = moe.args(hidden, ids, w, out)
-    wsb, need = moe.workspace_for(args_c)
-
-    def step(i):
-        F.fp4_moe_grouped_gemm(args_c, wsb, need, device_tensor=hidden)
-
-    steps = max(5, args.steps // 10)
-    ms, wall = timed_graph(torch, step, steps, max(2, args.warmup // 5))
-    touched = int(torch.unique(ids).numel())
-    wbytes_expert = 3 * H * I // 2 + 3 * H * I // G
-    bytes_ = (touched + (1 if shared else 0)) * wbytes_expert + T_ * H * 2 * 2
-    flops = 2.0 * 3 * H * I * (T_ * k + (T_ if shared else 0))
-    # Roofline of the whole fp4_moe_grouped_gemm call (all of its launches on one
-    # stream, timed by the step graph's events): weight-streaming decode token counts
-    # against HBM, large token counts against the MFMA peak of the format's
-    # instruction (NVFP4: fp16 MFMA on the exact decode; MXFP4: FP4 MFMA).
-    if T_ * k >= 32 * E:
-        peak = 2500.0 if fmt == "nvfp4" else 10100.0
-        achieved = flops / (ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": "fp4_moe_grouped_gemm (whole call)",
-                "algorithmic_flops_per_call": flops, "avg_call_us": round(ms * 1e3, 2)}
-    else:
-        achieved = bytes_ / (ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                "frac": round(achieved / 8000.0, 4), "traffic": None,
-                "kernel": "fp4_moe_grouped_gemm (whole call)",
-                "algorithmic_bytes_per_call": bytes_, "avg_call_us": round(ms * 1e3, 2)}
-    res_cpu = None
     if not args.no_cpu_baseline:
-        res_cpu = cpu_baseline_moe(fmt, hv, ids, w, w13c, w13s, w2c, w2s, s13, s2, sh, kw,
-                                   E, k, H, I)
-    out_line = {
-        "metric": f"{fmt.upper()} MoE tokens/s (T={T_})", "value": round(T_ / (ms * 1e-3), 1),
-        "unit": "tokens/s", "ms_per_step": ms, "steps_override": steps,
-        "config": {"workload": f"{fmt.upper()} W4A4 MoE E={E} top-{k} H={H} I={I} T={T_}"
-                               + (" + shared, Zipf(1.1)" if shared else ""),
-                   "experts_touched": touched},
-        "roofline": roof,
-        "achieved_GBps": round(bytes_ / (ms * 1e-3) / 1e9, 1),
-        "achieved_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
-        "wall_s_timed": wall,
-    }
-    if res_cpu is not None:
-        out_line["cpu_baseline"] = res_cpu
-    return out_line
+        rec["cpu_baseline"] = cpu_baseline_prefill(fmt=fmt)
+    return rec
+
+
+class MoeLayer:
+    """One of the two MoE layers on the device: a few experts quantized on the GPU, the
+    others seeded row permutations of them (distinct memory, same distribution)."""
+
+    def __init__(self, torch, F, fmt):
+        import numpy as np
+        import synth
+        from block_scaled_fp4_quantize_amd import tensors as T
+        self.torch, self.F, self.T_mod, self.fmt = torch, F, T, fmt
+        dev = self.dev = torch.device("cuda:0")
+        if fmt == "nvfp4":
+            E, k, H, I, shared, zipf, copies = 128, 8, 2048, 768, False, None, 2
+        else:
+            E, k, H, I, shared, zipf, copies = 256, 8, 6144, 2048, True, 1.1, 1
+        self.E, self.k, self.H, self.I, self.shared_on, self.zipf = E, k, H, I, shared, zipf
+        G = self.G = 16 if fmt == "nvfp4" else 32
+        fm = F.FP4_NVFP4 if fmt == "nvfp4" else F.FP4_MXFP4
+
+        def qw(rows, cols, index, role):
+            w = torch.from_numpy(synth.normal((rows, cols), 0.02, seed=0, role=role, index=index)).to(dev)
+            ws2 = float(np.float32(float(w.abs().max().item()) / 2688.0)) if fmt == "nvfp4" else 1.0
+            c = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+            s = torch.empty((rows, cols // G), dtype=torch.uint8, device=dev)
+            F.fp4_quantize_weight(fm, w, rows, cols, cols, ws2, c, s)
+            return c, s, ws2
+
+        n_base = 4
+        base = [(qw(2 * I, H, b, synth.W13), qw(H, I, b, synth.W2)) for b in range(n_base + 1)]
+        # `copies` full sets of expert weights, used in turn by successive steps, so
+        # that the set a decode step reads is not left in the 256 MB last-level cache
+        self.sets = []
+        s13, s2 = np.zeros(E, np.float32), np.zeros(E, np.float32)
+        for c in range(copies):
+            w13c = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+            w13s = torch.empty((E, 2 * I, H // G), dtype=torch.uint8, device=dev)
+            w2c = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+            w2s = torch.empty((E, H, I // G), dtype=torch.uint8, device=dev)
+            for e in range(E):
+                (c13, sc13, ws13), (c2, sc2, ws2) = base[e % n_base]
+                p13 = torch.from_numpy(synth.rows_permutation(2 * I, seed=c, index=2 * e)).to(dev)
+                p2 = torch.from_numpy(synth.rows_permutation(H, seed=c, index=2 * e + 1)).to(dev)
+                w13c[e], w13s[e], w2c[e], w2s[e] = c13[p13], sc13[p13], c2[p2], sc2[p2]
+                s13[e], s2[e] = ws13, ws2
+            self.sets.append((w13c, w13s, w2c, w2s))
+        self.s13, self.s2 = s13, s2
+        self.sh = None
+        if shared:
+            (c13, sc13, _), (c2, sc2, _) = base[n_base]
+            self.sh = dict(w13_codes=c13, w13_scales=sc13, w2_codes=c2, w2_scales=sc2)
+        self.wbytes_expert = 3 * H * I // 2 + 3 * H * I // G
+
+    def bench(self, args, T_, copy):
+        import numpy as np
+        import synth
+        torch, F, T = self.torch, self.F, self.T_mod
+        E, k, H, I, fmt = self.E, self.k, self.H, self.I, self.fmt
+        dev = self.dev
+        hidden, hv = bf16_tensor(torch, synth.normal((T_, H), seed=0, role=synth.HIDDEN), dev)
+        # routing of successive steps varies (a decode step's tokens reach different
+        # experts); the large batches already reach every expert
+        n_var = 8 if T_ <= 64 else 1
+        routes = []
+        for v in range(n_var):
+            if self.zipf:
+                logits = synth.zipf_gumbel_logits(T_, E, self.zipf, seed=0, index=v)
+            else:
+                logits = synth.normal((T_, E), seed=0, role=synth.LOGITS, index=v)
+            ld = torch.from_numpy(logits).to(dev)
+            routes.append((ld,) + T.topk_softmax(ld, k))
+        kw = {}
+        if fmt == "nvfp4":
+            a13 = np.full(E, np.float32(np.abs(hv).max() / 2688.0), np.float32)
+            a2 = np.full(E, np.float32(4.0 / 2688.0), np.float32)   # fixed calibration for timing
+            kw = dict(w13_scale_2=self.s13, w2_scale_2=self.s2, a13_scale=a13, a2_scale=a2)
+        out = torch.empty((T_, H), dtype=torch.bfloat16, device=dev)
+        variants, keep = [], []
+        ws_need = 0
+        for v in range(max(n_var, len(self.sets))):
+            w13c, w13s, w2c, w2s = self.sets[v % len(self.sets)]
+            moe = T.Moe(fmt, "w4a4", H, I, E, w13c, w13s, w2c, w2s, shared=self.sh, **kw)
+            _, ids, w = routes[v % n_var]
+            a, kp = moe.args(hidden, ids, w, out)
+            keep.append((moe, kp))
+            variants.append(a)
+            ws_need = max(ws_need, F.fp4_moe_workspace_size(a))
+        wsb = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+
+        def step(i):
+            F.fp4_moe_grouped_gemm(variants[i % len(variants)], wsb, ws_need, device_tensor=hidden)
+
+        ms, per, wall = measure(torch, step, args.steps, args.warmup)
+        ld0 = routes[0][0]
+        ids_r = torch.empty((T_, k), dtype=torch.int32, device=dev)
+        w_r = torch.empty((T_, k), dtype=torch.float32, device=dev)
+        router_us = kernel_avg_us(
+            torch, lambda i: F.fp4_moe_topk_softmax(ld0, T_, E, k, 1, ids_r, w_r), args.steps, 2)
+        touched = statistics.mean(int(torch.unique(r[1]).numel()) for r in routes)
+        nbytes = (touched + (1 if self.sh else 0)) * self.wbytes_expert + T_ * H * 2 * 2
+        flops = 2.0 * 3 * H * I * (T_ * k + (T_ if self.sh else 0))
+        # roofline of the whole call: weight-streaming token counts against HBM, large
+        # token counts against the MFMA peak of the format's instruction (NVFP4: fp16
+        # MFMA on the exact decode; MXFP4: FP4 MFMA)
+        if T_ * k >= 32 * E:
+            peak = PEAK_TFLOPS["fp16"] if fmt == "nvfp4" else PEAK_TFLOPS["fp4"]
+            roof = mfma_roof(flops / (ms * 1e-3) / 1e12, peak, None,
+                             kernel="fp4_moe_grouped_gemm (whole call)",
+                             algorithmic_flops_per_call=flops, avg_call_us=round(ms * 1e3, 2))
+        else:
+            roof = hbm_roof(nbytes / (ms * 1e-3) / 1e9, copy, None,
+                            kernel="fp4_moe_grouped_gemm (whole call)",
+                            algorithmic_bytes_per_call=int(nbytes), avg_call_us=round(ms * 1e3, 2))
+        label = (f"{fmt.upper()} W4A4 MoE E={E} top-{k} H={H} I={I} T={T_}"
+                 + (" + shared expert, Zipf(1.1) routing" if self.sh else ", N(0,1) logits"))
+        rec = {
+            "metric": f"{fmt.upper()} MoE tokens/s (T={T_})",
+            "value": round(T_ / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": ms,
+            "dtype": "fp16" if fmt == "nvfp4" else "fp4",
+            "config": {"workload": label, "T": T_, "experts_touched_per_step": touched,
+                       "routing_variants": n_var, "weight_sets": len(self.sets)},
+            "roofline": roof,
+            "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "achieved_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "router_us": round(router_us, 2),
+            "samples_ms": [round(x, 6) for x in per], "wall_s_timed": wall,
+        }
+        if fmt == "nvfp4":
+            rec["zero_input_scale_call"] = self.reject_case(hidden, routes[0], kw, out)
+        if not args.no_cpu_baseline:
+            rec["cpu_baseline"] = cpu_baseline_moe(self, hv, routes[0][1], routes[0][2], kw)
+        return rec
+
+    def reject_case(self, hidden, route, kw, out):
+        """A weight-only checkpoint's zero activation scale: refused, nothing launched."""
+        import numpy as np
+        F, T = self.F, self.T_mod
+        a13 = kw["a13_scale"].copy()
+        a13[3] = 0.0
+        kw2 = dict(kw, a13_scale=a13)
+        moe = T.Moe(self.fmt, "w4a4", self.H, self.I, self.E, *self.sets[0], shared=self.sh, **kw2)
+        st = moe(hidden, route[1], route[2], out, check=False)[1]
+        return F.status_str(st)
 
 
 # ---------------------------------------------------------------------------------
@@ -380,8 +523,35 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline_decode(target_s=10.0, rows=2048):
-    import numpy as np
+def host_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = None
+    return {"os_cpu_count": os.cpu_count(), "affinity_cpus": aff, "cpu_model": model,
+            "blas_threads": blas_threads()}
+
+
+def _repeat(fn, target_s):
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn(n)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            return n, el
+
+
+def cpu_baseline_decode(target_s=CPU_TARGET_S, rows=2048):
     import synth
     from oracle import gemm as OG
     from oracle import quant as OQ
@@ -390,14 +560,7 @@ def cpu_baseline_decode(target_s=10.0, rows=2048):
     wc, ws, _ = OQ.quantize_weight("mxfp4", w)          # checkpoint preparation, untimed
     a32 = synth.with_outliers(synth.normal((M, K), seed=0, role=synth.ACT), seed=0)
     _, av = synth.bf16_bits(a32)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        OG.gemm_fused("mxfp4", av, wc, ws)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
+    n, el = _repeat(lambda i: OG.gemm_fused("mxfp4", av, wc, ws), target_s)
     step_bytes = rows * (K // 2 + K // 32) + M * K * 2 + M * rows * 2
     return {"value": round(step_bytes * n / el / 1e9, 4), "unit": "GB/s",
             "cores": blas_threads(), "kind": "oracle",
@@ -405,7 +568,21 @@ def cpu_baseline_decode(target_s=10.0, rows=2048):
                       f"{el:.1f} s: activation QDQ + float64 weight dequant + float64 matmul"}
 
 
-def cpu_baseline_prefill(target_s=10.0, rows=64, fmt="nvfp4"):
+def cpu_baseline_w4a16_small(target_s=1.0):
+    import numpy as np
+    import synth
+    from oracle import gemm as OG
+    from oracle import quant as OQ
+    M, N, K = 4, 256, 512
+    wc, ws, ws2 = OQ.quantize_weight("nvfp4", synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT))
+    _, av = synth.bf16_bits(synth.normal((M, K), seed=0, role=synth.ACT))
+    n, el = _repeat(lambda i: OG.gemm_w4a16("nvfp4", av, wc, ws, ws2), target_s)
+    return {"value": round(el / n * 1e6, 2), "unit": "us", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"the whole workload, {n} repetitions in {el:.1f} s: float64 weight dequant "
+                      "+ float64 matmul"}
+
+
+def cpu_baseline_prefill(target_s=CPU_TARGET_S, rows=64, fmt="nvfp4"):
     import numpy as np
     import synth
     from oracle import gemm as OG
@@ -415,14 +592,8 @@ def cpu_baseline_prefill(target_s=10.0, rows=64, fmt="nvfp4"):
     wc, ws, ws2 = OQ.quantize_weight(fmt, w)
     _, av = synth.bf16_bits(synth.normal((M, K), seed=0, role=synth.ACT, index=3))
     s = float(np.float32(np.abs(av).max()) / np.float32(2688.0)) if fmt == "nvfp4" else 1.0
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        OG.gemm_fused(fmt, av[n * rows % M:(n * rows % M) + rows], wc, ws, ws2, s)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
+    n, el = _repeat(lambda i: OG.gemm_fused(fmt, av[i * rows % M:(i * rows % M) + rows], wc, ws,
+                                            ws2, s), target_s)
     flops = 2.0 * rows * N * K * n
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
             "kind": "oracle",
@@ -430,13 +601,14 @@ def cpu_baseline_prefill(target_s=10.0, rows=64, fmt="nvfp4"):
                       f"{n} repetitions in {el:.1f} s"}
 
 
-def cpu_baseline_moe(fmt, hv, ids, w, w13c, w13s, w2c, w2s, s13, s2, sh, kw, E, k, H, I,
-                     target_s=10.0):
+def cpu_baseline_moe(layer, hv, ids, w, kw, target_s=CPU_TARGET_S):
     """The oracle MoE layer over the first tokens of the same problem (same routing,
-    the same expert codes and scales copied to the host), token by token, for about
-    target_s seconds."""
+    the same expert codes and scales copied to the host), one token at a time, for
+    about target_s seconds of oracle time (at least one token)."""
     import numpy as np
     from oracle import moe as OM
+    fmt, E, k, H, I = layer.fmt, layer.E, layer.k, layer.H, layer.I
+    w13c, w13s, w2c, w2s = layer.sets[0]
     ids_h = ids.cpu().numpy()
     w_h = w.cpu().numpy().astype(np.float64)
     cache = {}
@@ -445,7 +617,7 @@ def cpu_baseline_moe(fmt, hv, ids, w, w13c, w13s, w2c, w2s, s13, s2, sh, kw, E, 
         if e not in cache:
             kwe = {}
             if fmt == "nvfp4":
-                kwe = dict(w13_scale_2=float(s13[e]), w2_scale_2=float(s2[e]),
+                kwe = dict(w13_scale_2=float(layer.s13[e]), w2_scale_2=float(layer.s2[e]),
                            a13_scale=float(kw["a13_scale"][e]), a2_scale=float(kw["a2_scale"][e]))
             cache[e] = OM.Expert(w13c[e].cpu().numpy(), w13s[e].cpu().numpy(),
                                  w2c[e].cpu().numpy(), w2s[e].cpu().numpy(), **kwe)
@@ -454,12 +626,12 @@ def cpu_baseline_moe(fmt, hv, ids, w, w13c, w13s, w2c, w2s, s13, s2, sh, kw, E, 
     # experts the sampled token does not reach carry no weights, only valid scales
     idle = OM.Expert(None, None, None, None, a13_scale=1.0, a2_scale=1.0)
     shared = None
-    if sh is not None:
+    if layer.sh is not None:
+        sh = layer.sh
         shared = OM.Expert(sh["w13_codes"].cpu().numpy(), sh["w13_scales"].cpu().numpy(),
                            sh["w2_codes"].cpu().numpy(), sh["w2_scales"].cpu().numpy())
-    n = 0
-    el = 0.0
-    while el < target_s and n < hv.shape[0]:
+    n, el = 0, 0.0
+    while (el < target_s or n == 0) and n < hv.shape[0]:
         experts = {int(e): expert(int(e)) for e in ids_h[n]}      # host copies, untimed
         full = [experts.get(e, idle) for e in range(E)]
         t0 = time.perf_counter()
@@ -468,9 +640,12 @@ def cpu_baseline_moe(fmt, hv, ids, w, w13c, w13s, w2c, w2s, s13, s2, sh, kw, E, 
         n += 1
     return {"value": round(n / el, 4), "unit": "tokens/s", "cores": blas_threads(),
             "kind": "oracle",
-            "sample": f"the first {n} tokens one at a time ({n} x {k} routed experts"
-                      + (" + the shared expert" if sh is not None else "")
+            "sample": f"the first {n} token(s) one at a time ({n} x {k} routed experts"
+                      + (" + the shared expert" if layer.sh is not None else "")
                       + f", H={H}, I={I}) in {el:.1f} s of oracle time"}
+
+
+# ---------------------------------------------------------------------------------
 
 
 def main():
@@ -485,6 +660,7 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
     import block_scaled_fp4_quantize_amd as F   # raises if libfp4.so is missing
+    t_start = time.perf_counter()
     if args.copy_calibration:
         # a plain elementwise kernel that reads 256 MiB and writes 256 MiB: the
         # counter scale for FETCH_SIZE / WRITE_SIZE of the kernels measured after it
@@ -494,28 +670,55 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    if args.workload == "decode":
-        res = bench_decode(args, torch, F)
-        steps = args.steps
-    elif args.workload in ("prefill", "prefill-mxfp4"):
-        res = bench_prefill(args, torch, F, "nvfp4" if args.workload == "prefill" else "mxfp4")
-        steps = res.pop("steps_override")
-    else:
-        res = bench_moe(args, torch, F, args.workload.split("-")[1])
-        steps = res.pop("steps_override")
-    line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
-            "n_gpus": 1, "steps": steps, "warmup": args.warmup,
-            "ms_per_step": round(res.pop("ms_per_step"), 6), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": res.pop("dtype", "fp4"),
+    wl = "prefill-nvfp4" if args.workload == "prefill" else args.workload
+    copy = copy_bandwidth(torch) if wl in ("all", "decode", "w4a16-small", "moe-nvfp4",
+                                          "moe-mxfp4") else None
+
+    def log(msg):
+        print(f"[bench] {msg} ({time.perf_counter() - t_start:.1f} s)", file=sys.stderr, flush=True)
+
+    records = {}
+    if wl in ("all", "decode"):
+        records["decode"] = bench_decode(args, torch, F, copy)
+        log("decode done")
+    if wl in ("all", "w4a16-small"):
+        records["w4a16-small"] = bench_w4a16_small(args, torch, F, copy)
+        log("w4a16-small done")
+    for fmt in ("nvfp4", "mxfp4"):
+        if wl in ("all", f"prefill-{fmt}"):
+            records[f"prefill-{fmt}"] = bench_prefill(args, torch, F, copy, fmt)
+            torch.cuda.empty_cache()
+            log(f"prefill-{fmt} done")
+    for fmt, toks in (("nvfp4", (1, 64, 4096)), ("mxfp4", (64, 8192))):
+        if wl not in ("all", f"moe-{fmt}"):
+            continue
+        layer = MoeLayer(torch, F, fmt)
+        for T_ in ((args.tokens,) if args.tokens else toks):
+            records[f"moe-{fmt}-T{T_}"] = layer.bench(args, T_, copy)
+            torch.cuda.empty_cache()
+            log(f"moe-{fmt} T={T_} done")
+        del layer
+        torch.cuda.empty_cache()
+
+    head_key = "decode" if wl == "all" else next(iter(records))
+    head = dict(records[head_key])
+    line = {"metric": head.pop("metric"), "value": head.pop("value"), "unit": head.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(head.pop("ms_per_step"), 6),
+            "higher_is_better": head.pop("higher_is_better", True),
+            "scaling": "weak", "vs_baseline": None, "dtype": head.pop("dtype", "fp4"),
             "data": "synthetic (seeded N(0,0.02) weights quantized on the GPU, N(0,1) activations)",
-            "config": res.pop("config")}
-    line.update(res)
-    if not args.no_cpu_baseline:
-        if args.workload == "decode":
-            line["cpu_baseline"] = cpu_baseline_decode()
-        elif args.workload in ("prefill", "prefill-mxfp4"):
-            line["cpu_baseline"] = cpu_baseline_prefill(
-                fmt="nvfp4" if args.workload == "prefill" else "mxfp4")
+            "config": head.pop("config")}
+    line.update(head)
+    line["timing"] = (f"median of {SAMPLES} timed replays of a graph of {args.steps} steps "
+                      f"after {args.warmup} warmup steps; kernel averages from graphs of "
+                      f">= 50 back-to-back launches")
+    line["host"] = host_info()
+    if copy:
+        line["hbm_copy"] = copy
+    if wl == "all":
+        line["workloads"] = {k: v for k, v in records.items() if k != head_key}
+    line["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
     print(json.dumps(line), flush=True)
 
 

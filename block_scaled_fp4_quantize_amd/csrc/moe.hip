@@ -130,6 +130,20 @@ __device__ int block_exclusive_scan(int x, int* buf) {
 // (3) per chunk, slot i goes to base[chunk][e] + (number of earlier slots of the
 // chunk routed to e).  Positions follow i within every expert, as the stable
 // order requires.  Ids outside [0, E) are dropped (inverse -1).
+// Sorted positions past the routed count exist only when some ids were dropped.
+// Passes that walk every one of the T*k positions (the NVFP4 GEMM1 quantization, the
+// unfused SwiGLU) read their token and expert there, so those get token 0 / expert 0
+// (valid indices; the rows they produce are never gathered by the GEMMs or the
+// combine), and sorted_rows gets -1.
+__device__ __forceinline__ void fill_dropped_tail(const PermuteParams& p, int64_t routed,
+                                                  int64_t n, int tid, int nthreads) {
+  for (int64_t i = routed + tid; i < n; i += nthreads) {
+    p.sorted_rows[i] = -1;
+    p.row_expert[i] = 0;
+    p.src_token[i] = 0;
+  }
+}
+
 __global__ __launch_bounds__(kPermuteChunk) void permute_hist_kernel(PermuteParams p) {
   __shared__ int cnt[1024];
   const int tid = threadIdx.x;
@@ -174,6 +188,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_count_kernel(PermutePara
   __shared__ int partsum[kScanThreads];
   __shared__ int ebase[1024];
   __shared__ int total_mb;
+  __shared__ int total_rows;
   const int tid = threadIdx.x;
   const int64_t n = p.T * p.k;
   const int64_t nchunks = (n + kPermuteChunk - 1) / kPermuteChunk;
@@ -204,7 +219,10 @@ __global__ __launch_bounds__(kScanThreads) void permute_count_kernel(PermutePara
     for (int q = 0; q < part; ++q) base += partsum[q * E + e];
     chunk_walk(p.chunk_base, E, e, ch0, ch1, true, base);
   }
-  if (tid == E - 1) p.expert_offsets[E] = off + c;
+  if (tid == E - 1) {
+    p.expert_offsets[E] = off + c;
+    total_rows = off + c;
+  }
   const int nmb = (c + p.bm - 1) / p.bm;
   const int mbo = block_exclusive_scan(nmb, buf);
   if (tid == kScanThreads - 1) total_mb = mbo + nmb;
@@ -219,6 +237,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_count_kernel(PermutePara
     p.mblk_expert[i] = -1;
     p.mblk_row0[i] = 0;
   }
+  fill_dropped_tail(p, total_rows, n, tid, kScanThreads);
 }
 
 __global__ __launch_bounds__(kPermuteChunk) void permute_scatter_kernel(PermuteParams p) {
@@ -403,10 +422,13 @@ __global__ __launch_bounds__(kScanThreads) void permute_small_kernel(PermutePara
       q_exp[pos] = e;
     }
   }
+  // (ebase and cnt are final: the barriers inside the scans follow their last writes)
+  const int routed = ebase[E - 1] + cnt[E - 1];
+  fill_dropped_tail(p, routed, n, tid, kScanThreads);
   if (p.q_fmt < 0) return;  // uniform over the workgroup
   __syncthreads();
   // routed rows: the slots that hold a valid expert (the routed count)
-  const int64_t rows = p.q_routed ? (int64_t)(ebase[E - 1] + cnt[E - 1]) : p.q_rows;
+  const int64_t rows = p.q_routed ? (int64_t)routed : p.q_rows;
   const int G = p.q_fmt == kNV ? 16 : 32;
   const int64_t bpr = p.q_K / G;
   for (int64_t b = tid; b < rows * bpr; b += kScanThreads) {

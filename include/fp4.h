@@ -158,6 +158,9 @@ fp4_status fp4_moe_topk_softmax(const float* logits, int64_t T, int64_t E, int k
  * sync: any NVFP4 W4A4 a13/a2 scale that is zero, negative, non-finite or out of
  * range -> FP4_ERR_INPUT_SCALE (or the whole layer runs W4A16 with
  * FP4_FLAG_ALLOW_W4A16_FALLBACK).  Shared-expert pointers may all be NULL.
+ * Expert ids are device data and are not checked on the host: a slot whose id lies
+ * outside [0, E) (e.g. the router's output for a token with NaN logits) is dropped
+ * -- it contributes nothing to out[t] -- and every kernel stays inside its buffers.
  */
 typedef struct {
   fp4_format fmt;
@@ -183,7 +186,8 @@ typedef struct {
 typedef struct {
   size_t total_bytes;
   size_t expert_offsets;  /* int32 [E+1]: first sorted row of each expert */
-  size_t sorted_rows;     /* int32 [T*k]: flat index t*k+j of each sorted row */
+  size_t sorted_rows;     /* int32 [T*k]: flat index t*k+j of each sorted row; positions
+                             past the routed count (see dropped ids above) hold -1 */
   size_t inverse;         /* int32 [T*k]: sorted position of flat index t*k+j */
   size_t x_codes;         /* uint8 [rows, H/2] GEMM1 input codes (W4A4) */
   size_t x_scales;        /* uint8 [rows, H/G] */
@@ -208,11 +212,20 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
 /* Pure predicate: 1 if the architecture name (e.g. "gfx950:sramecc+:xnack-") is one
- * this library has kernels for, else 0.  No device access. */
+ * this library has kernels for, else 0.  No device access.  Every call above checks
+ * the current device with it and fails with FP4_ERR_DEVICE instead of launching:
+ * "vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A Complete Technical Guide", §2
+ * and §6.3 -- an FP4 kernel built for another architecture must fail loudly rather
+ * than run. */
 int fp4_arch_supported(const char* gcn_arch_name);
-/* Static string naming a status code. */
+/* Static string naming a status code (the error conventions above; the same guide's
+ * §6.3 and the GLM page's refused zero activation scale are the failures they name). */
 const char* fp4_status_str(fp4_status s);
-/* Name of the kernel variant the calling thread launched last ("" if none). */
+/* Name of the kernel variant the calling thread launched last ("" if none), so that a
+ * caller can see which kernel path ran ("vLLM on the DGX Spark, the Hard Way: Seven
+ * Months of GB10 Field Notes", the five-minute model, item 2: the kernel a format
+ * ends up on is chosen by a chain whose links fail silently, and the boot log's
+ * record of the chosen backend is how that shows). */
 const char* fp4_last_kernel(void);
 
 #ifdef __cplusplus

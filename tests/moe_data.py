@@ -29,18 +29,28 @@ class MoeProblem:
             w2 = synth.normal((H, I), 0.02, seed=seed, role=synth.W2, index=b)
             bases.append((OQ.quantize_weight(fmt, w13), OQ.quantize_weight(fmt, w2)))
         self.experts = []
+        # expert e = base e % n_base with its W13 rows permuted by perm13[e] and its W2
+        # rows by perm2[e] (identity for the bases themselves); the shared expert is
+        # base n_base, unpermuted
+        self.bases = bases
+        self.base_of, self.perm13, self.perm2 = [], [], []
         for e in range(E):
             (c13, s13, ws13), (c2, s2, ws2) = bases[e % n_base]
+            p13, p2 = np.arange(2 * I), np.arange(H)
             if e >= n_base:
                 p13 = synth.rows_permutation(2 * I, seed=seed, index=2 * e)
                 p2 = synth.rows_permutation(H, seed=seed, index=2 * e + 1)
                 c13, s13, c2, s2 = (_perm_rows(c13, p13), _perm_rows(s13, p13),
                                     _perm_rows(c2, p2), _perm_rows(s2, p2))
             self.experts.append(OM.Expert(c13, s13, c2, s2, ws13, ws2))
+            self.base_of.append(e % n_base)
+            self.perm13.append(p13)
+            self.perm2.append(p2)
         self.shared = None
         if shared:
             (c13, s13, ws13), (c2, s2, ws2) = bases[-1]
             self.shared = OM.Expert(c13, s13, c2, s2, ws13, ws2)
+        self._hat = {}
         x = synth.normal((T, H), seed=seed, role=synth.HIDDEN)
         self.hidden_bits, self.hidden = synth.bf16_bits(x)
         if zipf is None:
@@ -70,6 +80,25 @@ class MoeProblem:
             self.shared.a13_scale = float(np.float32(base13))
             h = OM.expert_h(self.fmt, self.mode, self.hidden[:n], self.shared)
             self.shared.a2_scale = float(np.float32(float(np.abs(h).max()) / 2688.0))
+
+    # -- dequantized weights, through the bases ------------------------------------
+    def base_hat(self, b):
+        """Exact dequantized (w13_hat [2I, H], w2_hat [H, I], |w2_hat|) of base b (the
+        shared expert is base n_base), computed once by the oracle's dequantizer."""
+        if b not in self._hat:
+            (c13, s13, _), (c2, s2, _) = self.bases[b]
+            w13 = OQ.dequantize_packed(self.fmt, c13, s13)
+            w2 = OQ.dequantize_packed(self.fmt, c2, s2)
+            self._hat[b] = (w13, w2, np.abs(w2))
+        return self._hat[b]
+
+    def expert_hat(self, e):
+        """(base index, perm13, perm2) of expert e, or of the shared expert for e ==
+        'shared': expert e's w13_hat is base_hat(b)[0][perm13] and its w2_hat is
+        base_hat(b)[1][perm2], so x @ w13_hat.T == (x @ base_w13_hat.T)[:, perm13]."""
+        if e == "shared":
+            return len(self.bases) - 1, slice(None), slice(None)
+        return self.base_of[e], self.perm13[e], self.perm2[e]
 
     # -- stacked arrays for the device --------------------------------------------
     def stacked(self):

@@ -73,7 +73,24 @@ SMALL = [(1, 16, 128), (5, 37, 256), (33, 50, 512), (17, 24, 384), (2, 8, 16), (
 def test_small_shapes(fmt, mode, shape):
     M, N, K = shape
     if K % OQ.GROUP[fmt]:
-        pytest.skip("K not a multiple of the block size")
+        # K not a multiple of the block size (MXFP4 K = 16, 48): refused on the host
+        # with FP4_ERR_SHAPE before any launch, the canary output left as it was
+        G = OQ.GROUP[fmt]
+        wcd = torch.zeros((N, K // 2), dtype=torch.uint8, device=DEV)
+        wsd = torch.full((N, (K + G - 1) // G), 127, dtype=torch.uint8, device=DEV)
+        ad, _ = bf16_dev(synth.normal((M, K), seed=1, role=synth.ACT))
+        out = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
+        ws = torch.empty(4096, dtype=torch.uint8, device=DEV)
+        st = F.fp4_gemm(fmt, mode, M, N, K, ad, K, None, None, wcd, wsd, 1.0, 1.0, out, N,
+                        F.FP4_OUT_BF16, 0, ws, 4096, check=False)
+        assert st == F.FP4_ERR_SHAPE, F.status_str(st)
+        ac = torch.zeros((M, K // 2), dtype=torch.uint8, device=DEV)
+        asc = torch.full((M, (K + G - 1) // G), 127, dtype=torch.uint8, device=DEV)
+        st = F.fp4_quantize_act(fmt, ad, M, K, K, 1.0, ac, asc, check=False)
+        assert st == F.FP4_ERR_SHAPE, F.status_str(st)
+        torch.cuda.synchronize()
+        assert (out == 7.0).all()
+        return
     run_and_check(fmt, mode, M, N, K, seed=sum(shape))
     run_and_check(fmt, mode, M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32)
 

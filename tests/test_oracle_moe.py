@@ -3,6 +3,8 @@
 Stages: "vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A Complete Technical Guide",
 §7.1 and §4.3.  Refusal rule: "GLM-5.3-Flash on vLLM, on GB10".
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -140,3 +142,141 @@ def test_token_subset_matches_full():
     full = Mo.moe(Q.MXFP4, Gm.W4A4, x, ids, w, exps)
     sub = Mo.moe(Q.MXFP4, Gm.W4A4, x, ids, w, exps, tokens=[7, 2])
     assert np.allclose(sub, full[[7, 2]], rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------------
+# W4A4 expert chain written out independently of oracle.quant / oracle.gemm: block
+# scales through torch's float8 casts and decoders, elements by a brute-force nearest
+# search over the literal e2m1 magnitudes, products with torch in float64.
+# ----------------------------------------------------------------------------------
+
+_E2M1_LIT = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _lit_e2m1(y, sign_src):
+    """e2m1 codes of float64 magnitudes |y|: nearest literal value, a tie to the even
+    code (both candidates of a tie are adjacent, one even and one odd); sign of sign_src."""
+    d = np.abs(np.abs(y)[..., None] - _E2M1_LIT)
+    cand = d == d.min(-1, keepdims=True)
+    even = cand & (np.arange(8) % 2 == 0)
+    code = np.where(even.any(-1), np.argmax(even, -1), np.argmax(cand, -1))
+    return (code | (np.signbit(sign_src).astype(np.int64) << 3)).astype(np.int64)
+
+
+def _lit_value(code):
+    return _E2M1_LIT[code & 7] * np.where(code & 8, -1.0, 1.0)
+
+
+def _lit_qdq_nvfp4(x, s):
+    """Dequantized NVFP4 values of fp32 rows x under the activation scale s:
+    g = 1/s, per 16-block sf = (amax g)/6 in fp32, scale = e4m3(sf) via torch's cast,
+    r = g/scale, element = nearest e2m1 of fp32(x r)."""
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    R, K = xt.shape
+    g = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(s, dtype=torch.float32)
+    xb = xt.view(R, K // 16, 16)
+    amax = xb.abs().amax(-1)
+    sf = (amax * g) / torch.tensor(6.0, dtype=torch.float32)
+    assert float(sf.max()) < 464.0             # torch's cast returns NaN from 464 on
+    sd = sf.to(torch.float8_e4m3fn).to(torch.float32)
+    r = torch.where(sd > 0, g / torch.where(sd > 0, sd, torch.ones_like(sd)), torch.zeros_like(sd))
+    y = (xb * r[..., None]).numpy().astype(np.float64)
+    code = _lit_e2m1(y, xb.numpy())
+    return (_lit_value(code) * sd.numpy().astype(np.float64)[..., None]).reshape(R, K)
+
+
+def _lit_qdq_mxfp4(x):
+    """Dequantized MXFP4 values: per 32-block E = floor(log2 amax) - 2 (from frexp),
+    element = nearest e2m1 of x 2^-E, value = element 2^E."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    R, K = x.shape
+    xb = x.reshape(R, K // 32, 32)
+    amax = np.abs(xb).max(-1)
+    _, ex = np.frexp(amax)                     # amax = m 2^ex, m in [0.5, 1)
+    E = np.where(amax > 0, np.clip(ex - 1 - 2, -127, 127), -127)
+    code = _lit_e2m1(xb * np.ldexp(1.0, -E)[..., None], xb)
+    return (_lit_value(code) * np.ldexp(1.0, E)[..., None]).reshape(R, K)
+
+
+def _chain_written_out(fmt, x, ex):
+    """One W4A4 expert: x_hat (under a13) -> gate/up * alpha13 -> SiLU(gate)*up in
+    float64 -> rounded to fp32 -> h_hat (under a2) -> down * alpha2."""
+    nv = fmt == Q.NVFP4
+    qdq = (lambda v, s: _lit_qdq_nvfp4(v, s)) if nv else (lambda v, s: _lit_qdq_mxfp4(v))
+    W13 = torch.from_numpy(_lit_dequant(fmt, ex.w13_codes, ex.w13_scales))
+    W2 = torch.from_numpy(_lit_dequant(fmt, ex.w2_codes, ex.w2_scales))
+    al13 = ex.w13_scale_2 * ex.a13_scale if nv else 1.0
+    al2 = ex.w2_scale_2 * ex.a2_scale if nv else 1.0
+    I = W2.shape[1]
+    gu = al13 * (torch.from_numpy(qdq(x, ex.a13_scale)) @ W13.T)
+    h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+    h32 = h.numpy().astype(np.float32)
+    return al2 * (torch.from_numpy(qdq(h32, ex.a2_scale)) @ W2.T).numpy()
+
+
+@pytest.mark.parametrize("fmt", [Q.NVFP4, Q.MXFP4])
+def test_w4a4_layer_written_out(fmt):
+    # three routed experts (top-2) and a shared one; NVFP4 experts each carry their
+    # own a13 != a2, at ratios that are not powers of two (a power-of-two change of
+    # an activation scale leaves the output unchanged, so it would pin nothing)
+    rng = np.random.default_rng(26)
+    T, H, I, E, k = 6, 64, 32, 3, 2
+    _, x = synth.bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    exps = [_expert(rng, fmt, H, I) for _ in range(E)]
+    shared = _expert(rng, fmt, H, I)
+    if fmt == Q.NVFP4:
+        base13 = float(np.abs(x).max()) / 2688.0
+        for e, ex in enumerate(exps + [shared]):
+            ex.a13_scale = float(np.float32(base13 * (1.0 + 0.3 * e)))
+            h = Mo.expert_h(fmt, Gm.W4A4, x, ex)
+            ex.a2_scale = float(np.float32(float(np.abs(h).max()) / 2688.0 * (1.7 + 0.2 * e)))
+            assert ex.a13_scale != ex.a2_scale
+    ids = np.array([[0, 1], [2, 0], [1, 2], [0, 2], [1, 0], [2, 1]], np.int32)
+    w = np.array([[0.7, 0.3], [0.6, 0.4], [0.55, 0.45], [0.8, 0.2], [0.5, 0.5], [0.9, 0.1]])
+    got = Mo.moe(fmt, Gm.W4A4, x, ids, w, exps, shared)
+    want = _chain_written_out(fmt, x, shared)                # the shared expert, weight 1
+    ys = [_chain_written_out(fmt, x, ex) for ex in exps]
+    for t in range(T):
+        for j in range(k):
+            want[t] += w[t, j] * ys[ids[t, j]][t]
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    # the routed experts matter and the shared expert enters with weight exactly 1
+    assert not np.allclose(got, _chain_written_out(fmt, x, shared), rtol=1e-3)
+    alone = Mo.moe(fmt, Gm.W4A4, x, ids, w, exps)
+    assert np.allclose(got - alone, _chain_written_out(fmt, x, shared),
+                       rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def _load_requant_golden(name):
+    d = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                key, v = line.split(":", 1)
+                d[key.strip()] = v.strip()
+    h = np.array([float(t) for t in d["h"].split()], dtype=np.float64)
+    codes = np.array([int(t, 16) for t in d["codes"].split()], dtype=np.uint8)
+    sc = np.array([int(t, 0) for t in d["scale_codes"].split()], dtype=np.uint8)
+    deq = np.array([float(t) for t in d["dequant"].split()])
+    return d["fmt"], float(d["a2_scale"]), h, codes, sc, deq
+
+
+@pytest.mark.parametrize("name", ["nvfp4_requant_h.txt", "mxfp4_requant_h.txt"])
+def test_golden_requant_through_down_projection(name):
+    # expert_down takes float64 h; through an identity W2 (e2m1 1.0 on the diagonal,
+    # block scale 1, weight_scale_2 1) its output is alpha2 x the requantized h, so
+    # the hand-worked block pins the fp32 rounding of h, the scale it is quantized
+    # under and alpha2
+    fmt, a2, h, codes, sc, deq = _load_requant_golden(name)
+    n = h.size
+    G = Q.GROUP[fmt]
+    diag = np.zeros((n, n), np.uint8)
+    np.fill_diagonal(diag, 2)                              # e2m1 code 2 = 1.0
+    one = 0x38 if fmt == Q.NVFP4 else 127                  # block scale 1.0
+    ex = Mo.Expert(None, None, F.pack_nibbles(diag), np.full((n, n // G), one, np.uint8),
+                   w2_scale_2=1.0, a2_scale=a2)
+    q, s = Q.quantize(fmt, h.astype(np.float32).reshape(1, -1), a2)
+    assert list(q[0]) == list(codes) and list(s[0]) == list(sc)
+    y = Mo.expert_down(fmt, Gm.W4A4, h.reshape(1, -1), ex)[0]
+    assert np.array_equal(y, a2 * deq)

@@ -118,10 +118,20 @@ def test_input_scale_refusal():
 
 
 def test_weight_quant_uses_full_e4m3_range():
+    # weight_scale_2 = fp32(amax / 2688), 2688 = 6 * 448, values worked by hand:
+    #   amax 1: 1/2688 = 2^-7 / 21 and 1/21 = 2^-5 * 1.100001100001...b, whose 24th
+    #           significant bit onward (1100001...) rounds the 23-bit field up to
+    #           10000110000110000110001b: 0x1.861862p-12
+    #   amax 3: 3/2688 = 2^-7 / 7 and 1/7 = 2^-3 * 1.001001001...b, rounded up
+    #           likewise to 00100100100100100100101b: 0x1.24924ap-10
+    for amax, want in ((1.0, "0x1.861862p-12"), (3.0, "0x1.24924ap-10")):
+        w = np.zeros((2, 32), np.float32)
+        w[1, 5] = -amax
+        w[0, 3] = amax / 4
+        assert float(Q.weight_scale_2(w)) == float.fromhex(want)
     rng = np.random.default_rng(7)
     w = (rng.standard_normal((64, 128)) * 0.02).astype(np.float32)
     codes, sc, ws2 = Q.quantize_weight(Q.NVFP4, w)
-    assert ws2 == np.float32(np.abs(w).max()) / np.float32(2688.0)
     assert sc.max() == 0x7E                     # the block holding the max uses scale 448
     wd = Q.dequantize_packed(Q.NVFP4, codes, sc) * ws2
     assert np.abs(wd).max() == pytest.approx(np.abs(w).max(), rel=1 / 8)
