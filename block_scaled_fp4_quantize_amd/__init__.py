@@ -37,6 +37,7 @@ GROUP = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
 EXPORTED = [
     "fp4_quantize_act", "fp4_quantize_weight", "fp4_gemm", "fp4_gemm_workspace_size",
+    "fp4_gemm_noalloc",
     "fp4_moe_topk_softmax", "fp4_moe_workspace_size", "fp4_moe_workspace_layout",
     "fp4_moe_grouped_gemm", "fp4_arch_supported", "fp4_status_str", "fp4_last_kernel",
 ]
@@ -111,6 +112,9 @@ _c = {
     "fp4_quantize_weight": _proto("fp4_quantize_weight", _int, [_int, _vp, _i64, _i64, _i64, _f32, _vp, _vp, _vp]),
     "fp4_gemm": _proto("fp4_gemm", _int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                           _f32, _f32, _vp, _i64, _int, _u32, _vp, _sz, _vp]),
+    "fp4_gemm_noalloc": _proto("fp4_gemm_noalloc", _int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp,
+                                                          _vp, _vp, _vp, _f32, _f32, _vp, _i64, _int,
+                                                          _u32, _vp]),
     "fp4_gemm_workspace_size": _proto("fp4_gemm_workspace_size", _sz, [_int, _int, _i64, _i64, _int]),
     "fp4_moe_topk_softmax": _proto("fp4_moe_topk_softmax", _int, [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "fp4_moe_workspace_size": _proto("fp4_moe_workspace_size", _sz, [ctypes.POINTER(MoeArgs)]),
@@ -194,6 +198,16 @@ def fp4_gemm(fmt, mode, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scal
                         input_scale, _ptr(out), ldo, out_dtype, flags, _ptr(workspace),
                         workspace_bytes, _stream(stream, out, w_codes))
     return _check(st, "fp4_gemm", check)
+
+
+def fp4_gemm_noalloc(fmt, mode, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scales,
+                     weight_scale_2, input_scale, out, ldo, out_dtype=FP4_OUT_BF16, flags=0,
+                     stream=None, check=True):
+    st = _c["fp4_gemm_noalloc"](_fmt(fmt), _mode(mode), M, N, K, _ptr(a_bf16), lda, _ptr(a_codes),
+                                _ptr(a_scales), _ptr(w_codes), _ptr(w_scales), weight_scale_2,
+                                input_scale, _ptr(out), ldo, out_dtype, flags,
+                                _stream(stream, out, w_codes))
+    return _check(st, "fp4_gemm_noalloc", check)
 
 
 def fp4_moe_topk_softmax(logits, T, E, k, renormalize, topk_ids, topk_w, stream=None, check=True):

@@ -15,6 +15,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "fp4.h"
@@ -279,12 +280,54 @@ size_t fp4_gemm_workspace_size(fp4_format fmt, fp4_mode mode, int64_t M, int64_t
   return gemm_ws_bytes(fmt, M, K);
 }
 
-fp4_status fp4_gemm(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t K,
-                    const void* a_bf16, int64_t lda, const uint8_t* a_codes,
-                    const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
-                    float weight_scale_2, float input_scale, void* out, int64_t ldo,
-                    fp4_out out_dtype, uint32_t flags, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- the allocation-free variant's scratch ------------------------------------------
+// One array per device (each device's code object holds its own copy), holding the
+// fused W4A4 GEMM's quantized activations.  Host code never uses the symbol itself:
+// its host-side name is a stand-in, not a device address.  The device address is
+// resolved once per device, with that device current, and kept here.
+static __device__ __align__(256) uint8_t scratch[FP4_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// Device address of the current device's scratch array (FP4_ERR_DEVICE if it cannot
+// be resolved).
+fp4_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return FP4_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return FP4_ERR_DEVICE;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP4_OK;
+}
+
+// fp4_gemm and fp4_gemm_noalloc: with use_scratch the fused quantization writes into
+// the device's scratch array (workspace / workspace_bytes are ignored, the capacity is
+// FP4_NOALLOC_SCRATCH_BYTES) instead of a caller workspace.
+fp4_status gemm_call(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t K,
+                     const void* a_bf16, int64_t lda, const uint8_t* a_codes,
+                     const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                     float weight_scale_2, float input_scale, void* out, int64_t ldo,
+                     fp4_out out_dtype, uint32_t flags, void* workspace,
+                     size_t workspace_bytes, void* stream, bool use_scratch) {
+  if (use_scratch) {
+    workspace = nullptr;
+    workspace_bytes = FP4_NOALLOC_SCRATCH_BYTES;
+  }
   if (!fmt_ok(fmt) || !mode_ok(mode) || (out_dtype != FP4_OUT_BF16 && out_dtype != FP4_OUT_F32) ||
       (flags & ~FP4_FLAG_ALLOW_W4A16_FALLBACK))
     return FP4_ERR_FORMAT;
@@ -316,11 +359,16 @@ fp4_status fp4_gemm(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t
   }
   const bool fused = w4a4 && a_bf16;
   if (fused) {
-    if (!workspace || workspace_bytes < gemm_ws_bytes(fmt, M, K)) return FP4_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return FP4_ERR_ALIGN;
+    if ((!use_scratch && !workspace) || workspace_bytes < gemm_ws_bytes(fmt, M, K))
+      return FP4_ERR_WORKSPACE;
+    if (!use_scratch && !aligned16(workspace)) return FP4_ERR_ALIGN;
   }
   fp4_status st = device_check();
   if (st != FP4_OK) return st;
+  if (fused && use_scratch) {
+    st = scratch_for_current_device(&workspace);
+    if (st != FP4_OK) return st;
+  }
 
   hipStream_t s = (hipStream_t)stream;
   const char* name = "";
@@ -359,6 +407,32 @@ fp4_status fp4_gemm(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t
   hipError_t e = fp4::launch_gemm(fmt, w4a4 ? fp4::kA_FP4 : fp4::kA_BF16, p, s, &name);
   st = launched(e, name);
   return st == FP4_OK ? ok_status : st;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4_status fp4_gemm(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t K,
+                    const void* a_bf16, int64_t lda, const uint8_t* a_codes,
+                    const uint8_t* a_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                    float weight_scale_2, float input_scale, void* out, int64_t ldo,
+                    fp4_out out_dtype, uint32_t flags, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return gemm_call(fmt, mode, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scales,
+                   weight_scale_2, input_scale, out, ldo, out_dtype, flags, workspace,
+                   workspace_bytes, stream, false);
+}
+
+fp4_status fp4_gemm_noalloc(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t K,
+                            const void* a_bf16, int64_t lda, const uint8_t* a_codes,
+                            const uint8_t* a_scales, const uint8_t* w_codes,
+                            const uint8_t* w_scales, float weight_scale_2, float input_scale,
+                            void* out, int64_t ldo, fp4_out out_dtype, uint32_t flags,
+                            void* stream) {
+  return gemm_call(fmt, mode, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scales,
+                   weight_scale_2, input_scale, out, ldo, out_dtype, flags, nullptr, 0, stream,
+                   true);
 }
 
 fp4_status fp4_moe_topk_softmax(const float* logits, int64_t T, int64_t E, int k,

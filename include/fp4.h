@@ -135,6 +135,33 @@ fp4_status fp4_gemm(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t
 size_t fp4_gemm_workspace_size(fp4_format fmt, fp4_mode mode, int64_t M, int64_t K,
                                int has_a_bf16);
 
+/* Capacity of fp4_gemm_noalloc's per-device scratch array (32 MiB). */
+#define FP4_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * fp4_gemm without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, semantics and results as fp4_gemm (the same kernels);
+ * the fused W4A4 activation quantization writes into a scratch array the library
+ * holds in each device's memory (FP4_NOALLOC_SCRATCH_BYTES, resident until the
+ * process ends).  Nothing is allocated or freed by the call.
+ *   Limit: the fused case needs fp4_gemm_workspace_size(...) <= the capacity, i.e.
+ *   M*K/2 + M*K/G bytes (each part rounded up to 256) -- about 59 M activation
+ *   elements for NVFP4 (M = 8192 at K = 7168); larger calls return FP4_ERR_WORKSPACE
+ *   before any launch.  Pre-quantized W4A4 and W4A16 calls use no scratch.
+ *   Races: every call on one device shares that device's array, so calls that can
+ *   overlap on one device (different streams, or threads without ordering) race on
+ *   it; calls ordered on one stream do not.  The array keeps the last call's contents.
+ *   The first call on a device resolves the array's device address (outside stream
+ *   capture: make one call before capturing).
+ */
+fp4_status fp4_gemm_noalloc(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t K,
+                            const void* a_bf16, int64_t lda, const uint8_t* a_codes,
+                            const uint8_t* a_scales, const uint8_t* w_codes,
+                            const uint8_t* w_scales, float weight_scale_2, float input_scale,
+                            void* out, int64_t ldo, fp4_out out_dtype, uint32_t flags,
+                            void* stream);
+
 /*
  * Router (guide §7.1 [Router]; top-k softmax).  logits fp32 [T, E] (device);
  * topk_ids int32 [T, k]: the k largest logits, largest first, ties to the lower

@@ -238,3 +238,18 @@ def test_row_block_capacity_bound_exhaustive():
                 cap = -(-P // bm) + min(E, P)
                 worst = max(sum(-(-c // bm) for c in split) for split in partitions(P, E, P))
                 assert worst <= cap, (bm, E, P, worst, cap)
+
+
+def test_noalloc_gemm_validation():
+    # the allocation-free variant validates like fp4_gemm, and refuses a fused call
+    # larger than its 32 MiB scratch array before touching a device
+    NV, W44 = F.FP4_NVFP4, F.FP4_W4A4
+
+    def gn(M=8192, K=8192, **kw):
+        return F.fp4_gemm_noalloc(NV, W44, M, 64, K, kw.get("a", A), K, None, None, B, C,
+                                  1.0, kw.get("s", 1.0), D, 64, check=False)
+    assert gn() == F.FP4_ERR_WORKSPACE                    # 37.7 MB > 32 MiB
+    assert gn(s=0.0) == F.FP4_ERR_INPUT_SCALE
+    assert gn(a=A + 8) == F.FP4_ERR_ALIGN
+    if NO_GPU:
+        assert gn(M=8192, K=4096) == F.FP4_ERR_DEVICE    # fits: stops at the device check
