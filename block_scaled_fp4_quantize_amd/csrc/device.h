@@ -157,6 +157,9 @@ __device__ __forceinline__ bf16x8 decode8_bf16(uint32_t packed, float scale) {
 __device__ __forceinline__ uint32_t dword_of(const uint4& q, int j) {
   return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
 }
+__device__ __forceinline__ uint32_t dword_of_v(const u32x4& q, int j) {
+  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+}
 
 // An e4m3 block-scale value as a packed fp16 pair (exact: e4m3 values are fp16 numbers).
 __device__ __forceinline__ f16x2 f16_pair(float v) {

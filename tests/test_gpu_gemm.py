@@ -185,10 +185,10 @@ def test_raw_codes(fmt, shape):
 
 
 # dense problems with at least 256 tiles of 256 x 256: the 8-wave 256-row tile, with K of
-# one and three stages (fewer than the copy pipeline holds) and of eight, ragged rows
-# and columns; the oracle checks the first and last 300 rows and 200 sampled ones
-# K of 1, 3, 5, 8 and 17 stages of 128: the 256-row tile copies the block scales of 4
-# stages at a time, so these cover a group cut short at 1, 3 and 1 stages and whole ones
+# 1, 3, 5, 8 and 17 stages of 128 (the 256-row tile copies the block scales of 4 stages
+# at a time, so these cover a group cut short at 1, 3 and 1 stages, and whole ones),
+# ragged rows and columns; the oracle checks the first and last 300 rows and 200
+# sampled ones
 TILED_256 = [(2300, 7324, 128), (2049, 7324, 384), (4096, 4096, 1024), (4096, 4096, 640),
              (4352, 4096, 2176)]
 
