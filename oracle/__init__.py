@@ -25,6 +25,10 @@ Modules
   quant    NVFP4 / MXFP4 quantize and dequantize (activation and weight)
   gemm     dequantize + float64 matmul, W4A4 and W4A16
   moe      top-k softmax routing, permute bookkeeping, the expert chain, combine
+  fp8      MXFP8 (e4m3 elements, e8m0 scale per 32) and FP8 W8A8 with per-tensor,
+           rowwise (per token / per channel) or 1x128 / 128x128 block scales
+           ("vLLM per-format kernel capability matrix derived from source": the MX
+           group size, MXFP8 native on gfx95, FP8's three scaling modes)
 
 Pins (tests/test_oracle_*.py) tie every function to something outside itself:
 closed-form value tables, torch's float8 decoders, hand-worked examples in
