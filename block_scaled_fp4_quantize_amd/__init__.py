@@ -1,6 +1,8 @@
-"""Python binding of libfp4, the gfx950 block-scaled FP4 (NVFP4 / MXFP4) library.
+"""Python binding of libfp4, the gfx950 block-scaled FP4 (NVFP4 / MXFP4) library and its
+8-bit members (MXFP8, FP8 W8A8).
 
-The functions carry the C names of include/fp4.h and only marshal arguments:
+The functions carry the C names of include/fp4.h and include/fp8.h and only marshal
+arguments:
 torch tensors (or raw integer device addresses) become pointers, the current
 torch stream becomes the hipStream_t, and negative status codes raise
 ``Fp4Error``.  Every computation runs in the HIP kernels of libfp4.so; there is
@@ -31,7 +33,11 @@ FP4_ERR_WORKSPACE = -7
 FP4_ERR_DEVICE = -8
 FP4_ERR_LAUNCH = -9
 
+FP8_MX, FP8_PER_TENSOR, FP8_ROWWISE, FP8_BLOCK = 0, 1, 2, 3
+
 FORMATS = {"nvfp4": FP4_NVFP4, "mxfp4": FP4_MXFP4}
+FP8_MODES = {"mx": FP8_MX, "per_tensor": FP8_PER_TENSOR, "rowwise": FP8_ROWWISE,
+             "block": FP8_BLOCK}
 MODES = {"w4a4": FP4_W4A4, "w4a16": FP4_W4A16}
 GROUP = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
@@ -40,6 +46,7 @@ EXPORTED = [
     "fp4_gemm_noalloc",
     "fp4_moe_topk_softmax", "fp4_moe_workspace_size", "fp4_moe_workspace_layout",
     "fp4_moe_grouped_gemm", "fp4_arch_supported", "fp4_status_str", "fp4_last_kernel",
+    "fp8_quantize_act", "fp8_quantize_weight", "fp8_gemm",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -124,6 +131,11 @@ _c = {
     "fp4_arch_supported": _proto("fp4_arch_supported", _int, [ctypes.c_char_p]),
     "fp4_status_str": _proto("fp4_status_str", ctypes.c_char_p, [_int]),
     "fp4_last_kernel": _proto("fp4_last_kernel", ctypes.c_char_p, []),
+    "fp8_quantize_act": _proto("fp8_quantize_act", _int, [_int, _vp, _i64, _i64, _i64, _f32, _vp, _vp, _vp]),
+    "fp8_quantize_weight": _proto("fp8_quantize_weight", _int, [_int, _vp, _i64, _i64, _i64, _f32, _vp, _vp,
+                                                                _vp]),
+    "fp8_gemm": _proto("fp8_gemm", _int, [_int, _i64, _i64, _i64, _vp, _vp, _f32, _vp, _vp, _f32, _vp,
+                                          _i64, _int, _vp]),
 }
 
 
@@ -157,6 +169,10 @@ def _fmt(f):
 
 def _mode(m):
     return MODES.get(m, m) if isinstance(m, str) else int(m)
+
+
+def _f8mode(m):
+    return FP8_MODES.get(m, m) if isinstance(m, str) else int(m)
 
 
 def _check(st, where, raise_on_error):
@@ -281,3 +297,23 @@ def fp4_status_str(st):
 
 def fp4_last_kernel():
     return _c["fp4_last_kernel"]().decode()
+
+
+def fp8_quantize_act(mode, x, M, K, ldx, tensor_scale, codes, scales, stream=None, check=True):
+    st = _c["fp8_quantize_act"](_f8mode(mode), _ptr(x), M, K, ldx, tensor_scale, _ptr(codes),
+                                _ptr(scales), _stream(stream, x, codes))
+    return _check(st, "fp8_quantize_act", check)
+
+
+def fp8_quantize_weight(mode, w, N, K, ldw, tensor_scale, codes, scales, stream=None, check=True):
+    st = _c["fp8_quantize_weight"](_f8mode(mode), _ptr(w), N, K, ldw, tensor_scale, _ptr(codes),
+                                   _ptr(scales), _stream(stream, w, codes))
+    return _check(st, "fp8_quantize_weight", check)
+
+
+def fp8_gemm(mode, M, N, K, a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale,
+             out, ldo, out_dtype=FP4_OUT_BF16, stream=None, check=True):
+    st = _c["fp8_gemm"](_f8mode(mode), M, N, K, _ptr(a_codes), _ptr(a_scales), a_tensor_scale,
+                        _ptr(w_codes), _ptr(w_scales), w_tensor_scale, _ptr(out), ldo, out_dtype,
+                        _stream(stream, out, w_codes))
+    return _check(st, "fp8_gemm", check)

@@ -19,6 +19,7 @@
 #include <vector>
 
 #include "fp4.h"
+#include "fp8.h"
 #include "internal.h"
 
 namespace {
@@ -780,6 +781,122 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
 #undef FP4_TRY
   t_last_kernel = "moe";
   return ok_status;
+}
+
+}  // extern "C"
+
+// ---- FP8 family (MXFP8, FP8 W8A8) ---------------------------------------------------
+namespace {
+
+static_assert(FP8_MX == fp4::kF8_MX && FP8_PER_TENSOR == fp4::kF8_TENSOR &&
+                  FP8_ROWWISE == fp4::kF8_ROW && FP8_BLOCK == fp4::kF8_BLOCK,
+              "fp8_scaling codes are the kernels' mode numbers");
+
+bool f8mode_ok(int m) { return m == FP8_MX || m == FP8_PER_TENSOR || m == FP8_ROWWISE || m == FP8_BLOCK; }
+int64_t f8_kmult(int m) { return m == FP8_MX ? 32 : (m == FP8_BLOCK ? 128 : 8); }
+
+fp4_status fp8_quantize_common(int mode, const void* x, bool weight, int64_t M, int64_t K,
+                               int64_t ldx, float ts, uint8_t* codes, void* scales,
+                               void* stream, fp4_status bad_scale) {
+  if (!f8mode_ok(mode)) return FP4_ERR_FORMAT;
+  if (M < 0 || K < 0 || K % f8_kmult(mode)) return FP4_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP4_OK;
+  if (ldx < K) return FP4_ERR_SHAPE;
+  const bool tensor = mode == FP8_PER_TENSOR;
+  if (!x || !codes || (!tensor && !scales)) return FP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || (scales && !aligned16(scales)) ||
+      ldx % (weight ? 4 : 8))
+    return FP4_ERR_ALIGN;
+  if (tensor) {
+    if (!scale_ok(ts)) return bad_scale;
+    if (scales) return FP4_ERR_FORMAT;
+  } else if (ts != 1.0f) {
+    return FP4_ERR_FORMAT;
+  }
+  fp4_status st = device_check();
+  if (st != FP4_OK) return st;
+  fp4::Fp8QuantParams p{};
+  p.x = x;
+  p.in_f32 = weight ? 1 : 0;
+  p.M = M;
+  p.K = K;
+  p.ldx = ldx;
+  p.weight_blocks = weight && mode == FP8_BLOCK;
+  p.tensor_scale = ts;
+  p.codes = codes;
+  p.mx_scales = mode == FP8_MX ? static_cast<uint8_t*>(scales) : nullptr;
+  p.f_scales = (mode == FP8_ROWWISE || mode == FP8_BLOCK) ? static_cast<float*>(scales) : nullptr;
+  const char* name = "";
+  hipError_t e = fp4::launch_fp8_quant(mode, p, (hipStream_t)stream, &name);
+  return launched(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4_status fp8_quantize_act(fp8_scaling mode, const void* x_bf16, int64_t M, int64_t K,
+                            int64_t ldx, float tensor_scale, uint8_t* codes, void* scales,
+                            void* stream) {
+  return fp8_quantize_common(mode, x_bf16, false, M, K, ldx, tensor_scale, codes, scales,
+                             stream, FP4_ERR_INPUT_SCALE);
+}
+
+fp4_status fp8_quantize_weight(fp8_scaling mode, const float* w, int64_t N, int64_t K,
+                               int64_t ldw, float tensor_scale, uint8_t* codes, void* scales,
+                               void* stream) {
+  return fp8_quantize_common(mode, w, true, N, K, ldw, tensor_scale, codes, scales, stream,
+                             FP4_ERR_WEIGHT_SCALE);
+}
+
+fp4_status fp8_gemm(fp8_scaling mode, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                    const void* a_scales, float a_tensor_scale, const uint8_t* w_codes,
+                    const void* w_scales, float w_tensor_scale, void* out, int64_t ldo,
+                    fp4_out out_dtype, void* stream) {
+  if (!f8mode_ok(mode) || (out_dtype != FP4_OUT_BF16 && out_dtype != FP4_OUT_F32))
+    return FP4_ERR_FORMAT;
+  if (M < 0 || N < 0 || K <= 0 || K % 128) return FP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP4_OK;
+  if (ldo < N) return FP4_ERR_SHAPE;
+  const bool tensor = mode == FP8_PER_TENSOR;
+  if (!a_codes || !w_codes || !out || (!tensor && (!a_scales || !w_scales))) return FP4_ERR_NULL;
+  const void* ptrs[] = {a_codes, a_scales, w_codes, w_scales, out};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return FP4_ERR_ALIGN;
+  float alpha = 1.0f;
+  if (tensor) {
+    if (!scale_ok(a_tensor_scale)) return FP4_ERR_INPUT_SCALE;
+    if (!scale_ok(w_tensor_scale)) return FP4_ERR_WEIGHT_SCALE;
+    alpha = a_tensor_scale * w_tensor_scale;
+    // the product is applied once per output: it must be a finite normal fp32
+    if (!std::isfinite(alpha) || alpha < 0x1p-126f) return FP4_ERR_INPUT_SCALE;
+    if (a_scales || w_scales) return FP4_ERR_FORMAT;
+  } else if (a_tensor_scale != 1.0f || w_tensor_scale != 1.0f) {
+    return FP4_ERR_FORMAT;
+  }
+  fp4_status st = device_check();
+  if (st != FP4_OK) return st;
+  fp4::Fp8GemmParams p{};
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.a_codes = a_codes;
+  p.w_codes = w_codes;
+  if (mode == FP8_MX) {
+    p.a_mx = static_cast<const uint8_t*>(a_scales);
+    p.w_mx = static_cast<const uint8_t*>(w_scales);
+  } else if (!tensor) {
+    p.a_s = static_cast<const float*>(a_scales);
+    p.w_s = static_cast<const float*>(w_scales);
+  }
+  p.alpha = alpha;
+  p.unit_scale = 127;   // e8m0 code of 1.0: the MFMA's block scale for non-MX modes
+  p.out = out;
+  p.ldo = ldo;
+  p.out_f32 = out_dtype == FP4_OUT_F32;
+  const char* name = "";
+  hipError_t e = fp4::launch_fp8_gemm(mode, p, (hipStream_t)stream, &name);
+  return launched(e, name);
 }
 
 }  // extern "C"

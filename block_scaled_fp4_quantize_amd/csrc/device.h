@@ -174,6 +174,29 @@ __device__ __forceinline__ bf16x8 bits_to_bf16x8(uint4 v) {
 }
 
 
+// 8 consecutive elements (bf16 bits or fp32) as fp32, one or two 16-byte loads
+template <typename Tin>
+__device__ __forceinline__ void load8(const Tin* p, float v[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float v[8]) {
+  uint4 q = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 // SwiGLU of one gate/up pair: SiLU(z) * u with SiLU(z) = z / (1 + e^-z), in fp32.
 __device__ __forceinline__ float swiglu1(float z, float u) {
   const float silu = z / (1.0f + expf(-z));

@@ -97,6 +97,37 @@ hipError_t launch_gemm_resident(int fmt, int mt, const GemmParams& p, hipStream_
 // activation blocks)
 hipError_t launch_gemm_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name);
 
+// ---- MXFP8 and FP8 W8A8 (e4m3 operands) ---------------------------------------------
+// scaling modes, in the order of the C ABI's fp8_scaling
+enum Fp8Mode : int { kF8_MX = 0, kF8_TENSOR = 1, kF8_ROW = 2, kF8_BLOCK = 3 };
+struct Fp8QuantParams {
+  const void* x;            // bf16 bits or fp32 [M, ldx]
+  int in_f32;
+  int64_t M, K, ldx;
+  int weight_blocks;        // BLOCK: 128 x 128 blocks (weights) instead of 1 x 128
+  float tensor_scale;       // TENSOR: the divisor
+  uint8_t* codes;           // e4m3 [M, K]
+  uint8_t* mx_scales;       // MX: e8m0 [M, K/32]
+  float* f_scales;          // ROW: [M]; BLOCK: [M, K/128] or [ceil(M/128), K/128]
+};
+hipError_t launch_fp8_quant(int mode, const Fp8QuantParams& p, hipStream_t s, const char** name);
+struct Fp8GemmParams {
+  int64_t M, N, K;
+  const uint8_t* a_codes;   // [M, K]
+  const uint8_t* w_codes;   // [N, K]
+  const uint8_t* a_mx;      // MX: e8m0 [M, K/32]
+  const uint8_t* w_mx;      // MX: e8m0 [N, K/32]
+  const float* a_s;         // ROW: [M]; BLOCK: [M, K/128]
+  const float* w_s;         // ROW: [N]; BLOCK: [ceil(N/128), K/128]
+  float alpha;              // TENSOR: a_scale * w_scale; MX and BLOCK: 1
+  int unit_scale;           // the e8m0 code of 1.0 (127), passed at run time
+  void* out;
+  int64_t ldo;
+  int out_f32;
+};
+// K % 128 == 0
+hipError_t launch_fp8_gemm(int mode, const Fp8GemmParams& p, hipStream_t s, const char** name);
+
 // ---- MoE stages ------------------------------------------------------------------
 hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,
                                int renormalize, int32_t* ids, float* w, hipStream_t s,

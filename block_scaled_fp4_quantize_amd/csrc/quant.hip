@@ -18,28 +18,6 @@
 
 namespace fp4 {
 
-template <typename Tin>
-__device__ __forceinline__ void load8(const Tin* p, float v[8]);
-
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float v[8]) {
-  uint4 q = *reinterpret_cast<const uint4*>(p);
-  uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-  }
-}
-
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
-  float4 a = reinterpret_cast<const float4*>(p)[0];
-  float4 b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
 // One lane = 8 consecutive elements of one row.  FMT kNV: 2 lanes per 16-block;
 // kMX: 4 lanes per 32-block.  Blocks never straddle rows (K % G == 0).
 template <int FMT, typename Tin>

@@ -2,10 +2,12 @@
 device and call the library.  Plumbing only; no arithmetic happens here."""
 import torch
 
-from . import (FP4_MXFP4, FP4_NVFP4, FP4_OUT_BF16, FP4_OUT_F32, FP4_W4A4, FP4_W4A16, GROUP,
-               _fmt, _mode, fp4_gemm, fp4_gemm_workspace_size, fp4_moe_grouped_gemm,
-               fp4_moe_topk_softmax, fp4_moe_workspace_layout, fp4_moe_workspace_size,
-               fp4_quantize_act, fp4_quantize_weight, make_moe_args)
+from . import (FP4_MXFP4, FP4_NVFP4, FP4_OUT_BF16, FP4_OUT_F32, FP4_W4A4, FP4_W4A16,
+               FP8_BLOCK, FP8_MX, FP8_ROWWISE, GROUP, _f8mode, _fmt, _mode,
+               fp4_gemm, fp4_gemm_workspace_size, fp4_moe_grouped_gemm, fp4_moe_topk_softmax,
+               fp4_moe_workspace_layout, fp4_moe_workspace_size, fp4_quantize_act,
+               fp4_quantize_weight, fp8_gemm, fp8_quantize_act, fp8_quantize_weight,
+               make_moe_args)
 
 
 def _alloc_u8(rows, cols, device):
@@ -52,6 +54,52 @@ def gemm(fmt, mode, w_codes, w_scales, a_bf16=None, a_codes=None, a_scales=None,
                   float(weight_scale_2), float(input_scale), out, out.stride(0), od, flags,
                   workspace, wsz if workspace is not None else 0)
     return out, st
+
+
+def _fp8_scales(mode, rows, K, device, weight):
+    """Scale tensor of an FP8 operand (None for per-tensor scaling)."""
+    if mode == FP8_MX:
+        return torch.empty((rows, K // 32), dtype=torch.uint8, device=device)
+    if mode == FP8_ROWWISE:
+        return torch.empty((rows,), dtype=torch.float32, device=device)
+    if mode == FP8_BLOCK:
+        r = (rows + 127) // 128 if weight else rows
+        return torch.empty((r, K // 128), dtype=torch.float32, device=device)
+    return None
+
+
+def fp8_quantize_act_t(mode, x, tensor_scale=1.0):
+    """x: bf16 [M, K] -> (codes uint8 [M, K], scales by mode or None)."""
+    m = _f8mode(mode)
+    M, K = x.shape
+    codes = _alloc_u8(M, K, x.device)
+    scales = _fp8_scales(m, M, K, x.device, False)
+    fp8_quantize_act(m, x, M, K, x.stride(0), float(tensor_scale), codes, scales)
+    return codes, scales
+
+
+def fp8_quantize_weight_t(mode, w, tensor_scale=1.0):
+    """w: fp32 [N, K] -> (codes uint8 [N, K], scales by mode or None)."""
+    m = _f8mode(mode)
+    N, K = w.shape
+    codes = _alloc_u8(N, K, w.device)
+    scales = _fp8_scales(m, N, K, w.device, True)
+    fp8_quantize_weight(m, w, N, K, w.stride(0), float(tensor_scale), codes, scales)
+    return codes, scales
+
+
+def fp8_gemm_t(mode, a_codes, a_scales, w_codes, w_scales, a_tensor_scale=1.0,
+               w_tensor_scale=1.0, out_dtype=torch.bfloat16, out=None):
+    """out [M, N] = a_hat @ w_hat^T for FP8 operands of one scaling mode."""
+    m = _f8mode(mode)
+    M, K = a_codes.shape
+    N = w_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=w_codes.device)
+    od = FP4_OUT_F32 if out.dtype == torch.float32 else FP4_OUT_BF16
+    fp8_gemm(m, M, N, K, a_codes, a_scales, float(a_tensor_scale), w_codes, w_scales,
+             float(w_tensor_scale), out, out.stride(0), od)
+    return out
 
 
 def topk_softmax(logits, k, renormalize=True):

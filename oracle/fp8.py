@@ -101,8 +101,10 @@ def _quantize_by(x, s):
     x = np.asarray(x, dtype=np.float32)
     s = np.asarray(s, dtype=np.float32)
     zero = s == 0
-    with np.errstate(divide="ignore", invalid="ignore"):
-        y = (x / np.where(zero, np.float32(1.0), s)).astype(np.float32)   # one fp32 division
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        # one fp32 division; a quotient beyond fp32 becomes inf and saturates like any
+        # value above 448
+        y = (x / np.where(zero, np.float32(1.0), s)).astype(np.float32)
     y = np.where(zero, np.copysign(np.float32(0.0), x), y)
     return e4m3_encode(y.astype(np.float32))
 

@@ -1,5 +1,5 @@
 """The C-ABI boundary, on the CPU: the library loads, exports every function that
-include/fp4.h declares, and refuses bad arguments before touching a device.
+include/*.h declares, and refuses bad arguments before touching a device.
 
 No call here reaches a kernel: each either fails host-side validation (fake but
 aligned addresses are never dereferenced) or stops at the device check, which on a
@@ -17,7 +17,7 @@ import pytest
 
 import block_scaled_fp4_quantize_amd as F
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fp4.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 A = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
 B = 0x20000
 C = 0x30000
@@ -36,14 +36,17 @@ NO_GPU = not _has_gpu()
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp4_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(fp[48]_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) >= 11
+    assert len(names) >= 15 and "fp8_gemm" in names
     lib = ctypes.CDLL(F.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -253,3 +256,65 @@ def test_noalloc_gemm_validation():
     assert gn(a=A + 8) == F.FP4_ERR_ALIGN
     if NO_GPU:
         assert gn(M=8192, K=4096) == F.FP4_ERR_DEVICE    # fits: stops at the device check
+
+
+# ---- FP8 family ("vLLM per-format kernel capability matrix derived from source": MXFP8,
+# FP8 THREE SCALING MODES) ---------------------------------------------------------------
+
+
+def q8(mode, x=A, M=4, K=128, ldx=128, s=1.0, codes=B, scales=C, weight=False):
+    f = F.fp8_quantize_weight if weight else F.fp8_quantize_act
+    return f(mode, x, M, K, ldx, s, codes, scales, check=False)
+
+
+def g8(mode, M=4, N=8, K=128, ac=A, asc=B, ats=1.0, wc=C, wsc=D, wts=1.0, out=0x50000, ldo=8,
+       od=0):
+    return F.fp8_gemm(mode, M, N, K, ac, asc, ats, wc, wsc, wts, out, ldo, od, check=False)
+
+
+def test_fp8_quantize_validation():
+    assert q8(9) == F.FP4_ERR_FORMAT
+    assert q8(F.FP8_MX, K=48, ldx=48) == F.FP4_ERR_SHAPE                   # K % 32
+    assert q8(F.FP8_BLOCK, K=96, ldx=96) == F.FP4_ERR_SHAPE                # K % 128
+    assert q8(F.FP8_ROWWISE, K=12, ldx=16) == F.FP4_ERR_SHAPE              # K % 8
+    assert q8(F.FP8_ROWWISE, M=-1) == F.FP4_ERR_SHAPE
+    assert q8(F.FP8_MX, ldx=64) == F.FP4_ERR_SHAPE                         # ldx < K
+    assert q8(F.FP8_MX, x=None) == F.FP4_ERR_NULL
+    assert q8(F.FP8_ROWWISE, scales=None) == F.FP4_ERR_NULL                # dynamic modes need scales
+    assert q8(F.FP8_MX, codes=A + 8) == F.FP4_ERR_ALIGN
+    assert q8(F.FP8_MX, ldx=132) == F.FP4_ERR_ALIGN                        # bf16 stride % 8
+    assert q8(F.FP8_MX, ldx=132, weight=True) != F.FP4_ERR_ALIGN           # fp32 stride % 4
+    for bad in (0.0, -2.0, float("inf"), float("nan"), 2.0 ** 101):
+        assert q8(F.FP8_PER_TENSOR, s=bad, scales=None) == F.FP4_ERR_INPUT_SCALE
+        assert q8(F.FP8_PER_TENSOR, s=bad, scales=None, weight=True) == F.FP4_ERR_WEIGHT_SCALE
+    assert q8(F.FP8_PER_TENSOR, s=0.5) == F.FP4_ERR_FORMAT                 # per-tensor: no scale array
+    for m in (F.FP8_MX, F.FP8_ROWWISE, F.FP8_BLOCK):
+        assert q8(m, s=0.5) == F.FP4_ERR_FORMAT                            # dynamic: tensor scale 1
+    assert q8(F.FP8_BLOCK, x=None, M=0, codes=None, scales=None) == F.FP4_OK
+
+
+def test_fp8_gemm_validation():
+    assert g8(4) == F.FP4_ERR_FORMAT
+    assert g8(F.FP8_MX, od=3) == F.FP4_ERR_FORMAT
+    assert g8(F.FP8_MX, K=96) == F.FP4_ERR_SHAPE                           # K % 128
+    assert g8(F.FP8_MX, K=0) == F.FP4_ERR_SHAPE
+    assert g8(F.FP8_MX, ldo=4) == F.FP4_ERR_SHAPE
+    assert g8(F.FP8_MX, M=0, ac=None, asc=None) == F.FP4_OK
+    assert g8(F.FP8_BLOCK, wsc=None) == F.FP4_ERR_NULL
+    assert g8(F.FP8_ROWWISE, out=None) == F.FP4_ERR_NULL
+    assert g8(F.FP8_MX, ac=A + 4) == F.FP4_ERR_ALIGN
+    assert g8(F.FP8_PER_TENSOR, asc=None, wsc=None, ats=0.0) == F.FP4_ERR_INPUT_SCALE
+    assert g8(F.FP8_PER_TENSOR, asc=None, wsc=None, wts=float("nan")) == F.FP4_ERR_WEIGHT_SCALE
+    # the product of the two tensor scales must stay a finite normal fp32
+    assert g8(F.FP8_PER_TENSOR, asc=None, wsc=None, ats=2.0 ** 90, wts=2.0 ** 90) == F.FP4_ERR_INPUT_SCALE
+    assert g8(F.FP8_PER_TENSOR, asc=None, wsc=None, ats=2.0 ** -90, wts=2.0 ** -90) == F.FP4_ERR_INPUT_SCALE
+    assert g8(F.FP8_PER_TENSOR, ats=0.5, wts=0.5) == F.FP4_ERR_FORMAT      # scale arrays given
+    assert g8(F.FP8_ROWWISE, ats=0.5) == F.FP4_ERR_FORMAT
+
+
+@pytest.mark.skipif(not NO_GPU, reason="device check only observable without a GPU")
+def test_fp8_valid_calls_stop_at_device_check_without_gpu():
+    assert q8(F.FP8_MX) == F.FP4_ERR_DEVICE
+    assert q8(F.FP8_BLOCK, weight=True) == F.FP4_ERR_DEVICE
+    assert g8(F.FP8_PER_TENSOR, asc=None, wsc=None, ats=0.5, wts=0.25) == F.FP4_ERR_DEVICE
+    assert g8(F.FP8_MX) == F.FP4_ERR_DEVICE
