@@ -22,6 +22,11 @@ and the other workloads ride along as records under "workloads":
   moe-nvfp4      NVFP4 MoE, 128 experts top-8, hidden 2048, intermediate 768, T = 1, 64, 4096
   moe-mxfp4      MXFP4 MoE, 256 experts top-8 + shared, hidden 6144, intermediate 2048,
                  Zipf(1.1) routing, T = 64, 8192
+  fp8-decode-mx, fp8-decode-rowwise
+                 MXFP8 / FP8 rowwise (per-token x per-channel) GEMM, N=14336, K=4096,
+                 M = 1, 8, 32: dynamic activation quantization + GEMM, rotated weights
+  fp8-prefill-mx, fp8-prefill-block
+                 MXFP8 / FP8 1x128-128x128 block-scaled GEMM, M=8192, N=4096, K=4096
 
 --workload NAME measures one of them alone (its record becomes the line; used for
 profiling runs).
@@ -63,7 +68,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="all",
                    choices=["all", "decode", "w4a16-small", "prefill-nvfp4", "prefill-mxfp4",
-                            "moe-nvfp4", "moe-mxfp4",
+                            "moe-nvfp4", "moe-mxfp4", "fp8-decode-mx", "fp8-decode-rowwise",
+                            "fp8-prefill-mx", "fp8-prefill-block",
                             "prefill"])            # (old name of prefill-nvfp4)
     p.add_argument("--tokens", type=int, default=None, help="MoE token count (one)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -366,6 +372,151 @@ def bench_prefill(args, torch, F, copy, fmt):
     return rec
 
 
+# ---- FP8 family: MXFP8 and FP8 W8A8 -----------------------------------------------
+
+
+def _fp8_scale_shape(mode, rows, K, weight):
+    if mode == "mx":
+        return (rows, K // 32), 1
+    if mode == "rowwise":
+        return (rows,), 4
+    if mode == "block":
+        return (((rows + 127) // 128) if weight else rows, K // 128), 4
+    return None, 0
+
+
+def _fp8_operands(torch, F, mode, N, K, dev, copies=1):
+    import synth
+    m = F.FP8_MODES[mode]
+    w = torch.from_numpy(synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT)).to(dev)
+    shp, esz = _fp8_scale_shape(mode, N, K, True)
+    sdt = torch.uint8 if esz == 1 else torch.float32
+    wc = torch.empty((copies, N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((copies,) + shp, dtype=sdt, device=dev)
+    F.fp8_quantize_weight(m, w, N, K, K, 1.0, wc[0], ws[0])
+    for c in range(1, copies):
+        wc[c] = wc[0]
+        ws[c] = ws[0]
+    del w
+    return wc, ws, N * K + ws[0].numel() * esz
+
+
+def bench_fp8_decode(args, torch, F, copy, mode):
+    import synth
+    dev = torch.device("cuda:0")
+    N, K, MMAX = 14336, 4096, 32
+    m = F.FP8_MODES[mode]
+    wbytes = N * K + (N * K // 32 if mode == "mx" else N * 4)
+    copies = max(2, -(-300 * 2 ** 20 // wbytes))          # > 256 MB last-level cache
+    wc, ws, wbytes = _fp8_operands(torch, F, mode, N, K, dev, copies)
+    a, _ = bf16_tensor(torch, synth.with_outliers(synth.normal((MMAX, K), seed=0, role=synth.ACT),
+                                                  seed=0), dev)
+    codes = torch.empty((MMAX, K), dtype=torch.uint8, device=dev)
+    shp, esz = _fp8_scale_shape(mode, MMAX, K, False)
+    scales = torch.empty(shp, dtype=torch.uint8 if esz == 1 else torch.float32, device=dev)
+    out = torch.empty((MMAX, N), dtype=torch.bfloat16, device=dev)
+    names = {}
+
+    def run(M):
+        def quant(i):
+            F.fp8_quantize_act(m, a, M, K, K, 1.0, codes, scales)
+            names["quant"] = F.fp4_last_kernel()
+
+        def gemm(i):
+            c = i % copies
+            F.fp8_gemm(m, M, N, K, codes, scales, 1.0, wc[c], ws[c], 1.0, out, N, F.FP4_OUT_BF16)
+            names["gemm"] = F.fp4_last_kernel()
+
+        def step(i):
+            quant(i)
+            gemm(i)
+        ms, per, wall = measure(torch, step, args.steps, args.warmup)
+        quant(0)
+        kus = kernel_avg_us(torch, gemm, args.steps, args.warmup)
+        qus = kernel_avg_us(torch, quant, args.steps, args.warmup)
+        a_sc = M * K // 32 if mode == "mx" else M * 4
+        step_bytes = wbytes + M * K * 2 + M * N * 2
+        kern_bytes = wbytes + M * K + a_sc + M * N * 2
+        flops = 2.0 * M * N * K
+        return {
+            "M": M, "ms_per_step": ms, "samples_ms": [round(x, 6) for x in per], "wall_s": wall,
+            "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+            "gemm_us": round(kus, 3), "quant_us": round(qus, 3),
+            "gemm_TFLOPs": round(flops / (kus * 1e-6) / 1e12, 3),
+            "roofline": hbm_roof(kern_bytes / (kus * 1e-6) / 1e9, copy,
+                                 stored_traffic(f"fp8_decode_{mode}_M{M}"),
+                                 kernel=names.get("gemm"), algorithmic_bytes_per_launch=kern_bytes,
+                                 avg_launch_us=round(kus, 3)),
+        }
+
+    per_m = {M: run(M) for M in (1, 8, MMAX)}
+    main = per_m[MMAX]
+    label = "MXFP8" if mode == "mx" else "FP8 rowwise"
+    rec = {
+        "metric": f"FP8 decode GEMM GB/s ({label}, M=32, N=14336, K=4096)",
+        "value": main["step_GBps"], "unit": "GB/s", "ms_per_step": main["ms_per_step"],
+        "dtype": "fp8",
+        "config": {"workload": f"{label} decode GEMM, M=32 (also M=1, 8 under per_m), N=14336, "
+                               "K=4096, dynamic activation quantization",
+                   "M": MMAX, "N": N, "K": K, "weight_copies_rotated": copies},
+        "roofline": main["roofline"],
+        "per_m": {str(mm): {k: v for k, v in r.items() if k != "wall_s"} for mm, r in per_m.items()},
+        "samples_ms": main["samples_ms"], "wall_s_timed": main["wall_s"],
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_fp8(mode, MMAX, N, K, w_rows=2048)
+    return rec
+
+
+def bench_fp8_prefill(args, torch, F, copy, mode):
+    import synth
+    dev = torch.device("cuda:0")
+    M, N, K = 8192, 4096, 4096
+    m = F.FP8_MODES[mode]
+    wc, ws, wbytes = _fp8_operands(torch, F, mode, N, K, dev)
+    wc, ws = wc[0], ws[0]
+    a, _ = bf16_tensor(torch, synth.normal((M, K), seed=0, role=synth.ACT, index=3), dev)
+    codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    shp, esz = _fp8_scale_shape(mode, M, K, False)
+    scales = torch.empty(shp, dtype=torch.uint8 if esz == 1 else torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    names = {}
+
+    def quant(i):
+        F.fp8_quantize_act(m, a, M, K, K, 1.0, codes, scales)
+        names["quant"] = F.fp4_last_kernel()
+
+    def gemm(i):
+        F.fp8_gemm(m, M, N, K, codes, scales, 1.0, wc, ws, 1.0, out, N, F.FP4_OUT_BF16)
+        names["gemm"] = F.fp4_last_kernel()
+
+    def step(i):
+        quant(i)
+        gemm(i)
+
+    ms, per, wall = measure(torch, step, args.steps, args.warmup)
+    kus = kernel_avg_us(torch, gemm, args.steps, 2)
+    qus = kernel_avg_us(torch, quant, args.steps, 2)
+    flops = 2.0 * M * N * K
+    tf = flops / (kus * 1e-6) / 1e12
+    label = "MXFP8" if mode == "mx" else "FP8 block-scaled"
+    rec = {
+        "metric": f"FP8 prefill GEMM TFLOP/s ({label}, M=8192, N=4096, K=4096)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": ms,
+        "dtype": "fp8",
+        "config": {"workload": f"{label} prefill GEMM, dynamic activation quantization, bf16 out",
+                   "M": M, "N": N, "K": K},
+        "roofline": mfma_roof(tf, PEAK_TFLOPS["fp8"], stored_traffic(f"fp8_prefill_{mode}"),
+                              kernel=names.get("gemm"), algorithmic_flops_per_launch=flops,
+                              avg_launch_us=round(kus, 2)),
+        "quant_us": round(qus, 2), "quant_kernel": names.get("quant"),
+        "samples_ms": [round(x, 6) for x in per], "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_fp8(mode, 64, N, K, prefill=True)
+    return rec
+
+
 class MoeLayer:
     """One of the two MoE layers on the device: a few experts quantized on the GPU, the
     others seeded row permutations of them (distinct memory, same distribution)."""
@@ -645,6 +796,48 @@ def cpu_baseline_moe(layer, hv, ids, w, kw, target_s=CPU_TARGET_S):
                       + f", H={H}, I={I}) in {el:.1f} s of oracle time"}
 
 
+def cpu_baseline_fp8(mode, M, N, K, w_rows=None, prefill=False, target_s=CPU_TARGET_S):
+    """The oracle's FP8 chain (dynamic activation quantization, dequantization of both
+    operands, float64 matmul) on a bounded sample."""
+    import synth
+    from oracle import fp8 as O8
+    w = synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT)
+    if w_rows:
+        w = w[:w_rows]
+    om = {"rowwise": O8.ROWWISE, "block": O8.BLOCK}
+    if mode == "mx":
+        wc, wsc = O8.quantize_mxfp8(w)
+    else:
+        wc, wsc = O8.quantize_weight(om[mode], w)
+    idx = 3 if prefill else 0
+    a = synth.normal((8192 if prefill else M, K), seed=0, role=synth.ACT, index=idx)
+    if not prefill:
+        a = synth.with_outliers(a, seed=0)
+    _, av = synth.bf16_bits(a)
+
+    def one(i):
+        x = av[(i * M) % av.shape[0]:(i * M) % av.shape[0] + M]
+        if mode == "mx":
+            ac, asc = O8.quantize_mxfp8(x)
+            return O8.gemm_mxfp8(ac, asc, wc, wsc)
+        ac, asc = O8.quantize_act(om[mode], x)
+        return O8.gemm(om[mode], ac, asc, wc, wsc)
+
+    n, el = _repeat(one, target_s)
+    rows = w.shape[0]
+    if prefill:
+        return {"value": round(2.0 * M * rows * K * n / el / 1e12, 6), "unit": "TFLOP/s",
+                "cores": blas_threads(), "kind": "oracle",
+                "sample": f"{M}-row slices of the 8192 activation rows against the full weight, "
+                          f"{n} repetitions in {el:.1f} s"}
+    wb = rows * K + (rows * K // 32 if mode == "mx" else rows * 4)
+    step_bytes = wb + M * K * 2 + M * rows * 2
+    return {"value": round(step_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"first {rows} of {N} weight rows (M={M}, K={K}), {n} repetitions in "
+                      f"{el:.1f} s: activation quantization + float64 dequant + float64 matmul"}
+
+
 # ---------------------------------------------------------------------------------
 
 
@@ -699,6 +892,18 @@ def main():
             log(f"moe-{fmt} T={T_} done")
         del layer
         torch.cuda.empty_cache()
+    for mode in ("mx", "rowwise"):
+        if wl in ("all", f"fp8-decode-{mode}"):
+            if copy is None:
+                copy = copy_bandwidth(torch)
+            records[f"fp8-decode-{mode}"] = bench_fp8_decode(args, torch, F, copy, mode)
+            torch.cuda.empty_cache()
+            log(f"fp8-decode-{mode} done")
+    for mode in ("mx", "block"):
+        if wl in ("all", f"fp8-prefill-{mode}"):
+            records[f"fp8-prefill-{mode}"] = bench_fp8_prefill(args, torch, F, copy, mode)
+            torch.cuda.empty_cache()
+            log(f"fp8-prefill-{mode} done")
 
     head_key = "decode" if wl == "all" else next(iter(records))
     head = dict(records[head_key])
