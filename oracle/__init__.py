@@ -29,6 +29,9 @@ Modules
            rowwise (per token / per channel) or 1x128 / 128x128 block scales
            ("vLLM per-format kernel capability matrix derived from source": the MX
            group size, MXFP8 native on gfx95, FP8's three scaling modes)
+  mx       MX formats with any element type (e2m1, e2m3, e3m2, e4m3), the 6-bit packing,
+           and matmuls whose two operands use different element types (same page: the
+           MXFP6 section)
 
 Pins (tests/test_oracle_*.py) tie every function to something outside itself:
 closed-form value tables, torch's float8 decoders, hand-worked examples in
