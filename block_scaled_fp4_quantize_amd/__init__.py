@@ -34,8 +34,11 @@ FP4_ERR_DEVICE = -8
 FP4_ERR_LAUNCH = -9
 
 FP8_MX, FP8_PER_TENSOR, FP8_ROWWISE, FP8_BLOCK = 0, 1, 2, 3
+MX_E2M1, MX_E2M3, MX_E3M2, MX_E4M3 = 0, 1, 2, 3
 
 FORMATS = {"nvfp4": FP4_NVFP4, "mxfp4": FP4_MXFP4}
+MX_ELEMS = {"e2m1": MX_E2M1, "e2m3": MX_E2M3, "e3m2": MX_E3M2, "e4m3": MX_E4M3}
+MX_BITS = {MX_E2M1: 4, MX_E2M3: 6, MX_E3M2: 6, MX_E4M3: 8}
 FP8_MODES = {"mx": FP8_MX, "per_tensor": FP8_PER_TENSOR, "rowwise": FP8_ROWWISE,
              "block": FP8_BLOCK}
 MODES = {"w4a4": FP4_W4A4, "w4a16": FP4_W4A16}
@@ -47,6 +50,7 @@ EXPORTED = [
     "fp4_moe_topk_softmax", "fp4_moe_workspace_size", "fp4_moe_workspace_layout",
     "fp4_moe_grouped_gemm", "fp4_arch_supported", "fp4_status_str", "fp4_last_kernel",
     "fp8_quantize_act", "fp8_quantize_weight", "fp8_gemm",
+    "mx_quantize_act", "mx_quantize_weight", "mx_gemm",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -134,6 +138,10 @@ _c = {
     "fp8_quantize_act": _proto("fp8_quantize_act", _int, [_int, _vp, _i64, _i64, _i64, _f32, _vp, _vp, _vp]),
     "fp8_quantize_weight": _proto("fp8_quantize_weight", _int, [_int, _vp, _i64, _i64, _i64, _f32, _vp, _vp,
                                                                 _vp]),
+    "mx_quantize_act": _proto("mx_quantize_act", _int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "mx_quantize_weight": _proto("mx_quantize_weight", _int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "mx_gemm": _proto("mx_gemm", _int, [_int, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64,
+                                        _int, _vp]),
     "fp8_gemm": _proto("fp8_gemm", _int, [_int, _i64, _i64, _i64, _vp, _vp, _f32, _vp, _vp, _f32, _vp,
                                           _i64, _int, _vp]),
 }
@@ -173,6 +181,10 @@ def _mode(m):
 
 def _f8mode(m):
     return FP8_MODES.get(m, m) if isinstance(m, str) else int(m)
+
+
+def _mxelem(t):
+    return MX_ELEMS.get(t, t) if isinstance(t, str) else int(t)
 
 
 def _check(st, where, raise_on_error):
@@ -317,3 +329,23 @@ def fp8_gemm(mode, M, N, K, a_codes, a_scales, a_tensor_scale, w_codes, w_scales
                         _ptr(w_codes), _ptr(w_scales), w_tensor_scale, _ptr(out), ldo, out_dtype,
                         _stream(stream, out, w_codes))
     return _check(st, "fp8_gemm", check)
+
+
+def mx_quantize_act(t, x, M, K, ldx, codes, scales, stream=None, check=True):
+    st = _c["mx_quantize_act"](_mxelem(t), _ptr(x), M, K, ldx, _ptr(codes), _ptr(scales),
+                               _stream(stream, x, codes))
+    return _check(st, "mx_quantize_act", check)
+
+
+def mx_quantize_weight(t, w, N, K, ldw, codes, scales, stream=None, check=True):
+    st = _c["mx_quantize_weight"](_mxelem(t), _ptr(w), N, K, ldw, _ptr(codes), _ptr(scales),
+                                  _stream(stream, w, codes))
+    return _check(st, "mx_quantize_weight", check)
+
+
+def mx_gemm(a_t, w_t, M, N, K, a_codes, a_scales, w_codes, w_scales, out, ldo,
+            out_dtype=FP4_OUT_BF16, stream=None, check=True):
+    st = _c["mx_gemm"](_mxelem(a_t), _mxelem(w_t), M, N, K, _ptr(a_codes), _ptr(a_scales),
+                       _ptr(w_codes), _ptr(w_scales), _ptr(out), ldo, out_dtype,
+                       _stream(stream, out, w_codes))
+    return _check(st, "mx_gemm", check)

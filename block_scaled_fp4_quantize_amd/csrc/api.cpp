@@ -20,6 +20,7 @@
 
 #include "fp4.h"
 #include "fp8.h"
+#include "mx.h"
 #include "internal.h"
 
 namespace {
@@ -896,6 +897,103 @@ fp4_status fp8_gemm(fp8_scaling mode, int64_t M, int64_t N, int64_t K, const uin
   p.out_f32 = out_dtype == FP4_OUT_F32;
   const char* name = "";
   hipError_t e = fp4::launch_fp8_gemm(mode, p, (hipStream_t)stream, &name);
+  return launched(e, name);
+}
+
+}  // extern "C"
+
+// ---- MX formats of any element type --------------------------------------------------
+namespace {
+
+// the scaled MFMA's element-type code of each mx_elem (e4m3 0, e2m3 2, e3m2 3, e2m1 4)
+int mfma_code(int t) { return t == MX_E2M1 ? 4 : (t == MX_E2M3 ? 2 : (t == MX_E3M2 ? 3 : 0)); }
+bool elem_ok(int t) { return t == MX_E2M1 || t == MX_E2M3 || t == MX_E3M2 || t == MX_E4M3; }
+
+fp4_status mx_quantize_common(int t, const void* x, bool weight, int64_t M, int64_t K,
+                              int64_t ldx, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!elem_ok(t)) return FP4_ERR_FORMAT;
+  if (M < 0 || K < 0 || K % 32) return FP4_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP4_OK;
+  if (ldx < K) return FP4_ERR_SHAPE;
+  if (!x || !codes || !scales) return FP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || ldx % (weight ? 4 : 8))
+    return FP4_ERR_ALIGN;
+  fp4_status st = device_check();
+  if (st != FP4_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  const char* name = "";
+  hipError_t e;
+  if (t == MX_E2M1) {                     // the MXFP4 quantizer of fp4_quantize_act
+    fp4::QuantParams q{};
+    q.x = x;
+    q.in_f32 = weight ? 1 : 0;
+    q.M = M;
+    q.K = K;
+    q.ldx = ldx;
+    q.g = 1.0f;
+    q.codes = codes;
+    q.scales = scales;
+    e = fp4::launch_quant(FP4_MXFP4, q, s, &name);
+  } else {
+    fp4::Fp8QuantParams q{};
+    q.x = x;
+    q.in_f32 = weight ? 1 : 0;
+    q.M = M;
+    q.K = K;
+    q.ldx = ldx;
+    q.tensor_scale = 1.0f;
+    q.codes = codes;
+    q.mx_scales = scales;
+    e = t == MX_E4M3 ? fp4::launch_fp8_quant(fp4::kF8_MX, q, s, &name)
+                     : fp4::launch_mx6_quant(mfma_code(t), q, s, &name);
+  }
+  return launched(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4_status mx_quantize_act(mx_elem t, const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                           uint8_t* codes, uint8_t* scales, void* stream) {
+  return mx_quantize_common(t, x_bf16, false, M, K, ldx, codes, scales, stream);
+}
+
+fp4_status mx_quantize_weight(mx_elem t, const float* w, int64_t N, int64_t K, int64_t ldw,
+                              uint8_t* codes, uint8_t* scales, void* stream) {
+  return mx_quantize_common(t, w, true, N, K, ldw, codes, scales, stream);
+}
+
+fp4_status mx_gemm(mx_elem a_t, mx_elem w_t, int64_t M, int64_t N, int64_t K,
+                   const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                   const uint8_t* w_scales, void* out, int64_t ldo, fp4_out out_dtype,
+                   void* stream) {
+  if (!elem_ok(a_t) || !elem_ok(w_t) || (out_dtype != FP4_OUT_BF16 && out_dtype != FP4_OUT_F32))
+    return FP4_ERR_FORMAT;
+  if (M < 0 || N < 0 || K <= 0 || K % 128) return FP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP4_OK;
+  if (ldo < N) return FP4_ERR_SHAPE;
+  if (!a_codes || !a_scales || !w_codes || !w_scales || !out) return FP4_ERR_NULL;
+  const void* ptrs[] = {a_codes, a_scales, w_codes, w_scales, out};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return FP4_ERR_ALIGN;
+  fp4_status st = device_check();
+  if (st != FP4_OK) return st;
+  fp4::Fp8GemmParams p{};
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.a_codes = a_codes;
+  p.w_codes = w_codes;
+  p.a_mx = a_scales;
+  p.w_mx = w_scales;
+  p.alpha = 1.0f;
+  p.unit_scale = 127;
+  p.out = out;
+  p.ldo = ldo;
+  p.out_f32 = out_dtype == FP4_OUT_F32;
+  const char* name = "";
+  hipError_t e = fp4::launch_mx_gemm(mfma_code(a_t), mfma_code(w_t), p, (hipStream_t)stream, &name);
   return launched(e, name);
 }
 

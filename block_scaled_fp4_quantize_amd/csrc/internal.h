@@ -128,6 +128,15 @@ struct Fp8GemmParams {
 // K % 128 == 0
 hipError_t launch_fp8_gemm(int mode, const Fp8GemmParams& p, hipStream_t s, const char** name);
 
+// MX formats of any element type.  Element types are the scaled MFMA's codes: 0 e4m3,
+// 2 e2m3, 3 e3m2, 4 e2m1.  MXFP6 quantization (elem 2 or 3) writes 24 bytes of codes per
+// 32 elements (element i at bits [6 i, 6 i + 6) of the little-endian group) and one e8m0
+// byte per 32 into mx_scales; K % 32 == 0.
+hipError_t launch_mx6_quant(int elem, const Fp8QuantParams& p, hipStream_t s, const char** name);
+// MX matmul with element types fa (activations) and fw (weights): a_mx / w_mx scales,
+// alpha 1, unit_scale unused; K % 128 == 0.  (e4m3 x e4m3 is launch_fp8_gemm's MX mode.)
+hipError_t launch_mx_gemm(int fa, int fw, const Fp8GemmParams& p, hipStream_t s, const char** name);
+
 // ---- MoE stages ------------------------------------------------------------------
 hipError_t launch_topk_softmax(const float* logits, int64_t T, int64_t E, int k,
                                int renormalize, int32_t* ids, float* w, hipStream_t s,

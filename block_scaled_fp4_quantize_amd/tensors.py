@@ -7,7 +7,7 @@ from . import (FP4_MXFP4, FP4_NVFP4, FP4_OUT_BF16, FP4_OUT_F32, FP4_W4A4, FP4_W4
                fp4_gemm, fp4_gemm_workspace_size, fp4_moe_grouped_gemm, fp4_moe_topk_softmax,
                fp4_moe_workspace_layout, fp4_moe_workspace_size, fp4_quantize_act,
                fp4_quantize_weight, fp8_gemm, fp8_quantize_act, fp8_quantize_weight,
-               make_moe_args)
+               make_moe_args, MX_BITS, _mxelem, mx_gemm, mx_quantize_act, mx_quantize_weight)
 
 
 def _alloc_u8(rows, cols, device):
@@ -99,6 +99,30 @@ def fp8_gemm_t(mode, a_codes, a_scales, w_codes, w_scales, a_tensor_scale=1.0,
     od = FP4_OUT_F32 if out.dtype == torch.float32 else FP4_OUT_BF16
     fp8_gemm(m, M, N, K, a_codes, a_scales, float(a_tensor_scale), w_codes, w_scales,
              float(w_tensor_scale), out, out.stride(0), od)
+    return out
+
+
+def mx_quantize_t(t, x):
+    """bf16 activations or fp32 weights [R, K] -> (packed codes [R, K*bits/8], e8m0 [R, K/32])."""
+    e = _mxelem(t)
+    R, K = x.shape
+    codes = _alloc_u8(R, K * MX_BITS[e] // 8, x.device)
+    scales = _alloc_u8(R, K // 32, x.device)
+    f = mx_quantize_weight if x.dtype == torch.float32 else mx_quantize_act
+    f(e, x, R, K, x.stride(0), codes, scales)
+    return codes, scales
+
+
+def mx_gemm_t(a_t, w_t, a_codes, a_scales, w_codes, w_scales, out_dtype=torch.bfloat16, out=None):
+    """out [M, N] = a_hat @ w_hat^T for MX operands of element types a_t and w_t."""
+    ea, ew = _mxelem(a_t), _mxelem(w_t)
+    M = a_codes.shape[0]
+    K = a_scales.shape[1] * 32
+    N = w_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=w_codes.device)
+    od = FP4_OUT_F32 if out.dtype == torch.float32 else FP4_OUT_BF16
+    mx_gemm(ea, ew, M, N, K, a_codes, a_scales, w_codes, w_scales, out, out.stride(0), od)
     return out
 
 

@@ -40,13 +40,13 @@ def header_functions():
     for h in sorted(os.listdir(INCLUDE)):
         if h.endswith(".h"):
             text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
-            names |= set(re.findall(r"\b(fp[48]_[a-z_0-9]+)\s*\(", text))
+            names |= set(re.findall(r"\b((?:fp[48]|mx)_[a-z_0-9]+)\s*\(", text))
     return sorted(names)
 
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) >= 15 and "fp8_gemm" in names
+    assert len(names) >= 18 and {"fp8_gemm", "mx_gemm"} <= set(names)
     lib = ctypes.CDLL(F.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -318,3 +318,35 @@ def test_fp8_valid_calls_stop_at_device_check_without_gpu():
     assert q8(F.FP8_BLOCK, weight=True) == F.FP4_ERR_DEVICE
     assert g8(F.FP8_PER_TENSOR, asc=None, wsc=None, ats=0.5, wts=0.25) == F.FP4_ERR_DEVICE
     assert g8(F.FP8_MX) == F.FP4_ERR_DEVICE
+
+
+# ---- MX formats of any element type (same page: group size 32, MXFP6, MXFP8) ----------
+
+
+def test_mx_validation():
+    qa = lambda t, **kw: F.mx_quantize_act(t, kw.get("x", A), kw.get("M", 4), kw.get("K", 64),
+                                           kw.get("ldx", 64), kw.get("c", B), kw.get("s", C),
+                                           check=False)
+    assert qa(7) == F.FP4_ERR_FORMAT
+    assert qa(F.MX_E2M3, K=48, ldx=48) == F.FP4_ERR_SHAPE                 # K % 32
+    assert qa(F.MX_E3M2, ldx=32) == F.FP4_ERR_SHAPE                       # ldx < K
+    assert qa(F.MX_E2M3, s=None) == F.FP4_ERR_NULL
+    assert qa(F.MX_E2M3, x=A + 4) == F.FP4_ERR_ALIGN
+    assert qa(F.MX_E2M3, ldx=68) == F.FP4_ERR_ALIGN                       # bf16 stride % 8
+    assert qa(F.MX_E2M3, M=0, x=None, c=None, s=None) == F.FP4_OK
+    wq = F.mx_quantize_weight(F.MX_E3M2, A, 4, 64, 68, B, C, check=False)
+    assert wq != F.FP4_ERR_ALIGN                                          # fp32 stride % 4
+    gm = lambda at, wt, **kw: F.mx_gemm(at, wt, kw.get("M", 4), kw.get("N", 8), kw.get("K", 128),
+                                        kw.get("ac", A), kw.get("asc", B), C, D,
+                                        kw.get("out", 0x50000), kw.get("ldo", 8), kw.get("od", 0),
+                                        check=False)
+    assert gm(F.MX_E2M1, 9) == F.FP4_ERR_FORMAT
+    assert gm(F.MX_E2M1, F.MX_E4M3, od=2) == F.FP4_ERR_FORMAT
+    assert gm(F.MX_E2M1, F.MX_E4M3, K=96) == F.FP4_ERR_SHAPE                # K % 128
+    assert gm(F.MX_E2M1, F.MX_E4M3, ldo=7) == F.FP4_ERR_SHAPE
+    assert gm(F.MX_E2M1, F.MX_E4M3, asc=None) == F.FP4_ERR_NULL
+    assert gm(F.MX_E2M1, F.MX_E4M3, out=0x50008) == F.FP4_ERR_ALIGN
+    assert gm(F.MX_E2M1, F.MX_E4M3, M=0, ac=None) == F.FP4_OK
+    if NO_GPU:
+        assert qa(F.MX_E2M3) == F.FP4_ERR_DEVICE
+        assert gm(F.MX_E3M2, F.MX_E2M1) == F.FP4_ERR_DEVICE
