@@ -27,6 +27,9 @@ and the other workloads ride along as records under "workloads":
                  M = 1, 8, 32: dynamic activation quantization + GEMM, rotated weights
   fp8-prefill-mx, fp8-prefill-block
                  MXFP8 / FP8 1x128-128x128 block-scaled GEMM, M=8192, N=4096, K=4096
+  mx-w4a8-decode MX GEMM with FP4 (e2m1) weights and FP8 (e4m3) activations, N=14336,
+                 K=4096, M = 1, 8, 32
+  mxfp6-prefill  MXFP6 (e2m3) x MXFP6 (e2m3) GEMM, M=8192, N=4096, K=4096
 
 --workload NAME measures one of them alone (its record becomes the line; used for
 profiling runs).
@@ -69,7 +72,8 @@ def parse():
     p.add_argument("--workload", default="all",
                    choices=["all", "decode", "w4a16-small", "prefill-nvfp4", "prefill-mxfp4",
                             "moe-nvfp4", "moe-mxfp4", "fp8-decode-mx", "fp8-decode-rowwise",
-                            "fp8-prefill-mx", "fp8-prefill-block",
+                            "fp8-prefill-mx", "fp8-prefill-block", "mx-w4a8-decode",
+                            "mxfp6-prefill",
                             "prefill"])            # (old name of prefill-nvfp4)
     p.add_argument("--tokens", type=int, default=None, help="MoE token count (one)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -517,6 +521,132 @@ def bench_fp8_prefill(args, torch, F, copy, mode):
     return rec
 
 
+# ---- MX formats of any element type ---------------------------------------------------
+
+
+def _mx_weights(torch, F, we, N, K, dev, copies=1):
+    import synth
+    e = F.MX_ELEMS[we]
+    w = torch.from_numpy(synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT)).to(dev)
+    wc = torch.empty((copies, N, K * F.MX_BITS[e] // 8), dtype=torch.uint8, device=dev)
+    ws = torch.empty((copies, N, K // 32), dtype=torch.uint8, device=dev)
+    F.mx_quantize_weight(e, w, N, K, K, wc[0], ws[0])
+    for c in range(1, copies):
+        wc[c] = wc[0]
+        ws[c] = ws[0]
+    del w
+    return wc, ws, N * K * F.MX_BITS[e] // 8 + N * K // 32
+
+
+def bench_mx_decode(args, torch, F, copy, ae="e4m3", we="e2m1"):
+    import synth
+    dev = torch.device("cuda:0")
+    N, K, MMAX = 14336, 4096, 32
+    ea, ew = F.MX_ELEMS[ae], F.MX_ELEMS[we]
+    wbytes = N * K * F.MX_BITS[ew] // 8 + N * K // 32
+    copies = max(2, -(-300 * 2 ** 20 // wbytes))          # > 256 MB last-level cache
+    wc, ws, wbytes = _mx_weights(torch, F, we, N, K, dev, copies)
+    a, _ = bf16_tensor(torch, synth.with_outliers(synth.normal((MMAX, K), seed=0, role=synth.ACT),
+                                                  seed=0), dev)
+    codes = torch.empty((MMAX, K * F.MX_BITS[ea] // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((MMAX, K // 32), dtype=torch.uint8, device=dev)
+    out = torch.empty((MMAX, N), dtype=torch.bfloat16, device=dev)
+    names = {}
+
+    def run(M):
+        def quant(i):
+            F.mx_quantize_act(ea, a, M, K, K, codes, scales)
+
+        def gemm(i):
+            c = i % copies
+            F.mx_gemm(ea, ew, M, N, K, codes, scales, wc[c], ws[c], out, N, F.FP4_OUT_BF16)
+            names["gemm"] = F.fp4_last_kernel()
+
+        def step(i):
+            quant(i)
+            gemm(i)
+        ms, per, wall = measure(torch, step, args.steps, args.warmup)
+        quant(0)
+        kus = kernel_avg_us(torch, gemm, args.steps, args.warmup)
+        step_bytes = wbytes + M * K * 2 + M * N * 2
+        kern_bytes = wbytes + M * (K * F.MX_BITS[ea] // 8 + K // 32) + M * N * 2
+        return {
+            "M": M, "ms_per_step": ms, "samples_ms": [round(x, 6) for x in per], "wall_s": wall,
+            "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 2), "gemm_us": round(kus, 3),
+            "roofline": hbm_roof(kern_bytes / (kus * 1e-6) / 1e9, copy,
+                                 stored_traffic(f"mx_decode_{ae}_{we}_M{M}"),
+                                 kernel=names.get("gemm"), algorithmic_bytes_per_launch=kern_bytes,
+                                 avg_launch_us=round(kus, 3)),
+        }
+
+    per_m = {M: run(M) for M in (1, 8, MMAX)}
+    main = per_m[MMAX]
+    rec = {
+        "metric": f"MX decode GEMM GB/s ({we} weights x {ae} activations, M=32, N=14336, K=4096)",
+        "value": main["step_GBps"], "unit": "GB/s", "ms_per_step": main["ms_per_step"],
+        "dtype": f"{we}x{ae}",
+        "config": {"workload": f"MX GEMM, {we} weights x {ae} activations quantized on the fly, "
+                               "M=32 (also M=1, 8 under per_m), N=14336, K=4096",
+                   "M": MMAX, "N": N, "K": K, "weight_copies_rotated": copies},
+        "roofline": main["roofline"],
+        "per_m": {str(mm): {k: v for k, v in r.items() if k != "wall_s"} for mm, r in per_m.items()},
+        "samples_ms": main["samples_ms"], "wall_s_timed": main["wall_s"],
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_mx(ae, we, MMAX, N, K, w_rows=2048)
+    return rec
+
+
+def bench_mx_prefill(args, torch, F, copy, ae="e2m3", we="e2m3"):
+    import synth
+    dev = torch.device("cuda:0")
+    M, N, K = 8192, 4096, 4096
+    ea, ew = F.MX_ELEMS[ae], F.MX_ELEMS[we]
+    wc, ws, _ = _mx_weights(torch, F, we, N, K, dev)
+    wc, ws = wc[0], ws[0]
+    a, _ = bf16_tensor(torch, synth.normal((M, K), seed=0, role=synth.ACT, index=3), dev)
+    codes = torch.empty((M, K * F.MX_BITS[ea] // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    names = {}
+
+    def quant(i):
+        F.mx_quantize_act(ea, a, M, K, K, codes, scales)
+        names["quant"] = F.fp4_last_kernel()
+
+    def gemm(i):
+        F.mx_gemm(ea, ew, M, N, K, codes, scales, wc, ws, out, N, F.FP4_OUT_BF16)
+        names["gemm"] = F.fp4_last_kernel()
+
+    def step(i):
+        quant(i)
+        gemm(i)
+
+    ms, per, wall = measure(torch, step, args.steps, args.warmup)
+    kus = kernel_avg_us(torch, gemm, args.steps, 2)
+    qus = kernel_avg_us(torch, quant, args.steps, 2)
+    flops = 2.0 * M * N * K
+    tf = flops / (kus * 1e-6) / 1e12
+    # the scaled MFMA runs 6- and 4-bit operands at the FP4/FP6 rate, anything with e4m3 at
+    # the FP8 rate
+    pk = PEAK_TFLOPS["fp8"] if "e4m3" in (ae, we) else PEAK_TFLOPS["fp4"]
+    rec = {
+        "metric": f"MX prefill GEMM TFLOP/s ({ae} x {we}, M=8192, N=4096, K=4096)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": ms,
+        "dtype": f"{ae}x{we}",
+        "config": {"workload": f"MX GEMM, {ae} activations quantized on the fly x {we} weights, "
+                               "bf16 out", "M": M, "N": N, "K": K},
+        "roofline": mfma_roof(tf, pk, stored_traffic(f"mx_prefill_{ae}_{we}"),
+                              kernel=names.get("gemm"), algorithmic_flops_per_launch=flops,
+                              avg_launch_us=round(kus, 2)),
+        "quant_us": round(qus, 2), "quant_kernel": names.get("quant"),
+        "samples_ms": [round(x, 6) for x in per], "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_mx(ae, we, 64, N, K, prefill=True)
+    return rec
+
+
 class MoeLayer:
     """One of the two MoE layers on the device: a few experts quantized on the GPU, the
     others seeded row permutations of them (distinct memory, same distribution)."""
@@ -838,6 +968,40 @@ def cpu_baseline_fp8(mode, M, N, K, w_rows=None, prefill=False, target_s=CPU_TAR
                       f"{el:.1f} s: activation quantization + float64 dequant + float64 matmul"}
 
 
+def cpu_baseline_mx(ae, we, M, N, K, w_rows=None, prefill=False, target_s=CPU_TARGET_S):
+    """The oracle's MX chain (activation quantization, dequantization of both operands,
+    float64 matmul) on a bounded sample."""
+    import synth
+    from oracle import mx as OX
+    w = synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT)
+    if w_rows:
+        w = w[:w_rows]
+    wc, wsc = OX.quantize(we, w)
+    a = synth.normal((8192 if prefill else M, K), seed=0, role=synth.ACT, index=3 if prefill else 0)
+    if not prefill:
+        a = synth.with_outliers(a, seed=0)
+    _, av = synth.bf16_bits(a)
+
+    def one(i):
+        x = av[(i * M) % av.shape[0]:(i * M) % av.shape[0] + M]
+        ac, asc = OX.quantize(ae, x)
+        return OX.gemm(ae, ac, asc, we, wc, wsc)
+
+    n, el = _repeat(one, target_s)
+    rows = w.shape[0]
+    if prefill:
+        return {"value": round(2.0 * M * rows * K * n / el / 1e12, 6), "unit": "TFLOP/s",
+                "cores": blas_threads(), "kind": "oracle",
+                "sample": f"{M}-row slices of the 8192 activation rows against the full weight, "
+                          f"{n} repetitions in {el:.1f} s"}
+    bits = OX.BITS[we]
+    step_bytes = rows * K * bits // 8 + rows * K // 32 + M * K * 2 + M * rows * 2
+    return {"value": round(step_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"first {rows} of {N} weight rows (M={M}, K={K}), {n} repetitions in "
+                      f"{el:.1f} s: activation quantization + float64 dequant + float64 matmul"}
+
+
 # ---------------------------------------------------------------------------------
 
 
@@ -904,6 +1068,16 @@ def main():
             records[f"fp8-prefill-{mode}"] = bench_fp8_prefill(args, torch, F, copy, mode)
             torch.cuda.empty_cache()
             log(f"fp8-prefill-{mode} done")
+    if wl in ("all", "mx-w4a8-decode"):
+        if copy is None:
+            copy = copy_bandwidth(torch)
+        records["mx-w4a8-decode"] = bench_mx_decode(args, torch, F, copy)
+        torch.cuda.empty_cache()
+        log("mx-w4a8-decode done")
+    if wl in ("all", "mxfp6-prefill"):
+        records["mxfp6-prefill"] = bench_mx_prefill(args, torch, F, copy)
+        torch.cuda.empty_cache()
+        log("mxfp6-prefill done")
 
     head_key = "decode" if wl == "all" else next(iter(records))
     head = dict(records[head_key])

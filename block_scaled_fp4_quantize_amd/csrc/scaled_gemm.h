@@ -150,10 +150,14 @@ __device__ __forceinline__ void store_block(const Fp8GemmParams& p, const v16f& 
 // ---- few activation rows (decode): one workgroup = 32 weight rows x 32 activation rows,
 // its 4 waves splitting K by 128-deep blocks (kb = wave, wave + 4, ...), operands loaded
 // straight from global memory, partial sums added through LDS in wave order (bitwise
-// reproducible).  Weights are read once per 32 activation rows.
+// reproducible).  Weights are read once per 32 activation rows.  (Each 16-byte-per-lane
+// load touches 32 rows' cache lines; 8 waves per workgroup, or two blocks in flight per
+// wave, measured slower: the extra lines in flight outgrow the L1.)
+constexpr int kRowsWaves = 4;
+
 template <int MODE, int FA, int FW>
-__global__ __launch_bounds__(256) void rows_kernel(Fp8GemmParams p) {
-  __shared__ v16f red[3][64];
+__global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) {
+  __shared__ v16f red[kRowsWaves - 1][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t ntiles = (p.N + 31) / 32;
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(256) void rows_kernel(Fp8GemmParams p) {
   v16f acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  for (int64_t kb = wave; kb < nkb; kb += 4) {
+  for (int64_t kb = wave; kb < nkb; kb += kRowsWaves) {
     const int64_t k0 = kb * 128;
     const v8i w0 = ld_lane<FW>(wrow, k0, h), w1 = ld_lane<FW>(wrow, k0 + 64, h);
     const v8i a0 = ld_lane<FA>(arow, k0, h), a1 = ld_lane<FA>(arow, k0 + 64, h);
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(256) void rows_kernel(Fp8GemmParams p) {
   __syncthreads();
   if (wave != 0 || m >= p.M) return;
 #pragma unroll
-  for (int wv = 0; wv < 3; ++wv) {
+  for (int wv = 0; wv < kRowsWaves - 1; ++wv) {
     const v16f o = red[wv][lane];
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] += o[v];
@@ -449,7 +453,7 @@ hipError_t launch(const Fp8GemmParams& p, hipStream_t s, const char** name, cons
     *name = rows_name;
     const int64_t grid = ((p.N + 31) / 32) * ((p.M + 31) / 32);
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rows_kernel<MODE, FA, FW>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((rows_kernel<MODE, FA, FW>), dim3((unsigned)grid), dim3(64 * kRowsWaves), 0, s, p);
     return hipGetLastError();
   }
   using C = TileCfg<FA, FW>;
