@@ -127,8 +127,8 @@ void moe_plan(const fp4_moe_args* a, bool w4a4, bool may_w4a16, MoePlan* pl) {
   pl->L.x_codes = take((size_t)x_rows * (size_t)(a->H / 2));
   pl->L.x_scales = take((size_t)x_rows * (size_t)(a->H / G));
   const int akind = w4a4 ? fp4::kA_FP4 : fp4::kA_BF16;
-  pl->fuse_routed = fp4::gemm_can_fuse_swiglu(akind, P, a->H, a->I, true, bm);
-  pl->fuse_shared = sh && fp4::gemm_can_fuse_swiglu(akind, a->T, a->H, a->I, false, bm);
+  pl->fuse_routed = fp4::gemm_can_fuse_swiglu(a->fmt, akind, P, a->H, a->I, true, bm, nmb);
+  pl->fuse_shared = sh && fp4::gemm_can_fuse_swiglu(a->fmt, akind, a->T, a->H, a->I, false, bm, 1);
   const int64_t gu_rows = (pl->fuse_routed ? 0 : P) + (sh && !pl->fuse_shared ? a->T : 0);
   pl->L.gu_rows = gu_rows;
   pl->L.swiglu_fused = (pl->fuse_routed ? 1 : 0) | (pl->fuse_shared ? 2 : 0);

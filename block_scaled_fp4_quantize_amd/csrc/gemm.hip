@@ -435,6 +435,72 @@ __device__ __forceinline__ void stream_compute(
   }
 }
 
+// Fused SwiGLU + requant epilogue of a gate/up GEMM on the streaming kernel: waves 0-1
+// hold gate columns c0 .. c0 + 31 and waves 2-3 the matching up columns (c0 = 32 nt);
+// h = SiLU(alpha g) * (alpha u) is formed through LDS and quantized 8 columns per lane
+// (2 lanes per NVFP4 block of 16, 4 per MXFP4 block of 32), the arithmetic of the
+// stand-alone SwiGLU kernel, into h_codes / h_scales at the rows of the output.
+template <int FMT, int MT>
+__device__ __forceinline__ void stream_swiglu_epilogue(const GemmParams& p, const v4f (&acc)[MT],
+                                                       float alpha, int grp, int64_t row0,
+                                                       int64_t row_end, int64_t nt, int wave,
+                                                       int lane, float* up, float* hb) {
+  constexpr int LD = 33;                   // padded row of 32 columns
+  constexpr int LPG = FMT == kNV ? 2 : 4;
+  const int r = lane & 15, cq = 4 * (lane >> 4);
+  __syncthreads();                         // every wave is done with the staging buffers
+  if (wave >= 2) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) up[(t * 16 + r) * LD + (wave - 2) * 16 + cq + v] = acc[t][v] * alpha;
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = (t * 16 + r) * LD + wave * 16 + cq + v;
+        hb[o] = swiglu1(acc[t][v] * alpha, up[o]);
+      }
+  }
+  __syncthreads();
+  const int tid = wave * 64 + lane;
+  if (wave >= MT) return;                  // 64 MT lanes: 16 MT rows x 4 chunks of 8
+  const int row = tid >> 2, chunk = tid & 3;
+  float h[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = hb[row * LD + chunk * 8 + i];
+    amax = fmaxf(amax, fabsf(h[i]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  if (LPG == 4) amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int64_t m = row0 + row;
+  if (m >= row_end) return;
+  const float g = p.h_grp_g ? p.h_grp_g[grp] : p.h_g;
+  uint32_t packed = 0, sc;
+  if (FMT == kNV) {
+    float rr;
+    sc = q_nv_scale(amax, g, &rr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed |= q_nv_pack2(h[2 * i], h[2 * i + 1], rr) << (8 * i);
+  } else {
+    int E;
+    sc = q_mx_scale(amax, &E);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed |= q_mx_pack2(h[2 * i], h[2 * i + 1], E) << (8 * i);
+  }
+  const int64_t col = nt * 32 + chunk * 8;
+  *reinterpret_cast<uint32_t*>(p.h_codes + m * (p.I / 2) + col / 2) = packed;
+  if ((chunk & (LPG - 1)) == 0) {
+    constexpr int G = FMT == kNV ? 16 : 32;
+    p.h_scales[m * (p.I / G) + col / G] = (uint8_t)sc;
+  }
+}
+
 template <int FMT, int MT, bool SVEC>
 __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
   using C = StreamCfg<FMT, MT>;
@@ -444,7 +510,8 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int64_t ntiles = (p.N + 63) >> 6;
+  // fused SwiGLU: a workgroup owns 32 intermediate columns (their gate and up rows)
+  const int64_t ntiles = p.fuse_swiglu ? p.I / 32 : (p.N + 63) >> 6;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
   int grp = 0;
@@ -466,7 +533,8 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
 
   const int r = lane & 15;
   const int gq = lane >> 4;
-  const int64_t wn_raw = nt * 64 + wave * 16 + r;
+  const int64_t wn_raw = !p.fuse_swiglu ? nt * 64 + wave * 16 + r
+                         : (wave < 2 ? nt * 32 + wave * 16 + r : p.I + nt * 32 + (wave - 2) * 16 + r);
   const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;
   const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
   const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
@@ -527,11 +595,17 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
     }
   }
 
+  if (p.fuse_swiglu) {
+    stream_swiglu_epilogue<FMT, MT>(p, acc, alpha, grp, row0, row_end, nt, wave, lane,
+                                    reinterpret_cast<float*>(a_lds[0]),
+                                    reinterpret_cast<float*>(a_lds[1]));
+    return;
+  }
+  const int64_t n0 = nt * 64 + wave * 16 + 4 * (lane >> 4);
   // a lane holds out[m][n0 .. n0+3]: one 8-byte (bf16) or 16-byte (fp32) store when the
   // four columns exist and the row stride and base allow it
   const bool vec = (p.ldo & 3) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.out) & (p.out_f32 ? 15 : 7)) == 0;
-  const int64_t n0 = nt * 64 + wave * 16 + 4 * (lane >> 4);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int64_t m = row0 + t * 16 + (lane & 15);
@@ -562,7 +636,7 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
 
 template <int FMT, int MT>
 hipError_t launch_stream(const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ntiles = (p.N + 63) / 64;
+  const int64_t ntiles = p.fuse_swiglu ? p.I / 32 : (p.N + 63) / 64;
   const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + 16 * MT - 1) / (16 * MT);
   const int64_t grid = ntiles * mblocks;
   if (grid == 0) return hipSuccess;
@@ -607,17 +681,31 @@ int gemm_block_rows(int /*fmt*/, int akind, int64_t rows_per_group, int64_t H, i
   return rows_per_group <= 16 ? 16 : 32;
 }
 
-bool gemm_can_fuse_swiglu(int akind, int64_t M, int64_t K, int64_t I, bool grouped, int bm) {
+bool gemm_can_fuse_swiglu(int fmt, int akind, int64_t M, int64_t K, int64_t I, bool grouped,
+                          int bm, int64_t n_mblocks) {
   if (akind != kA_FP4 || K % kKStep != 0 || I <= 0 || I % 128 != 0) return false;
-  return grouped ? bm == 128 : M > 64;
+  if (grouped ? bm == 128 : M > 64) return true;          // the tiled kernel
+  if (grouped && bm != 16 && bm != 32) return false;
+  // the streaming kernel: where the unfused GEMM would run on it anyway, or for at most
+  // 16 rows, where saving the SwiGLU launch outweighs the resident kernel's faster
+  // stream (measured: NVFP4, 8 routed rows, 12.6 -> 9.1 us; 512 rows, 53 -> 68 us)
+  const bool one = grouped ? bm == 16 : M <= 16;
+  const bool resident = one && !(grouped && fmt == kMX) &&
+                        resident_fits(fmt, 1, grouped ? 16 : M, 2 * I, K, grouped ? n_mblocks : 1);
+  return !resident || M <= 16;
 }
 
 hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
                        const char** name) {
-  if (p.fuse_swiglu) {   // only the tiled kernel has the fused SwiGLU epilogue
-    if (!gemm_can_fuse_swiglu(akind, p.M, p.K, p.I, p.mblk_expert != nullptr, p.bm))
+  if (p.fuse_swiglu) {   // the tiled or the streaming kernel
+    if (!gemm_can_fuse_swiglu(fmt, akind, p.M, p.K, p.I, p.mblk_expert != nullptr, p.bm,
+                              p.n_mblocks))
       return hipErrorInvalidValue;
-    return launch_gemm_tiled(fmt, p, s, name);
+    if (p.mblk_expert ? p.bm == 128 : p.M > 64) return launch_gemm_tiled(fmt, p, s, name);
+    if (p.mblk_expert && p.bm != 16 && p.bm != 32) return hipErrorInvalidValue;
+    const bool one1 = p.mblk_expert ? p.bm == 16 : p.M <= 16;
+    if (fmt == kNV) return one1 ? launch_stream<kNV, 1>(p, s, name) : launch_stream<kNV, 2>(p, s, name);
+    return one1 ? launch_stream<kMX, 1>(p, s, name) : launch_stream<kMX, 2>(p, s, name);
   }
   // row blocks of 32 (two 16-row activation tiles); dense problems of at most 16
   // rows, and expert tables of 16-row blocks, use one tile

@@ -78,7 +78,11 @@ struct GemmParams {
 enum AKind : int { kA_FP4 = 0, kA_BF16 = 1 };
 // Whether a gate/up GEMM of this shape runs on the tiled kernel, and so can take the
 // fused SwiGLU + requant epilogue (grouped: 128-row blocks; dense: more than 64 rows).
-bool gemm_can_fuse_swiglu(int akind, int64_t M, int64_t K, int64_t I, bool grouped, int bm);
+// Whether a gate/up GEMM of this shape takes the fused SwiGLU + requant epilogue: on
+// the tiled kernel (grouped: 128-row blocks; dense: more than 64 rows), else on the
+// streaming kernel when the plain GEMM would run there too or has at most 16 rows.
+bool gemm_can_fuse_swiglu(int fmt, int akind, int64_t M, int64_t K, int64_t I, bool grouped,
+                          int bm, int64_t n_mblocks);
 // Row-block height of the block table for grouped (MoE) GEMMs of these shapes
 // (GEMM1 has K = H, GEMM2 has K = I); launch_gemm picks its kernel from it.
 int gemm_block_rows(int fmt, int akind, int64_t rows_per_group, int64_t H, int64_t I);

@@ -228,9 +228,11 @@ typedef struct {
   int64_t x_rows;         /* rows in x_codes: T (MXFP4) or T*k + T (NVFP4) */
   int64_t gu_rows;        /* rows in gu */
   int32_t swiglu_fused;   /* bit 0: routed rows, bit 1: shared rows have SwiGLU and the
-                             requant fused into the gate/up GEMM (W4A4 on the tiled kernel:
-                             128-row expert blocks, or more than 64 tokens for the shared
-                             expert, and I % 128 == 0); their h is written without gu */
+                             requant fused into the gate/up GEMM (W4A4, H and I multiples
+                             of 128; on the tiled kernel -- 128-row expert blocks, or more
+                             than 64 tokens for the shared expert -- or on the streaming
+                             kernel where the plain GEMM would stream too or has at most
+                             16 rows); their h is written without gu */
 } fp4_moe_layout;
 
 size_t fp4_moe_workspace_size(const fp4_moe_args* a);

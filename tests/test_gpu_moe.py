@@ -349,6 +349,13 @@ SMALL = [
     # GEMMs run on 128-row tiles, with ragged expert row counts
     ("nvfp4", "w4a4", dict(T=150, H=256, I=128, E=4, k=2, shared=True)),
     ("mxfp4", "w4a4", dict(T=200, H=384, I=256, E=6, k=3, shared=True)),
+    # decode token counts with H and I multiples of 128: SwiGLU + requant ride on the
+    # streaming gate/up GEMM where it streams anyway (MXFP4 expert tables, the shared
+    # expert) or has at most 16 rows
+    ("nvfp4", "w4a4", dict(T=8, H=256, I=128, E=8, k=2, shared=True)),
+    ("nvfp4", "w4a4", dict(T=60, H=256, I=128, E=8, k=4, shared=False)),
+    ("mxfp4", "w4a4", dict(T=40, H=384, I=256, E=16, k=4, shared=True)),
+    ("mxfp4", "w4a4", dict(T=1, H=256, I=128, E=8, k=2, shared=False)),
 ]
 
 
@@ -356,12 +363,13 @@ SMALL = [
 def test_moe_small(fmt, mode, kw):
     pb = MoeProblem(fmt, mode, seed=kw["T"] + kw["E"], **kw)
     r = run_gpu(pb)
-    if mode == "w4a4" and kw["T"] * kw["k"] >= 48 * kw["E"] and kw["H"] % 128 == 0 and \
-            kw["I"] % 128 == 0:
-        # 128-row expert blocks: SwiGLU + requant run in the gate/up GEMM's epilogue
-        # (and in the shared expert's, above 64 tokens)
-        assert r["fused"] & 1, r["fused"]
-        assert bool(r["fused"] & 2) == (kw["shared"] and kw["T"] > 64), r["fused"]
+    if mode == "w4a4" and kw["H"] % 128 == 0 and kw["I"] % 128 == 0:
+        # 128-row expert blocks or MXFP4 expert tables (tiled or streaming kernels):
+        # SwiGLU + requant ride on the routed gate/up GEMM, and on the shared expert's
+        if kw["T"] * kw["k"] >= 48 * kw["E"] or fmt == "mxfp4":
+            assert r["fused"] & 1, r["fused"]
+        if kw["shared"]:
+            assert r["fused"] & 2, r["fused"]
     verify(pb, r, max_diff_abs=2)
 
 
@@ -403,6 +411,8 @@ def test_zero_activation_scale_rejected_not_zeroed():
     ("nvfp4", dict(T=200, H=256, I=64, E=16, k=8)),    # three-kernel dispatch, unfused SwiGLU
     ("nvfp4", dict(T=150, H=256, I=128, E=4, k=2)),    # 128-row tiles, fused SwiGLU
     ("mxfp4", dict(T=200, H=256, I=64, E=16, k=8)),
+    ("nvfp4", dict(T=20, H=256, I=128, E=8, k=4)),     # streaming fused SwiGLU
+    ("mxfp4", dict(T=9, H=384, I=128, E=8, k=2)),
 ])
 def test_moe_dropped_ids(fmt, kw):
     # expert ids outside [0, E) (device data, not checked on the host) drop their slot:
