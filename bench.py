@@ -12,7 +12,9 @@ The default run measures every workload of the metric -- FP4 GEMM TFLOP/s and GB
            step = the activation quantization plus the GEMM (the two launches of a
            fused fp4_gemm call, issued separately so the GEMM is timed by itself too).
            The weights rotate over copies that together exceed the 256 MB last-level
-           cache, so every step streams them from HBM.
+           cache, so every step streams them from HBM.  They are prepared once
+           (fp4_prepare_weights: the layout the decode kernels stream); the GEMM on the
+           row-major layout is timed beside it (gemm_us_row_major_weights).
 
 and the other workloads ride along as records under "workloads":
 
@@ -218,6 +220,12 @@ def bench_decode(args, torch, F, copy):
     ws = torch.empty((copies, N, K // 32), dtype=torch.uint8, device=dev)
     wc[:] = wc0
     ws[:] = ws0
+    # the weights prepared once, as a serving engine would at load (fp4_prepare_weights);
+    # the row-major layout is timed beside it
+    wp = torch.empty_like(wc)
+    chk = torch.zeros(1, dtype=torch.int32, device=dev)
+    for c in range(copies):
+        F.fp4_prepare_weights(F.FP4_MXFP4, wc[c], ws[c], N, K, wp[c], chk)
     a, _ = bf16_tensor(torch, synth.with_outliers(synth.normal((MMAX, K), seed=0, role=synth.ACT),
                                                   seed=0), dev)
     codes = torch.empty((MMAX, K // 2), dtype=torch.uint8, device=dev)
@@ -232,9 +240,14 @@ def bench_decode(args, torch, F, copy):
 
         def gemm(i):
             c = i % copies
+            F.fp4_gemm(F.FP4_MXFP4, F.FP4_W4A4, M, N, K, None, 0, codes, scales, wp[c], ws[c],
+                       1.0, 1.0, out, N, F.FP4_OUT_BF16, F.FP4_FLAG_PREPARED_WEIGHTS, None, 0)
+            names["gemm"] = F.fp4_last_kernel()
+
+        def gemm_row_major(i):
+            c = i % copies
             F.fp4_gemm(F.FP4_MXFP4, F.FP4_W4A4, M, N, K, None, 0, codes, scales, wc[c], ws[c],
                        1.0, 1.0, out, N, F.FP4_OUT_BF16, 0, None, 0)
-            names["gemm"] = F.fp4_last_kernel()
 
         def step(i):
             quant(i)
@@ -242,6 +255,7 @@ def bench_decode(args, torch, F, copy):
         ms, per, wall = measure(torch, step, args.steps, args.warmup)
         quant(0)
         kus = kernel_avg_us(torch, gemm, args.steps, args.warmup)
+        kus_rm = kernel_avg_us(torch, gemm_row_major, args.steps, args.warmup)
         qus = kernel_avg_us(torch, quant, args.steps, args.warmup)
         step_bytes = wbytes + M * K * 2 + M * N * 2                 # weights once, bf16 in, bf16 out
         kern_bytes = wbytes + M * (K // 2 + K // 32) + M * N * 2   # the GEMM's own operands
@@ -251,7 +265,8 @@ def bench_decode(args, torch, F, copy):
             "M": M, "ms_per_step": ms, "samples_ms": [round(x, 6) for x in per], "wall_s": wall,
             "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 2),
             "step_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 3),
-            "gemm_us": round(kus, 3), "quant_us": round(qus, 3),
+            "gemm_us": round(kus, 3), "gemm_us_row_major_weights": round(kus_rm, 3),
+            "quant_us": round(qus, 3),
             "gemm_TFLOPs": round(flops / (kus * 1e-6) / 1e12, 3),
             "roofline": hbm_roof(kgbs, copy, stored_traffic(f"decode_gemm_M{M}"),
                                  kernel=names.get("gemm"), algorithmic_bytes_per_launch=kern_bytes,
@@ -265,7 +280,8 @@ def bench_decode(args, torch, F, copy):
         "value": main["step_GBps"], "unit": "GB/s", "ms_per_step": main["ms_per_step"],
         "dtype": "fp4",
         "config": {"workload": "MXFP4 W4A4 decode GEMV/GEMM, M=32 (also M=1, 8 under per_m), "
-                               "N=14336, K=4096, activations quantized on the fly",
+                               "N=14336, K=4096, activations quantized on the fly, weights "
+                               "prepared once (fp4_prepare_weights)",
                    "M": MMAX, "N": N, "K": K, "weight_copies_rotated": copies},
         "roofline": main["roofline"],
         "per_m": {str(m): {k: v for k, v in r.items() if k not in ("wall_s",)}

@@ -20,6 +20,7 @@ FP4_NVFP4, FP4_MXFP4 = 0, 1
 FP4_W4A4, FP4_W4A16 = 0, 1
 FP4_OUT_BF16, FP4_OUT_F32 = 0, 1
 FP4_FLAG_ALLOW_W4A16_FALLBACK = 1
+FP4_FLAG_PREPARED_WEIGHTS = 2
 
 FP4_OK = 0
 FP4_OK_FELL_BACK_W4A16 = 1
@@ -46,7 +47,7 @@ GROUP = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
 EXPORTED = [
     "fp4_quantize_act", "fp4_quantize_weight", "fp4_gemm", "fp4_gemm_workspace_size",
-    "fp4_gemm_noalloc",
+    "fp4_gemm_noalloc", "fp4_prepared_weight_bytes", "fp4_prepare_weights",
     "fp4_moe_topk_softmax", "fp4_moe_workspace_size", "fp4_moe_workspace_layout",
     "fp4_moe_grouped_gemm", "fp4_arch_supported", "fp4_status_str", "fp4_last_kernel",
     "fp8_quantize_act", "fp8_quantize_weight", "fp8_gemm",
@@ -126,6 +127,8 @@ _c = {
     "fp4_gemm_noalloc": _proto("fp4_gemm_noalloc", _int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp,
                                                           _vp, _vp, _vp, _f32, _f32, _vp, _i64, _int,
                                                           _u32, _vp]),
+    "fp4_prepared_weight_bytes": _proto("fp4_prepared_weight_bytes", _sz, [_i64, _i64]),
+    "fp4_prepare_weights": _proto("fp4_prepare_weights", _int, [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "fp4_gemm_workspace_size": _proto("fp4_gemm_workspace_size", _sz, [_int, _int, _i64, _i64, _int]),
     "fp4_moe_topk_softmax": _proto("fp4_moe_topk_softmax", _int, [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "fp4_moe_workspace_size": _proto("fp4_moe_workspace_size", _sz, [ctypes.POINTER(MoeArgs)]),
@@ -236,6 +239,18 @@ def fp4_gemm_noalloc(fmt, mode, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes
                                 input_scale, _ptr(out), ldo, out_dtype, flags,
                                 _stream(stream, out, w_codes))
     return _check(st, "fp4_gemm_noalloc", check)
+
+
+def fp4_prepared_weight_bytes(N, K):
+    return _c["fp4_prepared_weight_bytes"](N, K)
+
+
+def fp4_prepare_weights(fmt, w_codes, w_scales, N, K, prepared_codes, check_i32, stream=None,
+                        check=True):
+    st = _c["fp4_prepare_weights"](_fmt(fmt), _ptr(w_codes), _ptr(w_scales), N, K,
+                                   _ptr(prepared_codes), _ptr(check_i32),
+                                   _stream(stream, w_codes, prepared_codes))
+    return _check(st, "fp4_prepare_weights", check)
 
 
 def fp4_moe_topk_softmax(logits, T, E, k, renormalize, topk_ids, topk_w, stream=None, check=True):

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libfp4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["quant.hip", "gemm.hip", "gemm_tile.hip", "gemm_resident.hip", "moe.hip", "fp8.hip", "mx.hip",
-           "api.cpp"]
+           "prepare.hip", "api.cpp"]
 
 DEVICE_FLAGS = [
     "--offload-arch=gfx950",

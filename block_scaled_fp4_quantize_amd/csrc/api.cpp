@@ -330,11 +330,16 @@ fp4_status gemm_call(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_
     workspace = nullptr;
     workspace_bytes = FP4_NOALLOC_SCRATCH_BYTES;
   }
+  const bool prepared = (flags & FP4_FLAG_PREPARED_WEIGHTS) != 0;
   if (!fmt_ok(fmt) || !mode_ok(mode) || (out_dtype != FP4_OUT_BF16 && out_dtype != FP4_OUT_F32) ||
-      (flags & ~FP4_FLAG_ALLOW_W4A16_FALLBACK))
+      (flags & ~(FP4_FLAG_ALLOW_W4A16_FALLBACK | FP4_FLAG_PREPARED_WEIGHTS)))
     return FP4_ERR_FORMAT;
   const int64_t G = group_of(fmt);
   if (M < 0 || N < 0 || K <= 0 || K % G) return FP4_ERR_SHAPE;
+  // prepared weights feed the decode kernels: W4A4, at most 64 rows, whole blocks
+  if (prepared && (mode != FP4_W4A4 || (flags & FP4_FLAG_ALLOW_W4A16_FALLBACK)))
+    return FP4_ERR_FORMAT;
+  if (prepared && (M > 64 || N % 16 || K % 128)) return FP4_ERR_SHAPE;
   if (M == 0 || N == 0) return FP4_OK;
   if (ldo < N) return FP4_ERR_SHAPE;
   const bool need_bf16 = mode == FP4_W4A16;
@@ -400,6 +405,7 @@ fp4_status gemm_call(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_
   p.a_scales = as;
   p.a_bf16 = static_cast<const uint16_t*>(a_bf16);
   p.lda = lda;
+  p.w_tiled = prepared ? 1 : 0;
   p.w_codes = w_codes;
   p.w_scales = w_scales;
   p.alpha = nv ? (w4a4 ? weight_scale_2 * input_scale : weight_scale_2) : 1.0f;
@@ -435,6 +441,36 @@ fp4_status fp4_gemm_noalloc(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N,
   return gemm_call(fmt, mode, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scales,
                    weight_scale_2, input_scale, out, ldo, out_dtype, flags, nullptr, 0, stream,
                    true);
+}
+
+size_t fp4_prepared_weight_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 16 || K % 128) return 0;
+  return (size_t)N * (size_t)(K / 2);
+}
+
+fp4_status fp4_prepare_weights(fp4_format fmt, const uint8_t* w_codes, const uint8_t* w_scales,
+                               int64_t N, int64_t K, uint8_t* prepared_codes, int32_t* check,
+                               void* stream) {
+  if (!fmt_ok(fmt)) return FP4_ERR_FORMAT;
+  if (N <= 0 || K <= 0 || N % 16 || K % 128) return FP4_ERR_SHAPE;
+  if (!w_codes || !w_scales || !prepared_codes || !check) return FP4_ERR_NULL;
+  if (!aligned16(w_codes) || !aligned16(w_scales) || !aligned16(prepared_codes) ||
+      (reinterpret_cast<uintptr_t>(check) & 3u))
+    return FP4_ERR_ALIGN;
+  fp4_status st = device_check();
+  if (st != FP4_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemsetAsync(check, 0, sizeof(int32_t), s) != hipSuccess) return launched(hipGetLastError(), "");
+  hipError_t e = fp4::launch_prepare(fmt, w_codes, w_scales, N, K, prepared_codes, check, s);
+  st = launched(e, "prepare_weights");
+  if (st != FP4_OK) return st;
+  int32_t bad = 0;
+  if (hipMemcpyAsync(&bad, check, sizeof(bad), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    (void)hipGetLastError();
+    return FP4_ERR_LAUNCH;
+  }
+  return bad ? FP4_ERR_WEIGHT_SCALE : FP4_OK;
 }
 
 fp4_status fp4_moe_topk_softmax(const float* logits, int64_t T, int64_t E, int k,

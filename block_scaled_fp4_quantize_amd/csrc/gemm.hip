@@ -347,17 +347,21 @@ __device__ __forceinline__ void stage_store(uint8_t* a_lds, uint8_t* s_lds, int 
   if (C::SBT >= 16) { sp[2] = rg.s2; sp[3] = rg.s3; }
 }
 
+// The lane's 16-byte code piece of step st (128 elements) sits at wbase + st * wstride:
+// row-major codes (stride 64 bytes), or the prepared layout of 16-row x 128-element
+// blocks stored in lane order (stride 1 KB, one contiguous kilobyte per wave).  Steps
+// at or past the end read step 0 (their operand is zeroed in stream_compute).
 template <int FMT, bool SVEC>
-__device__ __forceinline__ void stream_w_load(const uint8_t* wrow, const uint8_t* wsrow,
-                                              int64_t c, int64_t K, int64_t KS, int gq,
-                                              uint4 (&q)[kSSteps],
+__device__ __forceinline__ void stream_w_load(const uint8_t* wbase, int64_t wstride,
+                                              const uint8_t* wsrow, int64_t c, int64_t K,
+                                              int64_t KS, uint4 (&q)[kSSteps],
                                               uint4 (&sc)[StreamCfg<FMT, 1>::SDW]) {
   constexpr int SSTR = StreamCfg<FMT, 1>::SSTR;
-  const int64_t k0 = c * kSKC;
+  const int64_t S = K / kKStep;
 #pragma unroll
   for (int j = 0; j < kSSteps; ++j) {
-    const int64_t kk = k0 + j * kKStep + gq * 32;
-    q[j] = *reinterpret_cast<const uint4*>(wrow + (kk < K ? (kk >> 1) : 0));
+    const int64_t st = c * kSSteps + j;
+    q[j] = *reinterpret_cast<const uint4*>(wbase + (st < S ? st : 0) * wstride);
   }
 #pragma unroll
   for (int i = 0; i < StreamCfg<FMT, 1>::SDW; ++i) {
@@ -536,7 +540,11 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
   const int64_t wn_raw = !p.fuse_swiglu ? nt * 64 + wave * 16 + r
                          : (wave < 2 ? nt * 32 + wave * 16 + r : p.I + nt * 32 + (wave - 2) * 16 + r);
   const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;
-  const uint8_t* wrow = p.w_codes + grp * p.w_estride_codes + wn * KB;
+  const uint8_t* wcodes = p.w_codes + grp * p.w_estride_codes;
+  const uint8_t* wbase = p.w_tiled
+      ? wcodes + (((wn >> 4) * (K / kKStep)) * 64 + (wn & 15) + 16 * gq) * 16
+      : wcodes + wn * KB + gq * 16;
+  const int64_t wstride = p.w_tiled ? 1024 : kKStep / 2;
   const uint8_t* wsrow = p.w_scales + grp * p.w_estride_scales + wn * KS;
 
   // activation staging: thread -> (row, segment of the row's chunk)
@@ -562,7 +570,7 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
   };
 
   st = stage_load<FMT, MT>(s_codes, s_scales, 0, KB, KS, sseg);
-  stream_w_load<FMT, SVEC>(wrow, wsrow, 0, K, KS, gq, wA, sA);
+  stream_w_load<FMT, SVEC>(wbase, wstride, wsrow, 0, K, KS, wA, sA);
   stage_store<FMT, MT>(a_lds[0], s_lds[0], srow, sseg, st);
   __syncthreads();
   // (the prefetch of the chunk after the last one is skipped: it would only make the
@@ -573,7 +581,7 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
       // issued before the weight loads, so waiting for it leaves those in flight
       st = stage_load<FMT, MT>(s_codes, s_scales, c + 1, KB, KS, sseg);
       __builtin_amdgcn_sched_barrier(0);  // keep the staging loads ahead of the weight loads
-      stream_w_load<FMT, SVEC>(wrow, wsrow, c + 1, K, KS, gq, wB, sB);
+      stream_w_load<FMT, SVEC>(wbase, wstride, wsrow, c + 1, K, KS, wB, sB);
       stream_compute<FMT, MT>(a_lds[0], s_lds[0], wA, sA, steps_of(c), r, gq, acc);
       stage_store<FMT, MT>(a_lds[1], s_lds[1], srow, sseg, st);
       __syncthreads();
@@ -585,7 +593,7 @@ __global__ __launch_bounds__(256) void stream_gemm(GemmParams p) {
     if (c + 2 < nchunks) {
       st = stage_load<FMT, MT>(s_codes, s_scales, c + 2, KB, KS, sseg);
       __builtin_amdgcn_sched_barrier(0);
-      stream_w_load<FMT, SVEC>(wrow, wsrow, c + 2, K, KS, gq, wA, sA);
+      stream_w_load<FMT, SVEC>(wbase, wstride, wsrow, c + 2, K, KS, wA, sA);
       stream_compute<FMT, MT>(a_lds[1], s_lds[1], wB, sB, steps_of(c + 1), r, gq, acc);
       stage_store<FMT, MT>(a_lds[0], s_lds[0], srow, sseg, st);
       __syncthreads();
@@ -707,6 +715,9 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
     if (fmt == kNV) return one1 ? launch_stream<kNV, 1>(p, s, name) : launch_stream<kNV, 2>(p, s, name);
     return one1 ? launch_stream<kMX, 1>(p, s, name) : launch_stream<kMX, 2>(p, s, name);
   }
+  // prepared weights: only the decode kernels (streaming, resident) read that layout
+  if (p.w_tiled && (akind != kA_FP4 || p.mblk_expert || p.M > 64 || p.K % kKStep || p.N % 16))
+    return hipErrorInvalidValue;
   // row blocks of 32 (two 16-row activation tiles); dense problems of at most 16
   // rows, and expert tables of 16-row blocks, use one tile
   const bool one = p.mblk_expert ? p.bm == 16 : p.M <= 16;

@@ -277,11 +277,15 @@ __global__ __launch_bounds__(256, KSPLIT == 4 ? 4 : 1) void resident_gemm(GemmPa
   const int wrow = rg * 16 + r;
   const int64_t wn_raw = nt * C::RROWS + wrow;
   const int64_t wn = wn_raw < p.N ? wn_raw : p.N - 1;   // padded rows: outputs not stored
-  const uint8_t* wsrc = wcodes + wn * KB + gq * 16;
+  // row-major codes (64 bytes per step), or the prepared layout of 16-row x 128-element
+  // blocks in lane order (1 KB per step, contiguous over the wave)
+  const uint8_t* wsrc = p.w_tiled ? wcodes + (((wn >> 4) * NS) * 64 + (wn & 15) + 16 * gq) * 16
+                                  : wcodes + wn * KB + gq * 16;
+  const int64_t wstep = p.w_tiled ? 1024 : 64;
   u32x4 wq[RING];
 #pragma unroll
   for (int i = 0; i < RING; ++i)
-    wq[i] = *reinterpret_cast<const u32x4*>(wsrc + (s0 + i < s1 ? s0 + i : s1 - 1) * 64);
+    wq[i] = *reinterpret_cast<const u32x4*>(wsrc + (s0 + i < s1 ? s0 + i : s1 - 1) * wstep);
   __builtin_amdgcn_sched_barrier(0);
   // every activation load and LDS-direct copy of this wave has landed once at most
   // RING loads remain
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(256, KSPLIT == 4 ? 4 : 1) void resident_gemm(GemmPa
           res_fetch<FMT, MT, C::RROWS, C::ALDS>(a_lds, as_lds, ws_lds, KS, astr, j + 1, wrow, r, gq);
       res_mma<FMT, MT>(cur, 0xFFFFFFFFu, wq[i], acc, i % kNAcc);
       const int64_t jn = j + RING < s1 ? j + RING : s1 - 1;
-      wq[i] = *reinterpret_cast<const u32x4*>(wsrc + jn * 64);
+      wq[i] = *reinterpret_cast<const u32x4*>(wsrc + jn * wstep);
       cur = nxt;
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -39,6 +39,11 @@ struct QuantParams {
   uint8_t* scales;          // [M, K/G]
 };
 hipError_t launch_quant(int fmt, const QuantParams& p, hipStream_t s, const char** name);
+// One-time weight preparation: codes [N, K/2] -> the prepared layout of the decode
+// kernels (N % 16 == 0, K % 128 == 0); *bad (zeroed by the caller) set to 1 when a
+// block scale is a NaN code.
+hipError_t launch_prepare(int fmt, const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                          int64_t K, uint8_t* out, int32_t* bad, hipStream_t s);
 
 // ---- block-scaled matmul ----------------------------------------------------------
 struct GemmParams {
@@ -49,7 +54,9 @@ struct GemmParams {
   const uint16_t* a_bf16;
   int64_t lda;
   const int32_t* a_gather;  // optional: source row of virtual row p
-  // weights, one [N, K] matrix per group at these strides
+  // weights, one [N, K] matrix per group at these strides; w_tiled: codes in the
+  // prepared layout (16-row x 128-element blocks in lane order; N % 16 == 0, K % 128 == 0)
+  int w_tiled;
   const uint8_t* w_codes;
   const uint8_t* w_scales;
   int64_t w_estride_codes, w_estride_scales;

@@ -85,6 +85,8 @@ typedef enum { FP4_OUT_BF16 = 0, FP4_OUT_F32 = 1 } fp4_out;
 /* Opt-in: an NVFP4 W4A4 call whose activation scale is refused runs as W4A16 and
  * returns FP4_OK_FELL_BACK_W4A16 instead of FP4_ERR_INPUT_SCALE. */
 #define FP4_FLAG_ALLOW_W4A16_FALLBACK 1u
+/* w_codes are in the prepared layout written by fp4_prepare_weights (see there). */
+#define FP4_FLAG_PREPARED_WEIGHTS 2u
 
 /*
  * Activation quantization (guide §6.1 / §6.4; quantize-inside-the-kernel of §4.3).
@@ -239,6 +241,32 @@ size_t fp4_moe_workspace_size(const fp4_moe_args* a);
 fp4_status fp4_moe_workspace_layout(const fp4_moe_args* a, fp4_moe_layout* layout);
 fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * One-time weight preparation ("vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A Complete
+ * Technical Guide", §4.3: scale factors converted to the MMA layout once, at weight
+ * load; §5.3: the block scales repacked for the dequant kernel).  Repacks the codes of
+ * one weight matrix into the layout the decode kernels stream, and checks its block
+ * scales.
+ *   w_codes [N, K/2], w_scales [N, K/G] (the layout above); N % 16 == 0, K % 128 == 0.
+ *   prepared_codes: out, fp4_prepared_weight_bytes(N, K) = N * K / 2 bytes: blocks of 16
+ *     rows x 128 elements, ordered by row block then K block; inside a block the 16-byte
+ *     piece p = 16 q + r (q < 4, r < 16) holds bytes 16 q .. 16 q + 15 of row r's 64.
+ *     The scales stay in their own layout and are passed to fp4_gemm unchanged.
+ *   check: a caller-owned device int32, overwritten (the validation flag).
+ * Validation: a NaN scale code (NVFP4 e4m3 S.1111.111, MXFP4 e8m0 0xFF) fails with
+ * FP4_ERR_WEIGHT_SCALE.  This call synchronizes `stream` to read the flag (load-time
+ * work: it is not meant for capture); prepared_codes is written either way.
+ * Use: fp4_gemm / fp4_gemm_noalloc with FP4_FLAG_PREPARED_WEIGHTS and the prepared
+ * codes as w_codes, for W4A4 calls with at most 64 activation rows (the decode kernels,
+ * which then read each step of a wave's weights as one contiguous kilobyte); other
+ * calls with the flag fail with FP4_ERR_SHAPE (M, N, K) or FP4_ERR_FORMAT (W4A16, or
+ * together with FP4_FLAG_ALLOW_W4A16_FALLBACK).
+ */
+size_t fp4_prepared_weight_bytes(int64_t N, int64_t K);
+fp4_status fp4_prepare_weights(fp4_format fmt, const uint8_t* w_codes, const uint8_t* w_scales,
+                               int64_t N, int64_t K, uint8_t* prepared_codes, int32_t* check,
+                               void* stream);
 
 /* Pure predicate: 1 if the architecture name (e.g. "gfx950:sramecc+:xnack-") is one
  * this library has kernels for, else 0.  No device access.  Every call above checks

@@ -3,7 +3,9 @@ include/*.h declares, and refuses bad arguments before touching a device.
 
 No call here reaches a kernel: each either fails host-side validation (fake but
 aligned addresses are never dereferenced) or stops at the device check, which on a
-machine without a gfx950 GPU must say FP4_ERR_DEVICE.  Error conventions follow the
+machine without a gfx950 GPU must say FP4_ERR_DEVICE.  Every call that passes
+validation runs only where NO_GPU holds: on a machine with a GPU it would launch a
+kernel on the fake addresses.  Error conventions follow the
 pages' failure modes: "GLM-5.3-Flash on vLLM, on GB10" (a zero activation scale
 must be refused, not computed with) and "vLLM on the NVIDIA DGX Spark (GB10 /
 sm_121): A Complete Technical Guide", §6.3 (unsupported device fails loudly).
@@ -283,7 +285,8 @@ def test_fp8_quantize_validation():
     assert q8(F.FP8_ROWWISE, scales=None) == F.FP4_ERR_NULL                # dynamic modes need scales
     assert q8(F.FP8_MX, codes=A + 8) == F.FP4_ERR_ALIGN
     assert q8(F.FP8_MX, ldx=132) == F.FP4_ERR_ALIGN                        # bf16 stride % 8
-    assert q8(F.FP8_MX, ldx=132, weight=True) != F.FP4_ERR_ALIGN           # fp32 stride % 4
+    if NO_GPU:  # (passes validation: with a GPU it would launch on fake addresses)
+        assert q8(F.FP8_MX, ldx=132, weight=True) == F.FP4_ERR_DEVICE      # fp32 stride % 4
     for bad in (0.0, -2.0, float("inf"), float("nan"), 2.0 ** 101):
         assert q8(F.FP8_PER_TENSOR, s=bad, scales=None) == F.FP4_ERR_INPUT_SCALE
         assert q8(F.FP8_PER_TENSOR, s=bad, scales=None, weight=True) == F.FP4_ERR_WEIGHT_SCALE
@@ -334,8 +337,9 @@ def test_mx_validation():
     assert qa(F.MX_E2M3, x=A + 4) == F.FP4_ERR_ALIGN
     assert qa(F.MX_E2M3, ldx=68) == F.FP4_ERR_ALIGN                       # bf16 stride % 8
     assert qa(F.MX_E2M3, M=0, x=None, c=None, s=None) == F.FP4_OK
-    wq = F.mx_quantize_weight(F.MX_E3M2, A, 4, 64, 68, B, C, check=False)
-    assert wq != F.FP4_ERR_ALIGN                                          # fp32 stride % 4
+    if NO_GPU:  # (passes validation: with a GPU it would launch on fake addresses)
+        wq = F.mx_quantize_weight(F.MX_E3M2, A, 4, 64, 68, B, C, check=False)
+        assert wq == F.FP4_ERR_DEVICE                                     # fp32 stride % 4
     gm = lambda at, wt, **kw: F.mx_gemm(at, wt, kw.get("M", 4), kw.get("N", 8), kw.get("K", 128),
                                         kw.get("ac", A), kw.get("asc", B), C, D,
                                         kw.get("out", 0x50000), kw.get("ldo", 8), kw.get("od", 0),
@@ -350,3 +354,37 @@ def test_mx_validation():
     if NO_GPU:
         assert qa(F.MX_E2M3) == F.FP4_ERR_DEVICE
         assert gm(F.MX_E3M2, F.MX_E2M1) == F.FP4_ERR_DEVICE
+
+
+# ---- one-time weight preparation ("vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A
+# Complete Technical Guide", §4.3 / §5.3: scales converted once at load) -------------
+
+
+def test_prepare_validation():
+    assert F.fp4_prepared_weight_bytes(32, 256) == 32 * 128
+    assert F.fp4_prepared_weight_bytes(30, 256) == 0           # N % 16
+    assert F.fp4_prepared_weight_bytes(32, 192) == 0           # K % 128
+    pw = lambda fmt=F.FP4_MXFP4, N=32, K=256, c=A, s=B, o=C, chk=D: F.fp4_prepare_weights(
+        fmt, c, s, N, K, o, chk, check=False)
+    assert pw(fmt=5) == F.FP4_ERR_FORMAT
+    assert pw(N=24) == F.FP4_ERR_SHAPE
+    assert pw(K=320) == F.FP4_ERR_SHAPE
+    assert pw(chk=None) == F.FP4_ERR_NULL
+    assert pw(o=C + 8) == F.FP4_ERR_ALIGN
+    assert pw(chk=D + 2) == F.FP4_ERR_ALIGN
+    if NO_GPU:
+        assert pw() == F.FP4_ERR_DEVICE
+    P = F.FP4_FLAG_PREPARED_WEIGHTS
+    # prepared weights serve W4A4 calls of at most 64 rows with whole 16-row blocks
+    assert g(F.FP4_MXFP4, F.FP4_W4A16, a_bf16=A, K=128, lda=128, flags=P) == F.FP4_ERR_FORMAT
+    assert g(F.FP4_NVFP4, F.FP4_W4A4, a_codes=A, a_scales=B, K=128,
+             flags=P | F.FP4_FLAG_ALLOW_W4A16_FALLBACK) == F.FP4_ERR_FORMAT
+    assert g(F.FP4_MXFP4, F.FP4_W4A4, a_codes=A, a_scales=B, M=65, K=128, flags=P) == F.FP4_ERR_SHAPE
+    assert g(F.FP4_MXFP4, F.FP4_W4A4, a_codes=A, a_scales=B, N=24, ldo=24, K=128, flags=P) == \
+        F.FP4_ERR_SHAPE
+    assert g(F.FP4_MXFP4, F.FP4_W4A4, a_codes=A, a_scales=B, N=16, ldo=16, K=96, flags=P) == \
+        F.FP4_ERR_SHAPE
+    assert g(F.FP4_MXFP4, F.FP4_W4A4, a_codes=A, a_scales=B, flags=8) == F.FP4_ERR_FORMAT
+    if NO_GPU:
+        assert g(F.FP4_MXFP4, F.FP4_W4A4, a_codes=A, a_scales=B, N=16, ldo=16, K=128, flags=P) == \
+            F.FP4_ERR_DEVICE
