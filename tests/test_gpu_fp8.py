@@ -100,7 +100,14 @@ ACT_SHAPES = [(1, 128), (3, 256), (37, 512), (64, 4096), (2, 6144), (5, 96), (7,
 def test_act_quant_bit_exact(mode, shape):
     M, K = shape
     if K % {"mx": 32, "block": 128}.get(mode, 8):
-        pytest.skip("K is not a multiple of this mode's block (refused on the host)")
+        # K is not a multiple of this mode's block: refused on the host, nothing written
+        xd = torch.zeros((M, K), dtype=torch.bfloat16, device=DEV)
+        codes = torch.full((M, K), 0x5A, dtype=torch.uint8, device=DEV)
+        scales = torch.zeros((M, K // 8 + 1), dtype=torch.float32, device=DEV)
+        st = F.fp8_quantize_act(MODES[mode], xd, M, K, K, 1.0, codes, scales, check=False)
+        assert st == F.FP4_ERR_SHAPE
+        assert bool((codes == 0x5A).all())
+        return
     x = synth.normal((M, K), seed=3, role=synth.ACT, index=M * K)
     x = synth.with_outliers(x, 0.01, 20.0, seed=3, index=M)
     ts = act_tensor_scale(x) if mode == "per_tensor" else 1.0
