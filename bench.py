@@ -32,6 +32,7 @@ and the other workloads ride along as records under "workloads":
   mx-w4a8-decode MX GEMM with FP4 (e2m1) weights and FP8 (e4m3) activations, N=14336,
                  K=4096, M = 1, 8, 32
   mxfp6-prefill  MXFP6 (e2m3) x MXFP6 (e2m3) GEMM, M=8192, N=4096, K=4096
+  w4a16-prefill  NVFP4 W4A16 GEMM (bf16 activations), M=8192, N=4096, K=4096
 
 --workload NAME measures one of them alone (its record becomes the line; used for
 profiling runs).
@@ -75,7 +76,7 @@ def parse():
                    choices=["all", "decode", "w4a16-small", "prefill-nvfp4", "prefill-mxfp4",
                             "moe-nvfp4", "moe-mxfp4", "fp8-decode-mx", "fp8-decode-rowwise",
                             "fp8-prefill-mx", "fp8-prefill-block", "mx-w4a8-decode",
-                            "mxfp6-prefill",
+                            "mxfp6-prefill", "w4a16-prefill",
                             "prefill"])            # (old name of prefill-nvfp4)
     p.add_argument("--tokens", type=int, default=None, help="MoE token count (one)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -663,6 +664,48 @@ def bench_mx_prefill(args, torch, F, copy, ae="e2m3", we="e2m3"):
     return rec
 
 
+def bench_w4a16_prefill(args, torch, F, copy):
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    M, N, K = 8192, 4096, 4096
+    w = synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT)
+    ws2 = float(np.float32(np.abs(w).max()) / np.float32(2688.0))
+    wd = torch.from_numpy(w).to(dev)
+    wc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    wsc = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    F.fp4_quantize_weight(F.FP4_NVFP4, wd, N, K, K, ws2, wc, wsc)
+    del wd
+    a, _ = bf16_tensor(torch, synth.normal((M, K), seed=0, role=synth.ACT, index=3), dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    names = {}
+
+    def gemm(i):
+        F.fp4_gemm(F.FP4_NVFP4, F.FP4_W4A16, M, N, K, a, K, None, None, wc, wsc, ws2, 0.0,
+                   out, N, F.FP4_OUT_BF16, 0, None, 0)
+        names["gemm"] = F.fp4_last_kernel()
+
+    ms, per, wall = measure(torch, gemm, args.steps, args.warmup)
+    kus = kernel_avg_us(torch, gemm, args.steps, 2)
+    flops = 2.0 * M * N * K
+    tf = flops / (kus * 1e-6) / 1e12
+    rec = {
+        "metric": "FP4 W4A16 prefill GEMM TFLOP/s (NVFP4 weights, bf16 activations, M=8192, "
+                  "N=4096, K=4096)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": ms,
+        "dtype": "bf16",
+        "config": {"workload": "NVFP4 W4A16 prefill GEMM, bf16 activations, bf16 out",
+                   "M": M, "N": N, "K": K},
+        "roofline": mfma_roof(tf, PEAK_TFLOPS["bf16"], stored_traffic("w4a16_prefill_nvfp4"),
+                              kernel=names.get("gemm"), algorithmic_flops_per_launch=flops,
+                              avg_launch_us=round(kus, 2)),
+        "samples_ms": [round(x, 6) for x in per], "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_w4a16_prefill()
+    return rec
+
+
 class MoeLayer:
     """One of the two MoE layers on the device: a few experts quantized on the GPU, the
     others seeded row permutations of them (distinct memory, same distribution)."""
@@ -1018,6 +1061,22 @@ def cpu_baseline_mx(ae, we, M, N, K, w_rows=None, prefill=False, target_s=CPU_TA
                       f"{el:.1f} s: activation quantization + float64 dequant + float64 matmul"}
 
 
+def cpu_baseline_w4a16_prefill(target_s=CPU_TARGET_S, rows=64):
+    import numpy as np
+    import synth
+    from oracle import gemm as OG
+    from oracle import quant as OQ
+    M, N, K = 8192, 4096, 4096
+    wc, ws, ws2 = OQ.quantize_weight("nvfp4", synth.normal((N, K), 0.02, seed=0, role=synth.WEIGHT))
+    _, av = synth.bf16_bits(synth.normal((M, K), seed=0, role=synth.ACT, index=3))
+    n, el = _repeat(lambda i: OG.gemm_w4a16("nvfp4", av[i * rows % M:(i * rows % M) + rows], wc,
+                                            ws, ws2), target_s)
+    return {"value": round(2.0 * rows * N * K * n / el / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{rows}-row slices of the 8192 activation rows against the full weight, "
+                      f"{n} repetitions in {el:.1f} s: float64 weight dequant + float64 matmul"}
+
+
 # ---------------------------------------------------------------------------------
 
 
@@ -1090,6 +1149,10 @@ def main():
         records["mx-w4a8-decode"] = bench_mx_decode(args, torch, F, copy)
         torch.cuda.empty_cache()
         log("mx-w4a8-decode done")
+    if wl in ("all", "w4a16-prefill"):
+        records["w4a16-prefill"] = bench_w4a16_prefill(args, torch, F, copy)
+        torch.cuda.empty_cache()
+        log("w4a16-prefill done")
     if wl in ("all", "mxfp6-prefill"):
         records["mxfp6-prefill"] = bench_mx_prefill(args, torch, F, copy)
         torch.cuda.empty_cache()

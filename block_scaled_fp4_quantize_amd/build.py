@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["quant.hip", "gemm.hip", "gemm_tile.hip", "gemm_resident.hip", "moe.hip", "fp8.hip", "mx.hip",
-           "prepare.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_tile.hip", "gemm_resident.hip", "gemm_w4a16.hip",
+           "moe.hip", "fp8.hip", "mx.hip", "prepare.hip", "api.cpp"]
 
 DEVICE_FLAGS = [
     "--offload-arch=gfx950",

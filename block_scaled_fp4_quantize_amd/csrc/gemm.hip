@@ -718,6 +718,8 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   // prepared weights: only the decode kernels (streaming, resident) read that layout
   if (p.w_tiled && (akind != kA_FP4 || p.mblk_expert || p.M > 64 || p.K % kKStep || p.N % 16))
     return hipErrorInvalidValue;
+  // bf16 activations, many rows: the LDS-tiled bf16-MFMA kernel
+  if (akind == kA_BF16 && w4a16_tiled_ok(p)) return launch_gemm_w4a16_tiled(fmt, p, s, name);
   // row blocks of 32 (two 16-row activation tiles); dense problems of at most 16
   // rows, and expert tables of 16-row blocks, use one tile
   const bool one = p.mblk_expert ? p.bm == 16 : p.M <= 16;

@@ -359,3 +359,53 @@ def test_deterministic_canaries_and_two_streams():
     for o1, o2 in outs:
         assert torch.equal(o1, first)
         assert torch.equal(o2, ref2)
+
+
+# W4A16 for many rows (bf16 activations x FP4 weights decoded exactly to bf16): the
+# LDS-tiled bf16-MFMA kernel above 64 rows with K a multiple of 128 ("vLLM on the DGX
+# Spark, the Hard Way: Seven Months of GB10 Field Notes": weight-only checkpoints are
+# what costs prefill).  Ragged rows and columns, one to several stages of K.
+W4A16_TILED = [(65, 256, 128), (130, 300, 512), (257, 520, 1024), (96, 40, 384), (200, 256, 4096)]
+
+
+@pytest.mark.parametrize("shape", W4A16_TILED)
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_w4a16_tiled_shapes(fmt, shape):
+    M, N, K = shape
+    run_and_check(fmt, "w4a16", M, N, K, seed=sum(shape))
+    assert F.fp4_last_kernel() == "w4a16_tile_" + fmt, F.fp4_last_kernel()
+    run_and_check(fmt, "w4a16", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32)
+    # below the tiled kernel's size and for K % 128 != 0 the row-block kernel runs
+    run_and_check(fmt, "w4a16", 64, N, K, seed=1)
+    assert F.fp4_last_kernel().startswith("rowblock_"), F.fp4_last_kernel()
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_w4a16_tiled_strided_activations_and_output(fmt):
+    M, N, K = 150, 264, 640
+    wc, ws, ws2 = weights(fmt, N, K, seed=5)
+    a = synth.normal((M, K + 24), seed=5, role=synth.ACT)
+    ad, av = bf16_dev(a)
+    big = torch.full((M, N + 8), -3.0, dtype=torch.float32, device=DEV)
+    out, st = T.gemm(fmt, "w4a16", to_dev(wc), to_dev(ws), a_bf16=ad[:, :K], weight_scale_2=ws2,
+                     out=big[:, :N])
+    torch.cuda.synchronize()
+    assert st == F.FP4_OK and F.fp4_last_kernel() == "w4a16_tile_" + fmt
+    b = big.cpu().numpy()
+    assert (b[:, N:] == -3.0).all()
+    a_hat = av[:, :K].astype(np.float64)
+    w_hat = dequant(fmt, wc, ws)
+    al = OG.alpha(fmt, OG.W4A16, ws2)
+    check_gemm(b[:, :N].astype(np.float64), al * (a_hat @ w_hat.T), a_hat, w_hat, al, False,
+               what=f"{fmt} w4a16 strided")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_w4a16_prefill_full_size_sampled_rows(fmt):
+    # [8192, 4096] bf16 x [4096, 4096] FP4 weights, bf16 out; 64 sampled rows incl. the
+    # first and the last
+    M, N, K = 8192, 4096, 4096
+    rng = np.random.default_rng(7)
+    rows = np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 62, replace=False)])
+    run_and_check(fmt, "w4a16", M, N, K, seed=7, rows=np.sort(rows))
+    assert F.fp4_last_kernel() == "w4a16_tile_" + fmt
