@@ -684,7 +684,8 @@ hipError_t launch_rowblock(const GemmParams& p, hipStream_t s, const char** name
 int gemm_block_rows(int /*fmt*/, int akind, int64_t rows_per_group, int64_t H, int64_t I) {
   // experts averaging at least 48 rows: 128-row tiles; at most 16: one 16-row tile per
   // block (half the activation decode and MFMA work of a 32-row block); else 32
-  const bool tiled = akind == kA_FP4 && H % kKStep == 0 && I % kKStep == 0;
+  // (fp4 activations: the FP4 tile kernel; bf16 activations: the W4A16 tile kernel)
+  const bool tiled = H % kKStep == 0 && I % kKStep == 0;
   if (tiled && rows_per_group >= 48) return 128;
   return rows_per_group <= 16 ? 16 : 32;
 }
@@ -718,7 +719,7 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   // prepared weights: only the decode kernels (streaming, resident) read that layout
   if (p.w_tiled && (akind != kA_FP4 || p.mblk_expert || p.M > 64 || p.K % kKStep || p.N % 16))
     return hipErrorInvalidValue;
-  // bf16 activations, many rows: the LDS-tiled bf16-MFMA kernel
+  // bf16 activations, many rows (or 128-row expert blocks): the LDS-tiled bf16-MFMA kernel
   if (akind == kA_BF16 && w4a16_tiled_ok(p)) return launch_gemm_w4a16_tiled(fmt, p, s, name);
   // row blocks of 32 (two 16-row activation tiles); dense problems of at most 16
   // rows, and expert tables of 16-row blocks, use one tile

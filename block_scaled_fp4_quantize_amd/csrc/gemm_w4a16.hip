@@ -74,7 +74,20 @@ __global__ __launch_bounds__(512, 1) void w4a16_tile_kernel(GemmParams p) {
   const int64_t ntiles = (p.N + C::BN - 1) / C::BN;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
-  const int64_t row0 = mb * C::BM, K = p.K, nst = K / 128;
+  // dense, or one 128-row block of one expert (grouped MoE GEMMs: the block table gives
+  // the expert and its rows; activation rows may be gathered)
+  int grp = 0;
+  int64_t row0 = mb * C::BM, row_end = p.M;
+  if (p.mblk_expert) {
+    grp = p.mblk_expert[mb];
+    if (grp < 0) return;  // uniform over the workgroup
+    row0 = p.mblk_row0[mb];
+    row_end = p.group_end[grp];
+  }
+  const float alpha = p.alpha_g ? p.alpha_g[grp] : p.alpha;
+  const uint8_t* wcodes = p.w_codes + grp * p.w_estride_codes;
+  const uint8_t* wscales = p.w_scales + grp * p.w_estride_scales;
+  const int64_t K = p.K, nst = K / 128;
   const int64_t KB = K / 2, KS = K / G;
   // the lane's source of each copy of a stage (slot 64 (wave + 8 q) + lane)
   const uint8_t* dsrc[C::CPW];
@@ -84,13 +97,14 @@ __global__ __launch_bounds__(512, 1) void w4a16_tile_kernel(GemmParams p) {
     const int s = 64 * (wave + C::WAVES * q) + lane;
     if (s < C::ASLOTS) {
       const int r = s >> 4, pc = (s & 15) ^ (r & 15);
-      const int64_t m = row0 + r < p.M ? row0 + r : p.M - 1;
+      const int64_t v = row0 + r < row_end ? row0 + r : row_end - 1;
+      const int64_t m = p.a_gather ? (int64_t)p.a_gather[v] : v;
       dsrc[q] = reinterpret_cast<const uint8_t*>(p.a_bf16 + m * p.lda) + 16 * pc;
       dstep[q] = 256;
     } else {
       const int w = s - C::ASLOTS, r = w >> 2, pc = (w & 3) ^ ((r >> 2) & 3);
       const int64_t n = nt * C::BN + r < p.N ? nt * C::BN + r : p.N - 1;
-      dsrc[q] = p.w_codes + n * KB + 16 * pc;
+      dsrc[q] = wcodes + n * KB + 16 * pc;
       dstep[q] = 64;
     }
   }
@@ -102,7 +116,7 @@ __global__ __launch_bounds__(512, 1) void w4a16_tile_kernel(GemmParams p) {
     const int d = (64 * wave + lane) % (C::BN * DPR);
     const int r = d / DPR, j = d % DPR;
     const int64_t n = nt * C::BN + r < p.N ? nt * C::BN + r : p.N - 1;
-    ssrc = p.w_scales + n * KS + 4 * j;
+    ssrc = wscales + n * KS + 4 * j;
   }
   auto issue = [&](int64_t t) {
     uint8_t* buf = wsm + (int)(t % C::NBUF) * C::STAGE;
@@ -172,12 +186,12 @@ __global__ __launch_bounds__(512, 1) void w4a16_tile_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < C::NB; ++i) {
     const int64_t m = row0 + 32 * i + r;
-    if (m >= p.M) continue;
+    if (m >= row_end) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t n = nt * C::BN + wave * 32 + 8 * q + 4 * h;
-      const float x0 = acc[i][4 * q] * p.alpha, x1 = acc[i][4 * q + 1] * p.alpha;
-      const float x2 = acc[i][4 * q + 2] * p.alpha, x3 = acc[i][4 * q + 3] * p.alpha;
+      const float x0 = acc[i][4 * q] * alpha, x1 = acc[i][4 * q + 1] * alpha;
+      const float x2 = acc[i][4 * q + 2] * alpha, x3 = acc[i][4 * q + 3] * alpha;
       if (vec && n + 3 < p.N) {
         if (p.out_f32)
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + m * p.ldo + n) =
@@ -203,12 +217,14 @@ __global__ __launch_bounds__(512, 1) void w4a16_tile_kernel(GemmParams p) {
 }  // namespace
 
 bool w4a16_tiled_ok(const GemmParams& p) {
-  return !p.mblk_expert && !p.a_gather && p.M > 64 && p.K % 128 == 0 && (p.lda % 8) == 0;
+  const bool rows_ok = p.mblk_expert ? p.bm == W16Cfg::BM : (p.M > 64 && !p.a_gather);
+  return rows_ok && p.K % 128 == 0 && (p.lda % 8) == 0;
 }
 
 hipError_t launch_gemm_w4a16_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name) {
   using C = W16Cfg;
-  const int64_t grid = ((p.N + C::BN - 1) / C::BN) * ((p.M + C::BM - 1) / C::BM);
+  const int64_t mblocks = p.mblk_expert ? p.n_mblocks : (p.M + C::BM - 1) / C::BM;
+  const int64_t grid = ((p.N + C::BN - 1) / C::BN) * mblocks;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF || !w4a16_tiled_ok(p)) return hipErrorInvalidConfiguration;
   static std::atomic<uint64_t> lds_nv{0}, lds_mx{0};

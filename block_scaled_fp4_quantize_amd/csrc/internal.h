@@ -93,8 +93,9 @@ bool gemm_can_fuse_swiglu(int fmt, int akind, int64_t M, int64_t K, int64_t I, b
 // Row-block height of the block table for grouped (MoE) GEMMs of these shapes
 // (GEMM1 has K = H, GEMM2 has K = I); launch_gemm picks its kernel from it.
 int gemm_block_rows(int fmt, int akind, int64_t rows_per_group, int64_t H, int64_t I);
-// W4A16 for many rows (dense, bf16 activations, M > 64, K % 128 == 0, lda % 8 == 0):
-// the LDS-tiled bf16-MFMA kernel; w4a16_tiled_ok says whether a GEMM qualifies.
+// W4A16 for many rows (bf16 activations, dense above 64 rows or grouped 128-row expert
+// blocks, K % 128 == 0, lda % 8 == 0): the LDS-tiled bf16-MFMA kernel;
+// w4a16_tiled_ok says whether a GEMM qualifies.
 bool w4a16_tiled_ok(const GemmParams& p);
 hipError_t launch_gemm_w4a16_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name);
 hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,

@@ -356,6 +356,10 @@ SMALL = [
     ("nvfp4", "w4a4", dict(T=60, H=256, I=128, E=8, k=4, shared=False)),
     ("mxfp4", "w4a4", dict(T=40, H=384, I=256, E=16, k=4, shared=True)),
     ("mxfp4", "w4a4", dict(T=1, H=256, I=128, E=8, k=2, shared=False)),
+    # W4A16 experts averaging >= 48 rows, H and I multiples of 128: the grouped GEMMs run on
+    # the W4A16 tile kernel's 128-row blocks
+    ("nvfp4", "w4a16", dict(T=150, H=256, I=128, E=4, k=2, shared=True)),
+    ("mxfp4", "w4a16", dict(T=200, H=384, I=256, E=6, k=3, shared=False)),
 ]
 
 
