@@ -147,17 +147,47 @@ __device__ __forceinline__ void store_block(const Fp8GemmParams& p, const v16f& 
   }
 }
 
+// global -> LDS copies (the address of the LDS destination goes in M0): 16 bytes or 4
+// bytes per lane
+#define FP4_SG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+__device__ __forceinline__ void copy16(const void* g, uint8_t* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)FP4_SG_LDS(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0v), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void copy4(const void* g, uint8_t* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)FP4_SG_LDS(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(m0v), "v"(g) : "memory", "m0");
+}
+constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
 // ---- few activation rows (decode): one workgroup = 32 weight rows x 32 activation rows,
-// its 4 waves splitting K by 128-deep blocks (kb = wave, wave + 4, ...), operands loaded
-// straight from global memory, partial sums added through LDS in wave order (bitwise
-// reproducible).  Weights are read once per 32 activation rows.  (Each 16-byte-per-lane
-// load touches 32 rows' cache lines; 8 waves per workgroup, or two blocks in flight per
-// wave, measured slower: the extra lines in flight outgrow the L1.)
+// its 4 waves splitting K by 128-deep blocks (wave w takes blocks w, w + 4, ...).  Each
+// wave stages its blocks through its own two LDS buffers with global_load_lds copies of
+// whole cache lines (8 rows x 128 bytes, or 16 x 64, per kilobyte), the next block in
+// flight while the current one multiplies; no barrier until the partial sums are added
+// through LDS in wave order (bitwise reproducible).  Weights are read once per 32
+// activation rows.
 constexpr int kRowsWaves = 4;
+
+template <int FA, int FW>
+struct RowsCfg {
+  static constexpr int ASLOTS = 32 * Fmt<FA>::PIECES;     // 16-byte slots of one block
+  static constexpr int WSLOTS = 32 * Fmt<FW>::PIECES;
+  static constexpr int NCA = ASLOTS / 64, NCW = WSLOTS / 64;   // 1 KB copies (2, 3 or 4)
+  static constexpr int BUF = 16 * (ASLOTS + WSLOTS) + 256;     // + the MX scale words
+  static constexpr int RED = (kRowsWaves - 1) * 64 * 64;       // partial sums (v16f)
+  static constexpr int LDS = kRowsWaves * 2 * BUF + RED;
+  static_assert(ASLOTS % 64 == 0 && WSLOTS % 64 == 0, "whole 1 KB copies");
+};
 
 template <int MODE, int FA, int FW>
 __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) {
-  __shared__ v16f red[kRowsWaves - 1][64];
+  using C = RowsCfg<FA, FW>;
+  constexpr bool MX = MODE == kF8_MX;
+  constexpr int OPS = C::NCA + C::NCW + (MX ? 1 : 0);        // copies per block
+  extern __shared__ __attribute__((aligned(16))) uint8_t rsm[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t ntiles = (p.N + 31) / 32;
@@ -166,23 +196,64 @@ __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) 
   const int r = lane & 31, h = lane >> 5;
   const int64_t n = nt * 32 + r, m = mb * 32 + r;
   const int64_t nc = n < p.N ? n : p.N - 1, mc = m < p.M ? m : p.M - 1;
-  const uint8_t* wrow = p.w_codes + nc * (p.K * Fmt<FW>::BITS / 8);
-  const uint8_t* arow = p.a_codes + mc * (p.K * Fmt<FA>::BITS / 8);
+  const int64_t a_rowb = p.K * Fmt<FA>::BITS / 8, w_rowb = p.K * Fmt<FW>::BITS / 8;
   const int64_t nkb = p.K / 128;
   const int one = p.unit_scale;
   // the weight block of these 32 rows (BLOCK): 128-row blocks hold whole 32-row tiles
   const int64_t wblk = (nt * 32) / 128;
+  uint8_t* mybuf = rsm + wave * 2 * C::BUF;
+  // the lane's copy sources: slot 64 c + lane of the activation / weight region
+  const uint8_t* asrc[C::NCA];
+  const uint8_t* wsrc[C::NCW];
+#pragma unroll
+  for (int c = 0; c < C::NCA; ++c) {
+    int rr, pc;
+    piece_of<FA>(64 * c + lane, rr, pc);
+    const int64_t mm = mb * 32 + rr < p.M ? mb * 32 + rr : p.M - 1;
+    asrc[c] = p.a_codes + mm * a_rowb + 16 * pc;
+  }
+#pragma unroll
+  for (int c = 0; c < C::NCW; ++c) {
+    int rr, pc;
+    piece_of<FW>(64 * c + lane, rr, pc);
+    const int64_t nn = nt * 32 + rr < p.N ? nt * 32 + rr : p.N - 1;
+    wsrc[c] = p.w_codes + nn * w_rowb + 16 * pc;
+  }
+  // MX: lanes 0-31 copy the weight rows' e8m0 word of a block, lanes 32-63 the activation
+  // rows' (lane r + 32 h: row r of operand h)
+  const uint8_t* ssrc = MX ? (h == 0 ? p.w_mx + nc * (p.K / 32) : p.a_mx + mc * (p.K / 32)) : nullptr;
+  auto issue = [&](int64_t kb, int slot) {
+    uint8_t* buf = mybuf + slot * C::BUF;
+#pragma unroll
+    for (int c = 0; c < C::NCA; ++c) copy16(asrc[c] + kb * Fmt<FA>::RB, buf + c * 1024);
+#pragma unroll
+    for (int c = 0; c < C::NCW; ++c) copy16(wsrc[c] + kb * Fmt<FW>::RB, buf + 16 * C::ASLOTS + c * 1024);
+    if (MX) copy4(ssrc + kb * 4, buf + 16 * (C::ASLOTS + C::WSLOTS));
+  };
   v16f acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  for (int64_t kb = wave; kb < nkb; kb += kRowsWaves) {
-    const int64_t k0 = kb * 128;
-    const v8i w0 = ld_lane<FW>(wrow, k0, h), w1 = ld_lane<FW>(wrow, k0 + 64, h);
-    const v8i a0 = ld_lane<FA>(arow, k0, h), a1 = ld_lane<FA>(arow, k0 + 64, h);
+  int64_t kb = wave;
+  if (kb < nkb) issue(kb, 0);
+  for (int slot = 0; kb < nkb; kb += kRowsWaves, slot ^= 1) {
+    const int64_t nxt = kb + kRowsWaves;
+    // this wave's LDS reads of the other buffer are done before it is refilled
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (nxt < nkb) {
+      issue(nxt, slot ^ 1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(OPS));    // block kb landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+    }
+    asm volatile("" ::: "memory");
+    const uint8_t* buf = mybuf + slot * C::BUF;
+    const v8i a0 = lds_lane<FA>(buf, r, 0, h), a1 = lds_lane<FA>(buf, r, 1, h);
+    const v8i w0 = lds_lane<FW>(buf + 16 * C::ASLOTS, r, 0, h), w1 = lds_lane<FW>(buf + 16 * C::ASLOTS, r, 1, h);
     int ws0 = one, ws1 = one, as0 = one, as1 = one;
-    if (MODE == kF8_MX) {
-      const uint32_t wsw = *reinterpret_cast<const uint32_t*>(p.w_mx + nc * (p.K / 32) + kb * 4);
-      const uint32_t asw = *reinterpret_cast<const uint32_t*>(p.a_mx + mc * (p.K / 32) + kb * 4);
+    if (MX) {
+      const uint8_t* sw = buf + 16 * (C::ASLOTS + C::WSLOTS);
+      const uint32_t wsw = *reinterpret_cast<const uint32_t*>(sw + 4 * r);
+      const uint32_t asw = *reinterpret_cast<const uint32_t*>(sw + 128 + 4 * r);
       ws0 = (int)((wsw >> (8 * h)) & 0xFFu);
       ws1 = (int)((wsw >> (8 * (2 + h))) & 0xFFu);
       as0 = (int)((asw >> (8 * h)) & 0xFFu);
@@ -203,12 +274,13 @@ __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) 
       acc = mfma<FW, FA>(w1, a1, acc, ws1, as1);
     }
   }
-  if (wave > 0) red[wave - 1][lane] = acc;
+  v16f* red = reinterpret_cast<v16f*>(rsm + kRowsWaves * 2 * C::BUF);
+  if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
   __syncthreads();
   if (wave != 0 || m >= p.M) return;
 #pragma unroll
   for (int wv = 0; wv < kRowsWaves - 1; ++wv) {
-    const v16f o = red[wv][lane];
+    const v16f o = red[wv * 64 + lane];
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] += o[v];
   }
@@ -257,18 +329,6 @@ __device__ __forceinline__ int scale_row(int s) {
   return BM + g * 128 + 32 * (t % 4) + t / 4;
 }
 
-#define FP4_SG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-__device__ __forceinline__ void copy16(const void* g, uint8_t* lds) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)FP4_SG_LDS(lds));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(m0v), "v"(g) : "memory", "m0");
-}
-__device__ __forceinline__ void copy4(const void* g, uint8_t* lds) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)FP4_SG_LDS(lds));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(m0v), "v"(g) : "memory", "m0");
-}
-constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
 template <int MODE, int FA, int FW>
 __global__ __launch_bounds__(512, 1) void tile_kernel(Fp8GemmParams p) {
@@ -453,7 +513,13 @@ hipError_t launch(const Fp8GemmParams& p, hipStream_t s, const char** name, cons
     *name = rows_name;
     const int64_t grid = ((p.N + 31) / 32) * ((p.M + 31) / 32);
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rows_kernel<MODE, FA, FW>), dim3((unsigned)grid), dim3(64 * kRowsWaves), 0, s, p);
+    constexpr int lds = RowsCfg<FA, FW>::LDS;
+    static std::atomic<uint64_t> rows_lds{0};
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rows_kernel<MODE, FA, FW>), lds,
+                                      rows_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((rows_kernel<MODE, FA, FW>), dim3((unsigned)grid), dim3(64 * kRowsWaves), lds,
+                       s, p);
     return hipGetLastError();
   }
   using C = TileCfg<FA, FW>;
