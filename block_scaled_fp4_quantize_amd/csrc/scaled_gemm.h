@@ -186,7 +186,7 @@ template <int MODE, int FA, int FW>
 __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) {
   using C = RowsCfg<FA, FW>;
   constexpr bool MX = MODE == kF8_MX;
-  constexpr int OPS = C::NCA + C::NCW + (MX ? 1 : 0);        // copies per block
+  constexpr int OPS = C::NCA + C::NCW + (MX ? 1 : 0);        // copies per block (all rows)
   extern __shared__ __attribute__((aligned(16))) uint8_t rsm[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -222,10 +222,17 @@ __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) 
   // MX: lanes 0-31 copy the weight rows' e8m0 word of a block, lanes 32-63 the activation
   // rows' (lane r + 32 h: row r of operand h)
   const uint8_t* ssrc = MX ? (h == 0 ? p.w_mx + nc * (p.K / 32) : p.a_mx + mc * (p.K / 32)) : nullptr;
+  // activation copies that hold rows that exist (e4m3 / e2m1 copies hold whole rows: 8
+  // or 16 per kilobyte); the lanes of absent rows read stale LDS, which only reaches
+  // output rows that are not stored
+  constexpr int RPC = FA == kE4M3 ? 8 : (FA == kE2M1 ? 16 : 0);
+  const int64_t mrows = p.M - mb * 32 < 32 ? p.M - mb * 32 : 32;
+  const int nca = RPC ? (int)((mrows + RPC - 1) / RPC) : C::NCA;   // uniform
   auto issue = [&](int64_t kb, int slot) {
     uint8_t* buf = mybuf + slot * C::BUF;
 #pragma unroll
-    for (int c = 0; c < C::NCA; ++c) copy16(asrc[c] + kb * Fmt<FA>::RB, buf + c * 1024);
+    for (int c = 0; c < C::NCA; ++c)
+      if (c < nca) copy16(asrc[c] + kb * Fmt<FA>::RB, buf + c * 1024);
 #pragma unroll
     for (int c = 0; c < C::NCW; ++c) copy16(wsrc[c] + kb * Fmt<FW>::RB, buf + 16 * C::ASLOTS + c * 1024);
     if (MX) copy4(ssrc + kb * 4, buf + 16 * (C::ASLOTS + C::WSLOTS));
@@ -241,7 +248,11 @@ __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) 
     __builtin_amdgcn_s_waitcnt(0xC07F);
     if (nxt < nkb) {
       issue(nxt, slot ^ 1);
-      __builtin_amdgcn_s_waitcnt(vmcnt_enc(OPS));    // block kb landed
+      // block kb landed: at most the next block's copies outstanding
+      if (nca == C::NCA) __builtin_amdgcn_s_waitcnt(vmcnt_enc(OPS));
+      else if (nca == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(OPS - C::NCA + 1));
+      else if (nca == 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(OPS - C::NCA + 2));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_enc(OPS - C::NCA + 3));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
     }
