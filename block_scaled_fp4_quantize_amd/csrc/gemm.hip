@@ -735,9 +735,12 @@ hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
   // at most 16 rows (one 16-row activation tile): activations resident in LDS with
   // a deep weight stream, when they fit; two-tile blocks measure faster on the
   // streaming kernel below, and so do MXFP4 expert tables of 16-row blocks (many
-  // experts with a few rows each: 64 weight rows per workgroup amortize the staging)
+  // experts with a few rows each: 64 weight rows per workgroup amortize the staging),
+  // and short-K NVFP4 expert tables of at most 32 blocks (a few routed tokens: the
+  // resident kernel's per-block staging of the activations is not repaid by K < 1024)
   const bool grouped_mx = p.mblk_expert && fmt == kMX;
-  if (fast && one && !grouped_mx &&
+  const bool few_short = p.mblk_expert && p.K < 1024 && p.n_mblocks <= 32;
+  if (fast && one && !grouped_mx && !few_short &&
       resident_fits(fmt, 1, p.mblk_expert ? 16 : p.M, p.N, p.K, p.mblk_expert ? p.n_mblocks : 1))
     return launch_gemm_resident(fmt, 1, p, s, name);
   if (fast) {
