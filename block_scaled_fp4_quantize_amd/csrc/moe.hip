@@ -503,6 +503,12 @@ __global__ __launch_bounds__(256) void swiglu_kernel(SwigluParams p) {
 }
 
 // ---- combine: out[t] = sum_j w[t,j] * y[inverse[t,j]] (+ shared) -> bf16 ------
+// The k routed rows of a token are fetched eight at a time with every load of a
+// group in flight together (the slot indices first, then the rows at clamped
+// addresses), and added in slot order; a dropped slot (expert id out of range)
+// contributes nothing.
+constexpr int kCombineGroup = 8;
+
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int64_t chunks = p.H / 8;
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -512,15 +518,31 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < p.k; ++j) {
-    const int32_t pos = p.inverse[t * p.k + j];
-    if (pos < 0) continue;  // dropped (expert id out of range)
-    const float wj = p.w[t * p.k + j];
-    const float* yr = p.y + (int64_t)pos * p.H + col;
-    const float4 a = reinterpret_cast<const float4*>(yr)[0];
-    const float4 b = reinterpret_cast<const float4*>(yr)[1];
-    acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
-    acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+  for (int j0 = 0; j0 < p.k; j0 += kCombineGroup) {
+    int32_t pos[kCombineGroup];
+    float wj[kCombineGroup];
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      const int j = j0 + u < p.k ? j0 + u : p.k - 1;
+      pos[u] = p.inverse[t * p.k + j];
+      wj[u] = p.w[t * p.k + j];
+      if (j0 + u >= p.k) pos[u] = -1;
+    }
+    float4 a[kCombineGroup], b[kCombineGroup];
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      const float* yr = p.y + (int64_t)(pos[u] >= 0 ? pos[u] : 0) * p.H + col;
+      a[u] = reinterpret_cast<const float4*>(yr)[0];
+      b[u] = reinterpret_cast<const float4*>(yr)[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      if (pos[u] < 0) continue;
+      acc[0] += wj[u] * a[u].x; acc[1] += wj[u] * a[u].y;
+      acc[2] += wj[u] * a[u].z; acc[3] += wj[u] * a[u].w;
+      acc[4] += wj[u] * b[u].x; acc[5] += wj[u] * b[u].y;
+      acc[6] += wj[u] * b[u].z; acc[7] += wj[u] * b[u].w;
+    }
   }
   if (p.y_shared) {
     const float* yr = p.y_shared + t * p.H + col;
