@@ -83,8 +83,6 @@ struct GemmParams {
   uint8_t* h_scales;      // [rows, I/G]
 };
 enum AKind : int { kA_FP4 = 0, kA_BF16 = 1 };
-// Whether a gate/up GEMM of this shape runs on the tiled kernel, and so can take the
-// fused SwiGLU + requant epilogue (grouped: 128-row blocks; dense: more than 64 rows).
 // Whether a gate/up GEMM of this shape takes the fused SwiGLU + requant epilogue: on
 // the tiled kernel (grouped: 128-row blocks; dense: more than 64 rows), else on the
 // streaming kernel when the plain GEMM would run there too or has at most 16 rows.
