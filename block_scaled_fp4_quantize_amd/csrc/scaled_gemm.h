@@ -162,45 +162,49 @@ __device__ __forceinline__ void copy4(const void* g, uint8_t* lds) {
 }
 constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-// ---- few activation rows (decode): one workgroup = 32 weight rows x 32 activation rows,
-// its 4 waves splitting K by 128-deep blocks (wave w takes blocks w, w + 4, ...).  Each
-// wave stages its blocks through its own two LDS buffers with global_load_lds copies of
-// whole cache lines (8 rows x 128 bytes, or 16 x 64, per kilobyte), the next block in
-// flight while the current one multiplies; no barrier until the partial sums are added
-// through LDS in wave order (bitwise reproducible).  Weights are read once per 32
-// activation rows.
+// ---- few activation rows (decode): one workgroup = 32 NW weight rows x 32 activation
+// rows, its 4 waves splitting K by 128-deep blocks (wave w takes blocks w, w + 4, ...).
+// Each wave stages its blocks (the activation rows and its NW 32-row weight tiles)
+// through its own two LDS buffers with global_load_lds copies of whole cache lines (8
+// rows x 128 bytes, or 16 x 64, per kilobyte), the next block in flight while the
+// current one multiplies; no barrier until the partial sums are added through LDS in
+// wave order (bitwise reproducible).  Weights are read once per 32 activation rows;
+// each staged activation block serves NW weight tiles.
 constexpr int kRowsWaves = 4;
 
-template <int FA, int FW>
+template <int FA, int FW, int NW>
 struct RowsCfg {
   static constexpr int ASLOTS = 32 * Fmt<FA>::PIECES;     // 16-byte slots of one block
-  static constexpr int WSLOTS = 32 * Fmt<FW>::PIECES;
-  static constexpr int NCA = ASLOTS / 64, NCW = WSLOTS / 64;   // 1 KB copies (2, 3 or 4)
-  static constexpr int BUF = 16 * (ASLOTS + WSLOTS) + 256;     // + the MX scale words
-  static constexpr int RED = (kRowsWaves - 1) * 64 * 64;       // partial sums (v16f)
+  static constexpr int WSLOTS = 32 * NW * Fmt<FW>::PIECES;
+  static constexpr int NCA = ASLOTS / 64, NCW = WSLOTS / 64;   // 1 KB copies
+  static constexpr int SW = NW == 1 ? 256 : 512;               // MX scale words
+  static constexpr int BUF = 16 * (ASLOTS + WSLOTS) + SW;
+  static constexpr int RED = (kRowsWaves - 1) * NW * 64 * 64;  // partial sums (v16f)
   static constexpr int LDS = kRowsWaves * 2 * BUF + RED;
   static_assert(ASLOTS % 64 == 0 && WSLOTS % 64 == 0, "whole 1 KB copies");
+  static_assert(NW == 1 || NW == 2, "one or two weight tiles per wave");
 };
 
-template <int MODE, int FA, int FW>
+template <int MODE, int FA, int FW, int NW>
 __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) {
-  using C = RowsCfg<FA, FW>;
+  using C = RowsCfg<FA, FW, NW>;
   constexpr bool MX = MODE == kF8_MX;
-  constexpr int OPS = C::NCA + C::NCW + (MX ? 1 : 0);        // copies per block (all rows)
+  constexpr int OPS = C::NCA + C::NCW + (MX ? NW : 0);       // copies per block (all rows)
+  constexpr int WR = 32 * NW;                                // weight rows per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t rsm[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t ntiles = (p.N + 31) / 32;
+  const int64_t ntiles = (p.N + WR - 1) / WR;
   const int64_t mb = (int64_t)blockIdx.x / ntiles;
   const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
   const int r = lane & 31, h = lane >> 5;
-  const int64_t n = nt * 32 + r, m = mb * 32 + r;
-  const int64_t nc = n < p.N ? n : p.N - 1, mc = m < p.M ? m : p.M - 1;
+  const int64_t m = mb * 32 + r;
+  const int64_t mc = m < p.M ? m : p.M - 1;
   const int64_t a_rowb = p.K * Fmt<FA>::BITS / 8, w_rowb = p.K * Fmt<FW>::BITS / 8;
   const int64_t nkb = p.K / 128;
   const int one = p.unit_scale;
-  // the weight block of these 32 rows (BLOCK): 128-row blocks hold whole 32-row tiles
-  const int64_t wblk = (nt * 32) / 128;
+  // the weight block of these rows (BLOCK): 128-row blocks hold whole 32 NW-row tiles
+  const int64_t wblk = (nt * WR) / 128;
   uint8_t* mybuf = rsm + wave * 2 * C::BUF;
   // the lane's copy sources: slot 64 c + lane of the activation / weight region
   const uint8_t* asrc[C::NCA];
@@ -216,12 +220,26 @@ __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) 
   for (int c = 0; c < C::NCW; ++c) {
     int rr, pc;
     piece_of<FW>(64 * c + lane, rr, pc);
-    const int64_t nn = nt * 32 + rr < p.N ? nt * 32 + rr : p.N - 1;
+    const int64_t nn = nt * WR + rr < p.N ? nt * WR + rr : p.N - 1;
     wsrc[c] = p.w_codes + nn * w_rowb + 16 * pc;
   }
-  // MX: lanes 0-31 copy the weight rows' e8m0 word of a block, lanes 32-63 the activation
-  // rows' (lane r + 32 h: row r of operand h)
-  const uint8_t* ssrc = MX ? (h == 0 ? p.w_mx + nc * (p.K / 32) : p.a_mx + mc * (p.K / 32)) : nullptr;
+  // MX scale words of a block.  One tile: lanes 0-31 copy the weight rows' e8m0 word,
+  // lanes 32-63 the activation rows' (words 0-31 weights, 32-63 activations).  Two
+  // tiles: one copy of the 64 weight rows' words, one of the 32 activation rows'
+  // (lanes 32-63 repeat them into padding): words 0-63 weights, 64-95 activations.
+  const uint8_t* ssrc = nullptr;
+  const uint8_t* ssrc2 = nullptr;
+  if (MX) {
+    if (NW == 1) {
+      const int64_t nc = nt * 32 + r < p.N ? nt * 32 + r : p.N - 1;
+      ssrc = h == 0 ? p.w_mx + nc * (p.K / 32) : p.a_mx + mc * (p.K / 32);
+    } else {
+      const int64_t nl = nt * WR + lane < p.N ? nt * WR + lane : p.N - 1;
+      ssrc = p.w_mx + nl * (p.K / 32);
+      ssrc2 = p.a_mx + mc * (p.K / 32);
+    }
+  }
+  constexpr int AW = NW == 1 ? 128 : 256;   // byte offset of the activation words
   // activation copies that hold rows that exist (e4m3 / e2m1 copies hold whole rows: 8
   // or 16 per kilobyte); the lanes of absent rows read stale LDS, which only reaches
   // output rows that are not stored
@@ -235,11 +253,16 @@ __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) 
       if (c < nca) copy16(asrc[c] + kb * Fmt<FA>::RB, buf + c * 1024);
 #pragma unroll
     for (int c = 0; c < C::NCW; ++c) copy16(wsrc[c] + kb * Fmt<FW>::RB, buf + 16 * C::ASLOTS + c * 1024);
-    if (MX) copy4(ssrc + kb * 4, buf + 16 * (C::ASLOTS + C::WSLOTS));
+    if (MX) {
+      copy4(ssrc + kb * 4, buf + 16 * (C::ASLOTS + C::WSLOTS));
+      if (NW == 2) copy4(ssrc2 + kb * 4, buf + 16 * (C::ASLOTS + C::WSLOTS) + AW);
+    }
   };
-  v16f acc;
+  v16f acc[NW];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int j = 0; j < NW; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
   int64_t kb = wave;
   if (kb < nkb) issue(kb, 0);
   for (int slot = 0; kb < nkb; kb += kRowsWaves, slot ^= 1) {
@@ -259,44 +282,57 @@ __global__ __launch_bounds__(64 * kRowsWaves) void rows_kernel(Fp8GemmParams p) 
     asm volatile("" ::: "memory");
     const uint8_t* buf = mybuf + slot * C::BUF;
     const v8i a0 = lds_lane<FA>(buf, r, 0, h), a1 = lds_lane<FA>(buf, r, 1, h);
-    const v8i w0 = lds_lane<FW>(buf + 16 * C::ASLOTS, r, 0, h), w1 = lds_lane<FW>(buf + 16 * C::ASLOTS, r, 1, h);
-    int ws0 = one, ws1 = one, as0 = one, as1 = one;
+    int as0 = one, as1 = one;
+    const uint8_t* sw = buf + 16 * (C::ASLOTS + C::WSLOTS);
     if (MX) {
-      const uint8_t* sw = buf + 16 * (C::ASLOTS + C::WSLOTS);
-      const uint32_t wsw = *reinterpret_cast<const uint32_t*>(sw + 4 * r);
-      const uint32_t asw = *reinterpret_cast<const uint32_t*>(sw + 128 + 4 * r);
-      ws0 = (int)((wsw >> (8 * h)) & 0xFFu);
-      ws1 = (int)((wsw >> (8 * (2 + h))) & 0xFFu);
+      const uint32_t asw = *reinterpret_cast<const uint32_t*>(sw + AW + 4 * r);
       as0 = (int)((asw >> (8 * h)) & 0xFFu);
       as1 = (int)((asw >> (8 * (2 + h))) & 0xFFu);
     }
-    if (MODE == kF8_BLOCK) {
-      v16f t;
+    // this block's scales (BLOCK: activation row m, the weight block of the tiles)
+    const float bf = MODE == kF8_BLOCK ? p.a_s[mc * nkb + kb] * p.w_s[wblk * nkb + kb] : 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) t[v] = 0.0f;
-      t = mfma<FW, FA>(w0, a0, t, ws0, as0);
-      t = mfma<FW, FA>(w1, a1, t, ws1, as1);
-      // this block's partial sum times its two scales (activation row m, weight block)
-      const float f = p.a_s[mc * nkb + kb] * p.w_s[wblk * nkb + kb];
+    for (int j = 0; j < NW; ++j) {
+      const uint8_t* wreg = buf + 16 * C::ASLOTS;
+      const v8i w0 = lds_lane<FW>(wreg, 32 * j + r, 0, h), w1 = lds_lane<FW>(wreg, 32 * j + r, 1, h);
+      int ws0 = one, ws1 = one;
+      if (MX) {
+        const uint32_t wsw = *reinterpret_cast<const uint32_t*>(sw + 4 * (32 * j + r));
+        ws0 = (int)((wsw >> (8 * h)) & 0xFFu);
+        ws1 = (int)((wsw >> (8 * (2 + h))) & 0xFFu);
+      }
+      if (MODE == kF8_BLOCK) {
+        v16f t;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] += t[v] * f;
-    } else {
-      acc = mfma<FW, FA>(w0, a0, acc, ws0, as0);
-      acc = mfma<FW, FA>(w1, a1, acc, ws1, as1);
+        for (int v = 0; v < 16; ++v) t[v] = 0.0f;
+        t = mfma<FW, FA>(w0, a0, t, ws0, as0);
+        t = mfma<FW, FA>(w1, a1, t, ws1, as1);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] += t[v] * bf;
+      } else {
+        acc[j] = mfma<FW, FA>(w0, a0, acc[j], ws0, as0);
+        acc[j] = mfma<FW, FA>(w1, a1, acc[j], ws1, as1);
+      }
     }
   }
   v16f* red = reinterpret_cast<v16f*>(rsm + kRowsWaves * 2 * C::BUF);
-  if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) red[((wave - 1) * NW + j) * 64 + lane] = acc[j];
+  }
   __syncthreads();
   if (wave != 0 || m >= p.M) return;
-#pragma unroll
-  for (int wv = 0; wv < kRowsWaves - 1; ++wv) {
-    const v16f o = red[wv * 64 + lane];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] += o[v];
-  }
   const float fa = MODE == kF8_ROW ? p.a_s[m] : p.alpha;
-  store_block<MODE>(p, acc, m, nt * 32, h, fa);
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+#pragma unroll
+    for (int wv = 0; wv < kRowsWaves - 1; ++wv) {
+      const v16f o = red[(wv * NW + j) * 64 + lane];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] += o[v];
+    }
+    store_block<MODE>(p, acc[j], m, nt * WR + 32 * j, h, fa);
+  }
 }
 
 // ---- many activation rows (prefill): LDS-tiled -------------------------------------
@@ -517,21 +553,31 @@ __global__ __launch_bounds__(512, 1) void tile_kernel(Fp8GemmParams p) {
   for (int j = 0; j < NA; ++j) store_block<MODE>(p, acc[j], m, nt * C::BN + wrow0 + 32 * j, h, fa);
 }
 
+template <int MODE, int FA, int FW, int NW>
+hipError_t launch_rows(const Fp8GemmParams& p, hipStream_t s) {
+  const int64_t grid = ((p.N + 32 * NW - 1) / (32 * NW)) * ((p.M + 31) / 32);
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  constexpr int lds = RowsCfg<FA, FW, NW>::LDS;
+  static std::atomic<uint64_t> rows_lds{0};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rows_kernel<MODE, FA, FW, NW>), lds,
+                                    rows_lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rows_kernel<MODE, FA, FW, NW>), dim3((unsigned)grid), dim3(64 * kRowsWaves), lds,
+                     s, p);
+  return hipGetLastError();
+}
+
 template <int MODE, int FA, int FW>
 hipError_t launch(const Fp8GemmParams& p, hipStream_t s, const char** name, const char* rows_name,
                   const char* tile_name) {
   if (p.M <= 32) {
     *name = rows_name;
-    const int64_t grid = ((p.N + 31) / 32) * ((p.M + 31) / 32);
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    constexpr int lds = RowsCfg<FA, FW>::LDS;
-    static std::atomic<uint64_t> rows_lds{0};
-    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rows_kernel<MODE, FA, FW>), lds,
-                                      rows_lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((rows_kernel<MODE, FA, FW>), dim3((unsigned)grid), dim3(64 * kRowsWaves), lds,
-                       s, p);
-    return hipGetLastError();
+    // two weight tiles per wave halve the activation staging per weight byte, and the
+    // workgroups: measured faster for MX operands above 16 rows (M = 32: MXFP8 17.7 ->
+    // 16.6 us, FP4 weights x FP8 activations 13.6 -> 12.8 us at N = 14336, K = 4096),
+    // slower with fewer rows (fewer workgroups than CUs) and no faster for rowwise FP8
+    if (MODE == kF8_MX && p.M > 16) return launch_rows<MODE, FA, FW, 2>(p, s);
+    return launch_rows<MODE, FA, FW, 1>(p, s);
   }
   using C = TileCfg<FA, FW>;
   *name = tile_name;

@@ -82,10 +82,12 @@ fp4_status fp8_quantize_weight(fp8_scaling mode, const float* w, int64_t N, int6
  *   (FP4_ERR_FORMAT otherwise) and non-NULL scale arrays.
  *   K must be a positive multiple of 128 (the kernels advance K in 128-deep stages).
  *   M == 0 or N == 0 is a valid no-op.
- * Kernels: M <= 32 a direct-load kernel, 32 x 32 outputs per workgroup, K split over its
- * four waves; larger M an LDS-tiled kernel, 128 x 256 outputs per workgroup.  Both run on
- * the gfx950 scaled 32x32x64 MFMA with e4m3 operands (MX: the e8m0 codes are the
- * instruction's block scales; the other modes apply their fp32 scales outside it).
+ * Kernels: M <= 32 a decode kernel, 32 activation rows x 32 weight rows per workgroup
+ * (64 weight rows for MX operands above 16 rows), K split over its four waves, each
+ * staging its K blocks through LDS; larger M an LDS-tiled kernel, 128 x 256 outputs per
+ * workgroup.  Both run on the gfx950 scaled 32x32x64 MFMA with e4m3 operands (MX: the
+ * e8m0 codes are the instruction's block scales; the other modes apply their fp32 scales
+ * outside it).
  * Pointers must be 16-byte aligned (FP4_ERR_ALIGN).
  */
 fp4_status fp8_gemm(fp8_scaling mode, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,

@@ -67,10 +67,11 @@ fp4_status mx_quantize_weight(mx_elem t, const float* w, int64_t N, int64_t K, i
  * (nearest even) or fp32 with row stride ldo >= N.  MX formats carry no per-tensor scale.
  * K must be a positive multiple of 128 (the kernels advance K in 128-deep stages); M == 0
  * or N == 0 is a valid no-op; pointers must be 16-byte aligned (FP4_ERR_ALIGN).
- * Kernels: M <= 32 a direct-load kernel, 32 x 32 outputs per workgroup, K split over its
- * four waves; larger M an LDS-tiled kernel, 128 x 256 outputs per workgroup.  Both run on
- * the gfx950 scaled 32x32x64 MFMA, which takes each operand's element type and e8m0
- * block scales natively.
+ * Kernels: M <= 32 a decode kernel, 32 activation rows x 32 weight rows per workgroup
+ * (64 weight rows for MX operands above 16 rows), K split over its four waves, each
+ * staging its K blocks through LDS; larger M an LDS-tiled kernel, 128 x 256 outputs per
+ * workgroup.  Both run on the gfx950 scaled 32x32x64 MFMA, which takes each operand's
+ * element type and e8m0 block scales natively.
  */
 fp4_status mx_gemm(mx_elem a_t, mx_elem w_t, int64_t M, int64_t N, int64_t K,
                    const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
