@@ -360,6 +360,10 @@ SMALL = [
     # the W4A16 tile kernel's 128-row blocks
     ("nvfp4", "w4a16", dict(T=150, H=256, I=128, E=4, k=2, shared=True)),
     ("mxfp4", "w4a16", dict(T=200, H=384, I=256, E=6, k=3, shared=False)),
+    # more than 8 experts per token: the combine adds a token's slots in groups of 8,
+    # the last one partial
+    ("nvfp4", "w4a4", dict(T=7, H=128, I=64, E=24, k=12, shared=True)),
+    ("mxfp4", "w4a4", dict(T=5, H=128, I=64, E=32, k=20, shared=False)),
 ]
 
 
@@ -417,6 +421,7 @@ def test_zero_activation_scale_rejected_not_zeroed():
     ("mxfp4", dict(T=200, H=256, I=64, E=16, k=8)),
     ("nvfp4", dict(T=20, H=256, I=128, E=8, k=4)),     # streaming fused SwiGLU
     ("mxfp4", dict(T=9, H=384, I=128, E=8, k=2)),
+    ("nvfp4", dict(T=6, H=128, I=64, E=16, k=12)),     # two combine groups of slots
 ])
 def test_moe_dropped_ids(fmt, kw):
     # expert ids outside [0, E) (device data, not checked on the host) drop their slot:
