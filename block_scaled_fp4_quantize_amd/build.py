@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libfp4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["quant.hip", "gemm.hip", "gemm_tile.hip", "gemm_resident.hip", "gemm_w4a16.hip",
-           "moe.hip", "fp8.hip", "mx.hip", "prepare.hip", "api.cpp"]
+           "moe.hip", "moe_small.hip", "fp8.hip", "mx.hip", "prepare.hip", "api.cpp"]
 
 DEVICE_FLAGS = [
     "--offload-arch=gfx950",

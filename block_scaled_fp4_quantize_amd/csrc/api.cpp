@@ -575,6 +575,35 @@ fp4_status fp4_moe_grouped_gemm(const fp4_moe_args* a, void* workspace, size_t w
   int32_t* src_token = reinterpret_cast<int32_t*>(ws + pl.src_token);
   int32_t* mblk_expert = reinterpret_cast<int32_t*>(ws + pl.mblk_expert);
   int32_t* mblk_row0 = reinterpret_cast<int32_t*>(ws + pl.mblk_row0);
+  // a few routed slots of an NVFP4 W4A4 layer without a shared expert: the whole
+  // layer in two launches (the workspace rows it writes are the ones below)
+  if (nv && w4a4 && !pl.shared && pl.fuse_routed &&
+      fp4::moe_small_fits(T, a->k, E, H, I)) {
+    fp4::MoeSmallParams q{};
+    q.T = T;
+    q.H = H;
+    q.I = I;
+    q.E = E;
+    q.k = a->k;
+    q.hidden = static_cast<const uint16_t*>(a->hidden_bf16);
+    q.ids = a->topk_ids;
+    q.w = a->topk_w;
+    q.w13_codes = a->w13_codes;
+    q.w13_scales = a->w13_scales;
+    q.w2_codes = a->w2_codes;
+    q.w2_scales = a->w2_scales;
+    q.expert_offsets = offsets;
+    q.sorted_rows = sorted_rows;
+    q.inverse = inverse;
+    q.x_codes = ws + pl.L.x_codes;
+    q.x_scales = ws + pl.L.x_scales;
+    q.h_codes = ws + pl.L.h_codes;
+    q.h_scales = ws + pl.L.h_scales;
+    q.y = reinterpret_cast<float*>(ws + pl.L.y);
+    q.out = static_cast<uint16_t*>(a->out_bf16);
+    FP4_TRY(fp4::launch_moe_small(q, h.data(), s, &name));
+    return ok_status;
+  }
   {
     fp4::PermuteParams pp{};
     pp.ids = a->topk_ids;

@@ -226,4 +226,32 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s, const char** na
 hipError_t launch_upload_floats(float* dst, const float* host_vals, int64_t n,
                                 hipStream_t s);
 
+// ---- a whole NVFP4 W4A4 MoE layer for a few routed slots (moe_small.hip) ----------
+// Two launches: gate/up with routing, activation quantization and SwiGLU + requant;
+// down projection with the weighted combine.  The workspace rows named here are
+// written as the general path writes them (sorted positions).
+constexpr int kSmallSlots = 32;     // routed slots T k, at most
+constexpr int kSmallTokens = 4;     // tokens, at most
+constexpr int64_t kSmallMaxH = 4096;
+constexpr int64_t kSmallMaxI = 2048;
+struct MoeSmallParams {
+  int64_t T, H, I, E;
+  int k;
+  const uint16_t* hidden;          // bf16 [T, H]
+  const int32_t* ids;              // [T, k]
+  const float* w;                  // [T, k]
+  const uint8_t *w13_codes, *w13_scales, *w2_codes, *w2_scales;
+  int32_t* expert_offsets;         // [E + 1]
+  int32_t* sorted_rows;            // [T k]
+  int32_t* inverse;                // [T k]
+  uint8_t *x_codes, *x_scales;     // [T k, H/2], [T k, H/16] at sorted positions
+  uint8_t *h_codes, *h_scales;     // [T k, I/2], [T k, I/16]
+  float* y;                        // [T k, H]
+  uint16_t* out;                   // bf16 [T, H]
+};
+bool moe_small_fits(int64_t T, int k, int64_t E, int64_t H, int64_t I);
+// scal_host: the 4 E per-expert scalars g13, alpha13, g2, alpha2
+hipError_t launch_moe_small(const MoeSmallParams& p, const float* scal_host, hipStream_t s,
+                            const char** name);
+
 }  // namespace fp4

@@ -190,6 +190,12 @@ fp4_status fp4_moe_topk_softmax(const float* logits, int64_t T, int64_t E, int k
  * Expert ids are device data and are not checked on the host: a slot whose id lies
  * outside [0, E) (e.g. the router's output for a token with NaN logits) is dropped
  * -- it contributes nothing to out[t] -- and every kernel stays inside its buffers.
+ * Launches: an NVFP4 W4A4 layer without a shared expert, with at most 4 tokens and 32
+ * routed slots (H and I multiples of 128, H <= 4096, I <= 2048, E <= 192), runs in two
+ * launches (gate/up with the routing and the activation quantization inside, then the
+ * down projection with the weighted combine); other layers run dispatch, the two
+ * expert GEMMs and the combine as separate launches.  Both write the workspace stages
+ * below the same way.
  */
 typedef struct {
   fp4_format fmt;
@@ -234,7 +240,8 @@ typedef struct {
                              of 128; on the tiled kernel -- 128-row expert blocks, or more
                              than 64 tokens for the shared expert -- or on the streaming
                              kernel where the plain GEMM would stream too or has at most
-                             16 rows); their h is written without gu */
+                             16 rows, or in the two-launch small layer); their h is
+                             written without gu */
 } fp4_moe_layout;
 
 size_t fp4_moe_workspace_size(const fp4_moe_args* a);

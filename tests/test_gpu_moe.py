@@ -360,6 +360,15 @@ SMALL = [
     # the W4A16 tile kernel's 128-row blocks
     ("nvfp4", "w4a16", dict(T=150, H=256, I=128, E=4, k=2, shared=True)),
     ("mxfp4", "w4a16", dict(T=200, H=384, I=256, E=6, k=3, shared=False)),
+    # NVFP4 W4A4 with at most 4 tokens and 32 routed slots and no shared expert: the
+    # two-launch layer (gate/up with routing and activation quantization; down projection
+    # with the weighted combine), incl. its longer-K variants (H > 2048, I > 1024)
+    ("nvfp4", "w4a4", dict(T=1, H=256, I=128, E=8, k=2, shared=False)),
+    ("nvfp4", "w4a4", dict(T=3, H=384, I=256, E=16, k=8, shared=False)),
+    ("nvfp4", "w4a4", dict(T=2, H=128, I=128, E=20, k=16, shared=False)),
+    ("nvfp4", "w4a4", dict(T=4, H=256, I=128, E=9, k=8, shared=False)),
+    ("nvfp4", "w4a4", dict(T=2, H=4096, I=256, E=4, k=2, shared=False)),
+    ("nvfp4", "w4a4", dict(T=1, H=256, I=2048, E=4, k=3, shared=False)),
     # more than 8 experts per token: the combine adds a token's slots in groups of 8,
     # the last one partial
     ("nvfp4", "w4a4", dict(T=7, H=128, I=64, E=24, k=12, shared=True)),
@@ -422,12 +431,16 @@ def test_zero_activation_scale_rejected_not_zeroed():
     ("nvfp4", dict(T=20, H=256, I=128, E=8, k=4)),     # streaming fused SwiGLU
     ("mxfp4", dict(T=9, H=384, I=128, E=8, k=2)),
     ("nvfp4", dict(T=6, H=128, I=64, E=16, k=12)),     # two combine groups of slots
+    ("nvfp4", dict(T=3, H=256, I=128, E=8, k=4, shared=False)),   # the two-launch small layer
 ])
 def test_moe_dropped_ids(fmt, kw):
     # expert ids outside [0, E) (device data, not checked on the host) drop their slot:
     # it contributes nothing, and the passes that walk every sorted position stay in
-    # bounds.  Token 0 has every slot dropped and gets only the shared expert.
-    pb = MoeProblem(fmt, "w4a4", seed=kw["T"] + 11, shared=True, **kw)
+    # bounds.  Token 0 has every slot dropped and gets only the shared expert (zero
+    # without one).
+    kw = dict(kw)
+    shared = kw.pop("shared", True)
+    pb = MoeProblem(fmt, "w4a4", seed=kw["T"] + 11, shared=shared, **kw)
     rng = np.random.default_rng(12)
     ids = pb.ids.copy()
     drop = rng.random(ids.shape) < 0.2
