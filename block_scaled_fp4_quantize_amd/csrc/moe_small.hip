@@ -216,11 +216,14 @@ __global__ __launch_bounds__(512) void moe_small_down_nv(MoeSmallParams p, Small
 #pragma unroll
   for (int x = 0; x < kSmallTokens; ++x) tok[x] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int s = wave; s < n; s += WAVES) {
-    const int pos = p.inverse[s];   // the gate/up launch's routing (-1: dropped)
-    if (pos < 0) continue;          // uniform per wave
+    // the slot's expert, sorted position (the gate/up launch's routing; -1: dropped)
+    // and weight, fetched together
     const int e = p.ids[s];
+    const int pos = p.inverse[s];
+    float wt = p.w[s];
+    asm volatile("" : "+v"(wt));    // (keeps the three loads ahead of the branch)
+    if (pos < 0 || e < 0 || e >= E) continue;   // dropped slot (uniform per wave)
     const int t = s / p.k;
-    const float wt = p.w[s];
     const float alpha2 = pk.v[3 * E + e];
     const uint8_t* wrow = p.w2_codes + e * H * (I / 2) + (n0 + r) * (I / 2) + gq * 16;
     const uint8_t* wsrow = p.w2_scales + e * H * (I / 16) + (n0 + r) * (I / 16) + 2 * gq;
