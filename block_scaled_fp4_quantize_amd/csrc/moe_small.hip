@@ -34,14 +34,14 @@ struct SmallPack {
 
 // Routing of the few slots inside one wave: lane j < n holds slot j's expert id (-1
 // outside [0, E)).  A slot's sorted position is the number of routed slots before it in
-// expert order, slots of one expert in slot order (the general dispatch's order).
-__device__ __forceinline__ int small_ids(const MoeSmallParams& p, int n, int lane) {
-  int e = -1;
-  if (lane < n) {
-    e = p.ids[lane];
-    if (e < 0 || e >= p.E) e = -1;
-  }
-  return e;
+// expert order, slots of one expert in slot order (the general dispatch's order).  The
+// load is branch-free and its check separate, so that other loads can be issued between
+// the two.
+__device__ __forceinline__ int small_ids_load(const MoeSmallParams& p, int n, int lane) {
+  return p.ids[lane < n ? lane : 0];
+}
+__device__ __forceinline__ int small_ids_check(int raw, int n, int lane, int64_t E) {
+  return lane < n && raw >= 0 && raw < E ? raw : -1;
 }
 __device__ __forceinline__ int small_pos(int ej, int lane, int s, int es) {
   const bool before = ej >= 0 && (ej < es || (ej == es && lane < s));
@@ -55,8 +55,7 @@ template <int SMAX>
 __global__ __launch_bounds__(512) void moe_small_gateup_nv(MoeSmallParams p, SmallPack pk) {
   // the quantized row, decoded exactly to fp16 (its MFMA operand, shared by all lanes)
   __shared__ __attribute__((aligned(16))) _Float16 x16[kSmallMaxH];
-  __shared__ v4f khalf[4][64];  // the second K half's partial tiles
-  __shared__ float gu_l[64];    // gate columns 0..31, up columns 32..63 (times alpha13)
+  __shared__ float kp[2][4][16];   // [K half][row group][column]: the partial dot products
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -67,11 +66,14 @@ __global__ __launch_bounds__(512) void moe_small_gateup_nv(MoeSmallParams p, Sma
   const int nt = (int)(blockIdx.x - (int64_t)s * ntiles);
   const int64_t t = s / p.k;
   // loads first, in the order they are needed: the token's hidden row (known from the
-  // block index), this slot's expert id, that expert's weight rows, all slots' ids
+  // block index), all slots' ids, this slot's expert id, that expert's weight rows.
+  // Loads complete in issue order, so the routing and the quantization below wait for
+  // the first two only and run while the weights stream in.
   const uint16_t* xrow = p.hidden + t * H;
   const int64_t nch = H / 8;   // 8-element chunks of the row; thread tid takes chunk tid
   float xv[8];
   load8<uint16_t>(xrow + (tid < nch ? tid : nch - 1) * 8, xv);   // (past the row: its last)
+  const int ej_raw = small_ids_load(p, n, lane);
   int e = p.ids[s];
   e = (e >= 0 && e < E) ? e : -1;
   const int r = lane & 15, gq = lane >> 4;
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(512) void moe_small_gateup_nv(MoeSmallParams p, Sma
     wq[i] = *reinterpret_cast<const uint4*>(wrow + st * 64);
     wsb[i] = *reinterpret_cast<const uint16_t*>(wsrow + st * 8);
   }
-  const int ej = small_ids(p, n, lane);
   __builtin_amdgcn_sched_barrier(0);
+  const int ej = small_ids_check(ej_raw, n, lane, E);
 
   const int pos = small_pos(ej, lane, s, e);   // uniform; meaningful when e >= 0
   if (nt == 0 && wave == 0) {
@@ -169,41 +171,41 @@ __global__ __launch_bounds__(512) void moe_small_gateup_nv(MoeSmallParams p, Sma
   }
   v4f sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   asm volatile("" : "+v"(sum));
-  if (kh == 1) khalf[rg][lane] = sum;
-  __syncthreads();
-  if (kh == 0 && r == 0) {
-    // lane (row r, gq) holds columns 4 gq .. + 3 of the group's 16
-    sum += khalf[rg][lane];
+  // lane (row r, gq) holds columns 4 gq .. + 3 of the group's 16 (every r alike)
+  if (r == 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) gu_l[(rg >> 1) * 32 + (rg & 1) * 16 + 4 * gq + v] = sum[v] * alpha13;
+    for (int v = 0; v < 4; ++v) kp[kh][rg][4 * gq + v] = sum[v];
   }
   __syncthreads();
-  // SwiGLU + requant under g2: lanes 0-3 of wave 0 take 8 h columns each (a 16-column
-  // block across a lane pair), the arithmetic of the SwiGLU epilogues
-  if (tid < 4) {
-    float h[8];
-    float amax = 0.0f;
+  // SwiGLU + requant under g2, the arithmetic of the SwiGLU epilogues: lane c < 32 of
+  // wave 0 takes h column nt * 32 + c; a 16-column block is 16 lanes, a code byte a
+  // lane pair
+  if (tid < 32) {
+    const int c = tid & 15, b = tid >> 4;
+    const float g = (kp[0][b][c] + kp[1][b][c]) * alpha13;
+    const float u = (kp[0][2 + b][c] + kp[1][2 + b][c]) * alpha13;
+    const float h = swiglu1(g, u);
+    float amax = fabsf(h);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      h[i] = swiglu1(gu_l[8 * tid + i], gu_l[32 + 8 * tid + i]);
-      amax = fmaxf(amax, fabsf(h[i]));
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
     float rq;
     const uint32_t sc = q_nv_scale(amax, g2, &rq);
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) packed |= q_nv_pack2(h[2 * i], h[2 * i + 1], rq) << (8 * i);
-    *reinterpret_cast<uint32_t*>(p.h_codes + (int64_t)pos * (I / 2) + nt * 16 + tid * 4) = packed;
-    if ((tid & 1) == 0) p.h_scales[(int64_t)pos * (I / 16) + nt * 2 + tid / 2] = (uint8_t)sc;
+    const float h1 = __shfl_xor(h, 1);
+    if ((tid & 1) == 0)
+      p.h_codes[(int64_t)pos * (I / 2) + nt * 16 + tid / 2] = (uint8_t)q_nv_pack2(h, h1, rq);
+    if (c == 0) p.h_scales[(int64_t)pos * (I / 16) + nt * 2 + b] = (uint8_t)sc;
   }
 }
 
-// down projection + weighted combine; K-steps of 128: S <= SMAX
+// down projection + weighted combine; K-steps of 128: S <= SMAX.  A wave decodes its
+// slot's h row once, exactly to fp16, into its own LDS row (8-element chunks q = lane,
+// lane + 64, ..), and every lane reads its MFMA operand from there.
 template <int SMAX>
 __global__ __launch_bounds__(512) void moe_small_down_nv(MoeSmallParams p, SmallPack pk) {
   constexpr int WAVES = 8;
+  constexpr int HR = (SMAX * 16 + 63) / 64;   // h chunks per lane
   __shared__ float part[WAVES][kSmallTokens][16];
+  __shared__ __attribute__((aligned(16))) _Float16 hrow[WAVES][SMAX * 128];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -227,19 +229,29 @@ __global__ __launch_bounds__(512) void moe_small_down_nv(MoeSmallParams p, Small
     const float alpha2 = pk.v[3 * E + e];
     const uint8_t* wrow = p.w2_codes + e * H * (I / 2) + (n0 + r) * (I / 2) + gq * 16;
     const uint8_t* wsrow = p.w2_scales + e * H * (I / 16) + (n0 + r) * (I / 16) + 2 * gq;
-    const uint8_t* arow = p.h_codes + (int64_t)pos * (I / 2) + gq * 16;
-    const uint8_t* asrow = p.h_scales + (int64_t)pos * (I / 16) + 2 * gq;
-    uint4 wq[SMAX], aq[SMAX];
-    uint32_t wsb[SMAX], asb[SMAX];
+    const uint8_t* arow = p.h_codes + (int64_t)pos * (I / 2);
+    const uint8_t* asrow = p.h_scales + (int64_t)pos * (I / 16);
+    uint4 wq[SMAX];
+    uint32_t wsb[SMAX], hc[HR], hs[HR];
+#pragma unroll
+    for (int j = 0; j < HR; ++j) {   // (chunks past the row: its last, not stored)
+      const int q = lane + 64 * j < S * 16 ? lane + 64 * j : S * 16 - 1;
+      hc[j] = *reinterpret_cast<const uint32_t*>(arow + q * 4);
+      hs[j] = asrow[q / 2];
+    }
 #pragma unroll
     for (int st = 0; st < SMAX; ++st) {
       const int sc = st < S ? st : S - 1;
       wq[st] = *reinterpret_cast<const uint4*>(wrow + sc * 64);
       wsb[st] = *reinterpret_cast<const uint16_t*>(wsrow + sc * 8);
-      aq[st] = *reinterpret_cast<const uint4*>(arow + sc * 64);
-      asb[st] = *reinterpret_cast<const uint16_t*>(asrow + sc * 8);
     }
     __builtin_amdgcn_sched_barrier(0);
+    _Float16* hw = hrow[wave];
+#pragma unroll
+    for (int j = 0; j < HR; ++j)
+      if (lane + 64 * j < S * 16)
+        *reinterpret_cast<f16x8*>(hw + (lane + 64 * j) * 8) = decode8_f16(hc[j], f16_bcast(e4m3_pair_f16(hs[j]), 0));
+    __builtin_amdgcn_wave_barrier();   // the row is the wave's own: LDS keeps its order
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -248,11 +260,12 @@ __global__ __launch_bounds__(512) void moe_small_down_nv(MoeSmallParams p, Small
       const uint32_t keep = st < S ? 0xFFFFFFFFu : 0u;
       const uint4 wj = make_uint4(wq[st].x & keep, wq[st].y & keep, wq[st].z & keep, wq[st].w & keep);
       const f16x2 wsp = e4m3_pair_f16(wsb[st]);
-      const f16x2 asp = e4m3_pair_f16(asb[st]);
+      const int sa = st < S ? st : 0;
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         const f16x8 wop = decode8_f16(dword_of(wj, sub), f16_bcast(wsp, sub >> 1));
-        const f16x8 aop = decode8_f16(dword_of(aq[st], sub), f16_bcast(asp, sub >> 1));
+        // elements 128 sa + 32 gq + 8 sub .. + 7 of the h row
+        const f16x8 aop = *reinterpret_cast<const f16x8*>(hw + sa * 128 + gq * 32 + sub * 8);
         acc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc[sub], 0, 0, 0);
       }
     }
@@ -296,17 +309,31 @@ hipError_t launch_moe_small(const MoeSmallParams& p, const float* scal_host, hip
   for (int i = 0; i < kSmallPack; ++i) pk.v[i] = i < 4 * p.E ? scal_host[i] : 0.0f;
   const int64_t n = p.T * p.k;
   *name = "moe_small_gateup_nvfp4";
+  // K-steps per wave, the smallest instance that covers them: half of H / 128 for
+  // gate/up, I / 128 for down (steps past them are masked, not skipped)
   const dim3 g1((unsigned)(n * (p.I / 32)));
-  if (p.H <= 2048)   // K-steps per wave: half of H / 128
+  const int64_t s1 = p.H / 256 + (p.H % 256 ? 1 : 0);
+  if (s1 <= 4)
+    hipLaunchKernelGGL(moe_small_gateup_nv<4>, g1, dim3(512), 0, s, p, pk);
+  else if (s1 <= 8)
     hipLaunchKernelGGL(moe_small_gateup_nv<8>, g1, dim3(512), 0, s, p, pk);
+  else if (s1 <= 12)
+    hipLaunchKernelGGL(moe_small_gateup_nv<12>, g1, dim3(512), 0, s, p, pk);
   else
     hipLaunchKernelGGL(moe_small_gateup_nv<16>, g1, dim3(512), 0, s, p, pk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   *name = "moe_small_down_nvfp4";
   const dim3 g2((unsigned)(p.H / 16));
-  if (p.I <= 1024)
+  const int64_t s2 = p.I / 128;
+  if (s2 <= 4)
+    hipLaunchKernelGGL(moe_small_down_nv<4>, g2, dim3(512), 0, s, p, pk);
+  else if (s2 <= 6)
+    hipLaunchKernelGGL(moe_small_down_nv<6>, g2, dim3(512), 0, s, p, pk);
+  else if (s2 <= 8)
     hipLaunchKernelGGL(moe_small_down_nv<8>, g2, dim3(512), 0, s, p, pk);
+  else if (s2 <= 12)
+    hipLaunchKernelGGL(moe_small_down_nv<12>, g2, dim3(512), 0, s, p, pk);
   else
     hipLaunchKernelGGL(moe_small_down_nv<16>, g2, dim3(512), 0, s, p, pk);
   return hipGetLastError();
