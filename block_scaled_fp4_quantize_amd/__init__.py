@@ -47,6 +47,7 @@ GROUP = {FP4_NVFP4: 16, FP4_MXFP4: 32}
 
 EXPORTED = [
     "fp4_quantize_act", "fp4_quantize_weight", "fp4_gemm", "fp4_gemm_workspace_size",
+    "fp4_gemm_workspace_size_mnk",
     "fp4_gemm_noalloc", "fp4_prepared_weight_bytes", "fp4_prepare_weights",
     "fp4_moe_topk_softmax", "fp4_moe_workspace_size", "fp4_moe_workspace_layout",
     "fp4_moe_grouped_gemm", "fp4_arch_supported", "fp4_status_str", "fp4_last_kernel",
@@ -130,6 +131,8 @@ _c = {
     "fp4_prepared_weight_bytes": _proto("fp4_prepared_weight_bytes", _sz, [_i64, _i64]),
     "fp4_prepare_weights": _proto("fp4_prepare_weights", _int, [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "fp4_gemm_workspace_size": _proto("fp4_gemm_workspace_size", _sz, [_int, _int, _i64, _i64, _int]),
+    "fp4_gemm_workspace_size_mnk": _proto("fp4_gemm_workspace_size_mnk", _sz,
+                                          [_int, _int, _i64, _i64, _i64, _int]),
     "fp4_moe_topk_softmax": _proto("fp4_moe_topk_softmax", _int, [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "fp4_moe_workspace_size": _proto("fp4_moe_workspace_size", _sz, [ctypes.POINTER(MoeArgs)]),
     "fp4_moe_workspace_layout": _proto("fp4_moe_workspace_layout", _int,
@@ -219,6 +222,11 @@ def fp4_quantize_weight(fmt, w, N, K, ldw, weight_scale_2, codes, scales, stream
 
 def fp4_gemm_workspace_size(fmt, mode, M, K, has_a_bf16):
     return _c["fp4_gemm_workspace_size"](_fmt(fmt), _mode(mode), M, K, int(bool(has_a_bf16)))
+
+
+def fp4_gemm_workspace_size_mnk(fmt, mode, M, N, K, has_a_bf16):
+    return _c["fp4_gemm_workspace_size_mnk"](_fmt(fmt), _mode(mode), M, N, K,
+                                             int(bool(has_a_bf16)))
 
 
 def fp4_gemm(fmt, mode, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scales,

@@ -67,6 +67,13 @@ fp4_status launched(hipError_t e, const char* name) {
 size_t gemm_ws_bytes(int fmt, int64_t M, int64_t K) {
   return align256((size_t)M * (size_t)(K / 2)) + align256((size_t)M * (size_t)(K / group_of(fmt)));
 }
+// The stage-ordered block scales of both operands, for W4A4 GEMMs that run on the
+// 256 x 256 tile kernel (0 otherwise).
+size_t gemm_relayout_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  const int ifmt = fmt == FP4_NVFP4 ? fp4::kNV : fp4::kMX;
+  if (!fp4::gemm_big_tile(ifmt, M, N, K)) return 0;
+  return align256(fp4::scale_relayout_bytes(ifmt, M, K)) + align256(fp4::scale_relayout_bytes(ifmt, N, K));
+}
 
 // ---- MoE workspace layout ----------------------------------------------------------
 struct MoePlan {
@@ -282,6 +289,13 @@ size_t fp4_gemm_workspace_size(fp4_format fmt, fp4_mode mode, int64_t M, int64_t
   return gemm_ws_bytes(fmt, M, K);
 }
 
+size_t fp4_gemm_workspace_size_mnk(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N,
+                                   int64_t K, int has_a_bf16) {
+  if (!fmt_ok(fmt) || !mode_ok(mode) || M <= 0 || N <= 0 || K <= 0) return 0;
+  if (mode != FP4_W4A4 || K % group_of(fmt)) return 0;
+  return (has_a_bf16 ? gemm_ws_bytes(fmt, M, K) : 0) + gemm_relayout_bytes(fmt, M, N, K);
+}
+
 }  // extern "C"
 
 namespace {
@@ -377,6 +391,20 @@ fp4_status gemm_call(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_
     if (st != FP4_OK) return st;
   }
 
+  // Room for the stage-ordered scales after the fused quantization's area: used when
+  // the GEMM runs on the 256 x 256 tile (else its scales are gathered row by row)
+  const size_t fused_bytes = fused ? gemm_ws_bytes(fmt, M, K) : 0;
+  const size_t relayout_bytes = w4a4 ? gemm_relayout_bytes(fmt, M, N, K) : 0;
+  bool relayout = false;
+  if (relayout_bytes && (use_scratch || (workspace && aligned16(workspace))) &&
+      workspace_bytes >= fused_bytes + relayout_bytes) {
+    if (use_scratch && !fused) {
+      st = scratch_for_current_device(&workspace);
+      if (st != FP4_OK) return st;
+    }
+    relayout = true;
+  }
+
   hipStream_t s = (hipStream_t)stream;
   const char* name = "";
   const uint8_t* ac = a_codes;
@@ -412,6 +440,15 @@ fp4_status gemm_call(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_
   p.out = out;
   p.ldo = ldo;
   p.out_f32 = out_dtype == FP4_OUT_F32;
+  if (relayout) {
+    uint8_t* a_t = static_cast<uint8_t*>(workspace) + fused_bytes;
+    uint8_t* w_t = a_t + align256(fp4::scale_relayout_bytes(nv ? fp4::kNV : fp4::kMX, M, K));
+    hipError_t e = fp4::launch_scale_relayout(nv ? fp4::kNV : fp4::kMX, as, M, w_scales, N, K,
+                                              a_t, w_t, s);
+    if (e != hipSuccess) return launched(e, "scale_relayout");
+    p.a_scales_t = a_t;
+    p.w_scales_t = w_t;
+  }
   hipError_t e = fp4::launch_gemm(fmt, w4a4 ? fp4::kA_FP4 : fp4::kA_BF16, p, s, &name);
   st = launched(e, name);
   return st == FP4_OK ? ok_status : st;

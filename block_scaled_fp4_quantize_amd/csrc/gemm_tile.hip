@@ -7,7 +7,10 @@
 // fp16 for fp16 MFMA ("vLLM on the NVIDIA DGX Spark (GB10 / sm_121): A Complete
 // Technical Guide", §6.1 and §6.4 for the two block-scale formats).
 //
-// Tiling: a workgroup (4 waves, 2 x 2) owns 256 weight rows and 128 activation rows
+// Two tile kernels.  Dense problems with at least 256 tiles of 256 x 256 run big_gemm
+// (below): 4 waves, each 128 x 128 outputs, one workgroup per CU.  The rest (MoE
+// expert blocks, mid-size dense problems) run tile_gemm:
+// a workgroup (4 waves, 2 x 2) owns 256 weight rows and 128 activation rows
 // (MXFP4 runs two such workgroups per CU).  Each wave computes a 128 x 64 tile with
 // 16x16 MFMAs (weights as the A operand, so a lane ends up holding 4 consecutive
 // output columns).  K advances in stages of 128: the packed codes (64 bytes per row)
@@ -18,6 +21,7 @@
 // the MFMA (unit-scale convert, then one packed fp16 multiply by the e4m3 scale --
 // exact), MXFP4 needs no decode at all.
 #include <type_traits>
+#include <utility>
 
 #include "device.h"
 #include "internal.h"
@@ -69,32 +73,20 @@ struct TileCfg {
   static constexpr int SCOP = (SDW + 63) / 64;         // 256-byte scale copies
   static constexpr int SPW = (SCOP + WAVES - 1) / WAVES;  // ... per wave (padded)
   static constexpr int PLANES = SB / 4;                // scale words per row per stage
-  // Grouped scales (the 8-wave tile, whose LDS has room for them): a copy moves the
-  // words of 16 rows for 4 consecutive stages (16 bytes of each row), so each scale
-  // line is fetched once per 4 stages instead of once per stage.  A group (4 stages)
-  // takes SGI copies, issued a quarter per stage, into one of 3 group buffers.
-  static constexpr bool SGRP = BM == 256 && FMT == kMX;
-  static constexpr int SGI = ROWS / 16 * PLANES;       // 256-byte copies per group
-  static constexpr int SGW = SGI / 4 / WAVES;          // ... per wave per stage
-  static constexpr int ISTR = 320;                     // LDS stride of those copies
-  static constexpr int SGBYTES = SGI * ISTR;           // one group buffer
-  static constexpr int OPS = CPW + (SGRP ? SGW : SPW);  // copies per wave per stage
+  static constexpr int OPS = CPW + SPW;                // copies per wave per stage
   static constexpr int CODES = ROWS * 64;
-  static constexpr int STAGE = CODES + (SGRP ? 0 : WAVES * SPW * 256);  // bytes per LDS stage
+  static constexpr int STAGE = CODES + WAVES * SPW * 256;  // bytes per LDS stage
   // LDS stride between the scale words of consecutive 64-row blocks (as seen by a lane)
-  static constexpr int SBLK = SGRP ? 4 * ISTR : 256;
+  static constexpr int SBLK = 256;
   // workgroups per CU (the register budget follows from it: 512 / (PER_CU * WAVES /
-  // 4) per lane): 4-wave tiles that fit in 256 registers run two per CU (MXFP4 128 x
-  // 256, NVFP4 128 x 128), MXFP4 128 x 128 three; 8-wave tiles one.  Four stages
-  // in LDS when they fit next to the other workgroups, else three.
-  static constexpr int PER_CU =
-      BM == 128 ? (BN == 128 ? (FMT == kMX ? 3 : 2) : (FMT == kMX ? 2 : 1)) : 1;
+  // 4) per lane): tiles that fit in 256 registers run two per CU (MXFP4 128 x 256,
+  // NVFP4 128 x 128), MXFP4 128 x 128 three.  Four stages in LDS when they fit next
+  // to the other workgroups, else three.
+  static constexpr int PER_CU = BN == 128 ? (FMT == kMX ? 3 : 2) : (FMT == kMX ? 2 : 1);
   static constexpr int NBUF = PER_CU * 4 * STAGE <= 160 * 1024 ? 4 : 3;
-  static constexpr int SGOFF = NBUF * STAGE;           // group buffers follow the stages
-  static constexpr int LDS = NBUF * STAGE + (SGRP ? 3 * SGBYTES : 0);
-  static_assert(!SGRP || SGI % (4 * WAVES) == 0, "group copies split evenly over stages and waves");
+  static constexpr int LDS = NBUF * STAGE;
   static_assert(CCOP % WAVES == 0, "code copies split evenly over the waves");
-  static_assert(BM % 128 == 0 && BN % 128 == 0, "64-row scale blocks, 4-tile weight groups");
+  static_assert(BM == 128 && BN % 128 == 0, "64-row scale blocks, 4-tile weight groups");
   static_assert(NBUF >= 3 && NBUF <= 4, "the stage waits cover up to two stages in flight");
   static_assert(PER_CU * LDS <= 160 * 1024, "LDS per CU");
   static_assert(THREADS == 2 * BM, "launch bounds of tile_gemm");
@@ -315,23 +307,6 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
     dscale[q] = (rr < BM ? p.a_scales : wscales) + src_row(rr) * KS + plane * 4;
   }
 
-  // Grouped scales: copy c of a group (c = SGI/4 q + wave + WAVES w for quarter q) is
-  // plane c / (ROWS/16), 64-row block b = (c % (ROWS/16)) / 4 and rows 4 (c % 4) ..
-  // +3 of each of the block's 4 tiles; lane l fetches stage 4 g + l / 16 of tile l % 4,
-  // row 4 (c % 4) + (l / 4) % 4, so the 256 bytes land as [stage][row][tile] words and
-  // a lane reads its row's 4 tile words of one stage with one 16-byte read.
-  const uint8_t* gsrc[4][C::SGW > 0 ? C::SGW : 1];
-  if constexpr (C::SGRP) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int w = 0; w < C::SGW; ++w) {
-        const int c = (C::SGI / 4) * q + wave + C::WAVES * w;
-        const int plane = c / (C::ROWS / 16), rem = c % (C::ROWS / 16);
-        const int rr = (rem / 4) * 64 + (lane & 3) * 16 + 4 * (rem % 4) + ((lane >> 2) & 3);
-        gsrc[q][w] = (rr < BM ? p.a_scales : wscales) + src_row(rr) * KS + plane * 4;
-      }
-  }
   v4f acc[C::NJ][C::MI];
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j)
@@ -346,21 +321,11 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
   // exists) into the buffer computed at st - 1, computes stage st, then waits until
   // stage st + 1 has landed -- the stages after it may stay in flight -- and syncs.
   // The last iteration waits for everything, so no copy is outstanding after the loop.
-  // quarter q of scale group gi into group buffer gi % 3 (stages past the end re-read
-  // the last one: a group past the end is padding, its buffer free like any other)
-  auto issue_grp = [&](int64_t gi, int q, int w) {
-    uint8_t* gb = tsm + C::SGOFF + (int)(gi % 3) * C::SGBYTES;
-    int64_t stg = 4 * gi + (lane >> 4);
-    if (stg >= nstages) stg = nstages - 1;
-    tile_copy4(gsrc[q][w] + stg * C::SB, gb + ((C::SGI / 4) * q + wave + C::WAVES * w) * C::ISTR);
-  };
   // copy u (0 .. OPS-1) of stage t: the code copies, then the scale copies
   auto issue_part = [&](int64_t t, int u) {
     uint8_t* buf = tsm + (int)(t % C::NBUF) * C::STAGE;
     if (u < C::CPW) {
       tile_copy16(dcode[u] + t * 64, buf + (wave + C::WAVES * u) * 1024);
-    } else if constexpr (C::SGRP) {
-      issue_grp(t / 4 + 1, (int)(t % 4), u - C::CPW);
     } else {
       tile_copy4(dscale[u - C::CPW] + t * C::SB, buf + C::CODES + (wave + C::WAVES * (u - C::CPW)) * 256);
     }
@@ -393,122 +358,9 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
   }
   // this lane's scale words: plane gq / 2 (NVFP4), row r
   const int splane = FMT == kNV ? (gq >> 1) : 0;
-  const int srd = C::SGRP ? splane * (C::ROWS / 16) * C::ISTR + (r >> 2) * C::ISTR + (r & 3) * 16
-                          : C::CODES + splane * C::ROWS * 4 + r * 16;
-  auto stage_scales = [&](int64_t s, const uint8_t* cur) -> const uint8_t* {
-    return C::SGRP ? tsm + C::SGOFF + (int)((s / 4) % 3) * C::SGBYTES + (int)(s % 4) * 64 + srd
-                   : cur + srd;
-  };
-  // Scale group g is issued with code stages 4 g - 4 .. 4 g - 1 (group 0 up front) and
-  // read by stages 4 g .. 4 g + 3; its buffer last held group g - 3, whose reads all
-  // ended before the barrier that precedes the first of those issues.
-  if constexpr (C::SGRP) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int w = 0; w < C::SGW; ++w) issue_grp(0, q, w);
-  }
+  const int srd = C::CODES + splane * C::ROWS * 4 + r * 16;
 
-  if constexpr (FMT == kMX && C::NBUF == 4) {
-    // Software-pipelined: the LDS operands of stage st + 1 are read while the MFMAs of
-    // stage st run, each into the registers of an operand right after its last MFMA
-    // (weight tile j after tile j's MFMAs, activation tile i during the last weight
-    // tile's), so a stage's MFMAs never wait on LDS.  Stage st's buffer is free once
-    // its operands are in registers: iteration st refills it with stage st + NBUF, and
-    // waits (before its barrier) until stage st + 2 has landed.  Only with four stage
-    // buffers: with three, the copies would get one stage less to land than in the
-    // plain loop below, which measured faster there (MoE 128-row tiles).
-    const int wrow0 = BM + wn * (BN / 2);
-    u32x4 wf[C::NJ];
-    uint32_t wsb[C::NJ];
-    u32x4 af[C::MI];
-    uint32_t asb[C::MI];
-    const int ssh = 8 * gq;
-    auto rd_w = [&](const uint8_t* cur, int j) {
-      return *reinterpret_cast<const u32x4*>(cur + (wrow0 + 16 * j + r) * 64 + gcol);
-    };
-    auto rd_ws = [&](const uint8_t* sc, int k) {   // weight tiles 4 k .. 4 k + 3
-      const u32x4 w4 = *reinterpret_cast<const u32x4*>(sc + (wrow0 / 64 + k) * C::SBLK);
-      wsb[4 * k + 0] = w4.x >> ssh;
-      wsb[4 * k + 1] = w4.y >> ssh;
-      wsb[4 * k + 2] = w4.z >> ssh;
-      wsb[4 * k + 3] = w4.w >> ssh;
-    };
-    auto rd_a = [&](const uint8_t* cur, int i) {
-      return *reinterpret_cast<const u32x4*>(cur + (wm * 64 + 16 * i + r) * 64 + gcol);
-    };
-    auto rd_as = [&](const uint8_t* sc) {
-      const u32x4 a4 = *reinterpret_cast<const u32x4*>(sc + wm * C::SBLK);
-      asb[0] = a4.x >> ssh;
-      asb[1] = a4.y >> ssh;
-      asb[2] = a4.z >> ssh;
-      asb[3] = a4.w >> ssh;
-    };
-    auto mma = [&](int j, int i) {
-      const v8i wop = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
-      const v8i aop = {(int)af[i].x, (int)af[i].y, (int)af[i].z, (int)af[i].w, 0, 0, 0, 0};
-      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          wop, aop, acc[j][i], 4, 4, 0, (int)wsb[j], 0, (int)asb[i]);
-    };
-    static_assert(C::MI == 4 && C::NJ % 4 == 0, "scale words are read 4 tiles at a time");
-#pragma unroll
-    for (int t = 0; t < C::NBUF; ++t)
-      if (t < nstages) issue(t);
-    sync(nstages - 1 < C::NBUF - 1 ? nstages - 1 : C::NBUF - 1);   // stage 0 landed
-    {
-      const uint8_t* sc = stage_scales(0, tsm);
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) wf[j] = rd_w(tsm, j);
-#pragma unroll
-      for (int k = 0; k < C::NJ / 4; ++k) rd_ws(sc, k);
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) af[i] = rd_a(tsm, i);
-      rd_as(sc);
-    }
-    // stage 1 landed; every wave's reads of buffer 0 done
-    sync(nstages - 1 < C::NBUF - 1 ? (nstages - 1 > 0 ? nstages - 2 : 0) : C::NBUF - 2);
-    // copy u goes after MFMA group u (NJ - 1) / OPS <= NJ - 2: every copy is issued
-    static_assert(C::NJ >= 2, "at least two weight tiles per wave");
-    for (int64_t st = 0; st < nstages; ++st) {
-      // stage st + NBUF refills this stage's buffer; its OPS copies are spread over
-      // the MFMA groups below (issued in one burst, the copies of the 8 waves queue
-      // up in the texture unit and stall the waves behind them)
-      const bool refill = st + C::NBUF < nstages;
-      // operands of stage st + 1 (or stage st again after the last: its buffer is not
-      // refilled then, and the values go unused)
-      const int64_t sn = st + 1 < nstages ? st + 1 : st;
-      const uint8_t* cur = tsm + (int)(sn % C::NBUF) * C::STAGE;
-      const uint8_t* sc = stage_scales(sn, cur);
-#pragma unroll
-      for (int j = 0; j < C::NJ - 1; ++j) {
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i) mma(j, i);
-        // pins the order: the MFMAs above (their results pass through here), then the
-        // reads below (the memory clobber keeps them from being hoisted)
-        asm volatile("" : "+v"(acc[j][0]), "+v"(acc[j][1]), "+v"(acc[j][2]), "+v"(acc[j][3])
-                     :: "memory");
-#pragma unroll
-        for (int u = 0; u < C::OPS; ++u)
-          if (u * (C::NJ - 1) / C::OPS == j && refill) issue_part(st + C::NBUF, u);
-        wf[j] = rd_w(cur, j);
-        if (j % 4 == 3) rd_ws(sc, j / 4);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) {
-        mma(C::NJ - 1, i);
-        asm volatile("" : "+v"(acc[C::NJ - 1][i]) :: "memory");
-        af[i] = rd_a(cur, i);
-      }
-      wf[C::NJ - 1] = rd_w(cur, C::NJ - 1);
-      rd_ws(sc, C::NJ / 4 - 1);
-      rd_as(sc);
-      __builtin_amdgcn_sched_barrier(0);
-      // stage st + 2 landed (the stages issued after it may stay in flight)
-      const int64_t last = st + C::NBUF < nstages ? st + C::NBUF : nstages - 1;
-      sync(st + 2 <= nstages - 1 ? last - (st + 2) : 0);
-    }
-  } else {
+  {
     // Row blocks cut short take the per-tile form of the step through their own copy
     // of the loop (two forms in one loop would double the live registers)
     auto plain = [&](auto partial) {
@@ -521,16 +373,12 @@ __global__ __launch_bounds__(2 * BM, (TileCfg<FMT, BM, BN>::PER_CU)) void tile_g
         const int64_t t = st + C::NBUF - 1;
         if (t < nstages) issue(t);
         const uint8_t* cur = tsm + (int)(st % C::NBUF) * C::STAGE;
-        tile_step<FMT, BM, BN, PART>(cur, stage_scales(st, cur), gcol, r, gq, wm, wn, acc, nvt);
+        tile_step<FMT, BM, BN, PART>(cur, cur + srd, gcol, r, gq, wm, wn, acc, nvt);
         sync((t < nstages ? t : nstages - 1) - (st + 1));
       }
     };
-    if constexpr (BM == 128) {   // (the 256-row tile: dense only, no copy)
-      if (nvt < C::MI) {
-        plain(std::true_type{});
-      } else {
-        plain(std::false_type{});
-      }
+    if (nvt < C::MI) {
+      plain(std::true_type{});
     } else {
       plain(std::false_type{});
     }
@@ -673,9 +521,9 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (FMT == kNV)
     *name = FUSE ? (BN == 128 ? "tile_nvfp4_m128_n128_swiglu" : "tile_nvfp4_m128_swiglu")
-                 : (BM == 256 ? "tile_nvfp4_m256" : (BN == 128 ? "tile_nvfp4_m128_n128" : "tile_nvfp4_m128"));
+                 : (BN == 128 ? "tile_nvfp4_m128_n128" : "tile_nvfp4_m128");
   else
-    *name = FUSE ? "tile_mxfp4_m128_swiglu" : (BM == 256 ? "tile_mxfp4_m256" : "tile_mxfp4_m128");
+    *name = FUSE ? "tile_mxfp4_m128_swiglu" : "tile_mxfp4_m128";
   if (p.K % kTBK != 0 || p.K <= 0) return hipErrorInvalidValue;
   if (FUSE && (p.I <= 0 || p.I % 128 != 0 || p.N != 2 * p.I || !p.h_codes || !p.h_scales))
     return hipErrorInvalidValue;
@@ -689,22 +537,561 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s, const char** name) {
   return hipGetLastError();
 }
 
+// ---- dense problems with many 256 x 256 tiles: a 4-wave tile, 128 x 128 per wave ----
+// One wave per SIMD; wave (wm, wn) computes 128 activation rows x 128 weight rows as
+// 8 x 8 16x16 MFMA tiles (256 accumulator registers), so each LDS operand read feeds 8
+// MFMAs (the 8-wave tile's feed 4 or 8) and, for NVFP4, each decoded operand tile too.
+// The staged LDS layout is the one above (64-byte code rows, XOR-swizzled columns, scale
+// words in tile_sslot order), four stage buffers.  Weight rows are staged in pair order:
+// in each 32-row group, 16-row tile 2p holds rows 8q + v and tile 2p + 1 rows 8q + 4 + v
+// (q, v = 0..3), so a lane's accumulators of the two tiles are 8 consecutive output
+// columns (one 16-byte bf16 store).
+// Global row (within its 256-row tile) of staged weight row w.  MXFP4 (16x16 MFMAs, a
+// lane holds rows 4 gq + v of a 16-row tile): tile 2p holds rows 32 p + 8 q + v and
+// tile 2p + 1 rows 32 p + 8 q + 4 + v.  NVFP4 (32x32 MFMAs, a lane holds rows 8 g +
+// 4 h + v of a 32-row tile, g = 0..3): row 8 g + 4 h + v of tile T is 32 T + 16 (g >> 1)
+// + 8 h + 4 (g & 1) + v.  Either way a lane's accumulators cover runs of 8 consecutive
+// output columns.
+template <int FMT>
+__device__ __forceinline__ int big_wperm(int w) {
+  if (FMT == kMX) {
+    const int t = w >> 4, rho = w & 15;
+    return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3);
+  }
+  const int T = w >> 5, rho = w & 31, g = rho >> 3;
+  return 32 * T + 16 * (g >> 1) + 8 * ((rho >> 2) & 1) + 4 * (g & 1) + (rho & 3);
+}
+
+template <int FMT>
+struct BigCfg {
+  static constexpr int G = FMT == kNV ? 16 : 32;
+  static constexpr int SB = kTBK / G;           // scale bytes per row per stage
+  static constexpr int PLANES = SB / 4;         // scale words per row per stage
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int MI = 8, NJ = 8;          // 16-row activation / weight tiles per wave
+  static constexpr int ROWS = 512;              // staged rows: 256 activation, 256 weight
+  static constexpr int CPW = ROWS / 16 / WAVES; // 1 KB code copies per wave per stage
+  static constexpr int SDW = ROWS * PLANES;     // scale words per stage
+  static constexpr int SPW = SDW / 64 / WAVES;  // 256-byte scale copies per wave per stage
+  static constexpr int OPS = CPW + SPW;
+  static constexpr int CODES = ROWS * 64;
+  static constexpr int STAGE = CODES + SDW * 4;
+  static constexpr int NBUF = 4;
+  static constexpr int LDS = NBUF * STAGE;
+  static_assert(LDS <= 160 * 1024, "LDS per CU");
+  static_assert(SDW % (64 * WAVES) == 0, "scale copies split evenly over the waves");
+  static_assert(3 * OPS <= 63, "the stage waits fit the vmcnt field");
+};
+
+// Scheduling groups of one MXFP4 stage (in order): for each weight tile j < 7, its 8
+// MFMAs, the copies spread onto it and its LDS reads (plus the first scale read after
+// tile 3); then each MFMA of tile 7 followed by one activation read; then the last
+// four reads.  Masks: 0x008 MFMA, 0x020 vector memory read, 0x100 LDS read.
+template <int OPS, int J>
+__device__ __forceinline__ void big_mx_group() {
+  constexpr int nc = [] {
+    int n = 0;
+    for (int u = 0; u < OPS; ++u) n += u * 7 / OPS == J;
+    return n;
+  }();
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  if constexpr (nc > 0) __builtin_amdgcn_sched_group_barrier(0x020, nc, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, J == 3 ? 2 : 1, 0);
+}
+template <int OPS, int... J>
+__device__ __forceinline__ void big_mx_order(std::integer_sequence<int, J...>) {
+  (big_mx_group<OPS, J>(), ...);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+}
+
+// Scheduling groups of the NVFP4 k-step 7 (in order): the next stage's activation
+// code and scale reads (12 LDS reads), then per weight tile u: its decode (8 VALU), the
+// reads of its next-stage codes, its 4 MFMAs each followed by two VALU of the next
+// stage's first activation decode, and the copies spread onto it.
+template <int OPS, int U>
+__device__ __forceinline__ void big_nv_group7() {
+  constexpr int nc = [] {
+    int n = 0;
+    for (int q = 0; q < OPS; ++q) n += q * 4 / OPS == U;
+    return n;
+  }();
+  __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+  if constexpr (nc > 0) __builtin_amdgcn_sched_group_barrier(0x020, nc, 0);
+}
+template <int OPS, int... U>
+__device__ __forceinline__ void big_nv_order7(std::integer_sequence<int, U...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+  (big_nv_group7<OPS, U>(), ...);
+}
+
+// Eight consecutive outputs out[m][n .. n + 7] (alpha applied): one 16-byte bf16 store
+// (or two fp32 ones) when aligned and inside the matrix, else element by element.
+__device__ __forceinline__ void big_store8(const GemmParams& p, int64_t m, int64_t n,
+                                           const float (&x)[8], bool vec) {
+  if (vec && n + 7 < p.N) {
+    if (p.out_f32) {
+      float* o = reinterpret_cast<float*>(p.out) + m * p.ldo + n;
+      *reinterpret_cast<float4*>(o) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    } else {
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + n;
+      *reinterpret_cast<uint4*>(o) = make_uint4(bf16_pack2(x[0], x[1]), bf16_pack2(x[2], x[3]),
+                                                bf16_pack2(x[4], x[5]), bf16_pack2(x[6], x[7]));
+    }
+    return;
+  }
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    if (n + v >= p.N) break;
+    if (p.out_f32)
+      reinterpret_cast<float*>(p.out)[m * p.ldo + n + v] = x[v];
+    else
+      reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n + v] = (uint16_t)(bf16_pack2(x[v], 0.0f) & 0xFFFFu);
+  }
+}
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <int FMT>
+__global__ __launch_bounds__(256, 1) void big_gemm(GemmParams p) {
+  using C = BigCfg<FMT>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t ntiles = (p.N + 255) / 256;
+  const int64_t mb = (int64_t)blockIdx.x / ntiles;
+  const int64_t nt = (int64_t)blockIdx.x - mb * ntiles;
+  const int64_t row0 = mb * 256;
+  const int64_t K = p.K, KB = K >> 1, KS = K / C::G;
+  const int64_t nstages = K / kTBK;
+  const float alpha = p.alpha;
+
+  // global row of staged row rr: activations 0..255 in order, weights in pair order;
+  // rows past the end are clamped to the last one (their outputs are not stored)
+  auto src_row = [&](int rr) -> int64_t {
+    if (rr < 256) {
+      const int64_t m = row0 + rr;
+      return m < p.M ? m : p.M - 1;
+    }
+    const int64_t n = nt * 256 + big_wperm<FMT>(rr - 256);
+    return n < p.N ? n : p.N - 1;
+  };
+  // code copy q of this wave is copy c = wave + 4 q (staged rows 16 c ..): lane l
+  // fetches row 16 c + l/4, column (l & 3) ^ tile_swz(l/4) into LDS slot l; scale copy
+  // q (c = wave + 4 q) fills scale words 64 c + l.
+  const uint8_t* dcode[C::CPW];
+  const uint8_t* dscale[C::SPW];
+#pragma unroll
+  for (int q = 0; q < C::CPW; ++q) {
+    const int rr = 16 * (wave + C::WAVES * q) + (lane >> 2);
+    const int col = (lane & 3) ^ tile_swz(lane >> 2);
+    dcode[q] = (rr < 256 ? p.a_codes : p.w_codes) + src_row(rr) * KB + col * 16;
+  }
+  // scale copy q (c = wave + 4 q) fills the 64 words of plane c / 8, 64-row block c % 8
+  // of the stage: gathered from the rows (one word per row), or one contiguous 256-byte
+  // piece of the stage-ordered scales ([64-row block][stage][plane][64 words])
+  const bool stile = p.a_scales_t && p.w_scales_t;
+  const int64_t sstride = stile ? C::PLANES * 256 : C::SB;   // bytes per stage
+#pragma unroll
+  for (int q = 0; q < C::SPW; ++q) {
+    const int c = wave + C::WAVES * q;
+    const int e = 64 * c + lane;
+    const int plane = e / C::ROWS;
+    if (stile) {
+      const int blk = c % 8;   // 0..3 activation blocks, 4..7 weight blocks
+      const int64_t rb = blk < 4 ? mb * 4 + blk : nt * 4 + blk - 4;
+      dscale[q] = (blk < 4 ? p.a_scales_t : p.w_scales_t) + (rb * nstages * C::PLANES + plane) * 256 + lane * 4;
+    } else {
+      const int rr = tile_srow(e - plane * C::ROWS);
+      dscale[q] = (rr < 256 ? p.a_scales : p.w_scales) + src_row(rr) * KS + plane * 4;
+    }
+  }
+  // Stages past the last are issued too, as copies that all read one line (the
+  // first weight bytes): every iteration then issues the same copies and waits with
+  // the same counts, so the loop has no branches.  Their buffers are never read.
+  auto issue_part = [&](int64_t t, int u) {
+    uint8_t* buf = tsm + (int)(t % C::NBUF) * C::STAGE;
+    const bool real = t < nstages;
+    if (u < C::CPW) {
+      const uint8_t* src = real ? dcode[u] + t * 64 : p.w_codes;
+      tile_copy16(src, buf + (wave + C::WAVES * u) * 1024);
+    } else {
+      const uint8_t* src = real ? dscale[u - C::CPW] + t * sstride : p.w_scales;
+      tile_copy4(src, buf + C::CODES + (wave + C::WAVES * (u - C::CPW)) * 256);
+    }
+  };
+  // wait until all but the last AHEAD stages issued have landed, then barrier
+  auto sync = [&](auto ahead_tag) {
+    constexpr int AHEAD = decltype(ahead_tag)::value;
+    __builtin_amdgcn_s_waitcnt(tile_vmcnt(AHEAD * C::OPS));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const int r = lane & 15;
+  const int gq = lane >> 4;
+  const int gcol = (gq ^ tile_swz(r)) << 4;
+  const int wrow0 = 256 + wn * 128;   // this wave's staged weight rows
+  const int arow0 = wm * 128;         // ... and activation rows
+  // scale words of plane pl, 64-row block starting at staged row b0, this lane's row r:
+  // the 4 tiles' words in one 16-byte read
+  auto rd_s4 = [&](const uint8_t* cur, int pl, int b0) {
+    return *reinterpret_cast<const u32x4*>(cur + C::CODES + (pl * C::ROWS + b0 + 4 * r) * 4);
+  };
+  auto rd_w = [&](const uint8_t* cur, int j) {
+    return *reinterpret_cast<const u32x4*>(cur + (wrow0 + 16 * j + r) * 64 + gcol);
+  };
+  auto rd_a = [&](const uint8_t* cur, int i) {
+    return *reinterpret_cast<const u32x4*>(cur + (arow0 + 16 * i + r) * 64 + gcol);
+  };
+
+#pragma unroll
+  for (int t = 0; t < C::NBUF; ++t)
+#pragma unroll
+    for (int u = 0; u < C::OPS; ++u) issue_part(t, u);
+  using A1 = std::integral_constant<int, 1>;
+  using A2 = std::integral_constant<int, 2>;
+  using A3 = std::integral_constant<int, 3>;
+
+  if constexpr (FMT == kMX) {
+    v4f acc[C::NJ][C::MI];
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+    // The LDS operands of stage st + 1 are read while the MFMAs of stage st run, each
+    // into the registers of an operand right after its last MFMA; stage st's buffer
+    // is refilled (stage st + 4) from iteration st on, and iteration st ends by waiting
+    // until stage st + 2 has landed.
+    u32x4 wf[C::NJ], af[C::MI];
+    uint32_t wsb[C::NJ], asb[C::MI];
+    const int ssh = 8 * gq;
+    auto rd_ws = [&](const uint8_t* cur, int k) {
+      const u32x4 w4 = rd_s4(cur, 0, wrow0 + 64 * k);
+      wsb[4 * k + 0] = w4.x >> ssh;
+      wsb[4 * k + 1] = w4.y >> ssh;
+      wsb[4 * k + 2] = w4.z >> ssh;
+      wsb[4 * k + 3] = w4.w >> ssh;
+    };
+    auto rd_as = [&](const uint8_t* cur, int k) {
+      const u32x4 a4 = rd_s4(cur, 0, arow0 + 64 * k);
+      asb[4 * k + 0] = a4.x >> ssh;
+      asb[4 * k + 1] = a4.y >> ssh;
+      asb[4 * k + 2] = a4.z >> ssh;
+      asb[4 * k + 3] = a4.w >> ssh;
+    };
+    auto mma = [&](int j, int i) {
+      const v8i wop = {(int)wf[j].x, (int)wf[j].y, (int)wf[j].z, (int)wf[j].w, 0, 0, 0, 0};
+      const v8i aop = {(int)af[i].x, (int)af[i].y, (int)af[i].z, (int)af[i].w, 0, 0, 0, 0};
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          wop, aop, acc[j][i], 4, 4, 0, (int)wsb[j], 0, (int)asb[i]);
+    };
+    sync(A3{});   // stage 0 landed
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) wf[j] = rd_w(tsm, j);
+    rd_ws(tsm, 0);
+    rd_ws(tsm, 1);
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) af[i] = rd_a(tsm, i);
+    rd_as(tsm, 0);
+    rd_as(tsm, 1);
+    sync(A2{});   // stage 1 landed; every wave's reads of buffer 0 done
+    for (int64_t st = 0; st < nstages; ++st) {
+      // operands of stage st + 1 (after the last stage: a dummy stage, unused)
+      const uint8_t* cur = tsm + (int)((st + 1) % C::NBUF) * C::STAGE;
+#pragma unroll
+      for (int j = 0; j < C::NJ - 1; ++j) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) mma(j, i);
+#pragma unroll
+        for (int u = 0; u < C::OPS; ++u)
+          if (u * (C::NJ - 1) / C::OPS == j) issue_part(st + C::NBUF, u);
+        wf[j] = rd_w(cur, j);
+        if (j == 3) rd_ws(cur, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        mma(C::NJ - 1, i);
+        af[i] = rd_a(cur, i);
+      }
+      wf[C::NJ - 1] = rd_w(cur, C::NJ - 1);
+      rd_ws(cur, 1);
+      rd_as(cur, 0);
+      rd_as(cur, 1);
+      // the order of the body: 8 MFMAs, then weight tile j's copies and LDS reads, for
+      // each j; then each MFMA of the last weight tile followed by one activation read
+      big_mx_order<C::OPS>(std::make_integer_sequence<int, C::NJ - 1>{});
+      sync(A2{});   // stage st + 2 landed, st + 3 and st + 4 in flight
+    }
+    // the copies of the dummy stages must land before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(tile_vmcnt(0));
+
+    // epilogue: lane holds out[m][n .. n+3] of weight tile j (n per the pair order) for
+    // activation row m = 16 i + r; tiles 2 q and 2 q + 1 give 8 consecutive columns
+    const bool vec = (p.ldo & 7) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
+      const int64_t m = row0 + arow0 + 16 * i + r;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int q = 0; q < C::NJ / 2; ++q) {
+        const int64_t n = nt * 256 + 32 * (4 * wn + q) + 8 * gq;
+        float x[8];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x[v] = acc[2 * q][i][v] * alpha;
+          x[4 + v] = acc[2 * q + 1][i][v] * alpha;
+        }
+        big_store8(p, m, n, x, vec);
+      }
+    }
+  } else {
+    // NVFP4 on 32x32x16 fp16 MFMAs: wave tile = 4 weight x 4 activation tiles of 32
+    // rows (lane row rho = lane % 32).  Lane half h = lane / 32 holds elements [64 h,
+    // 64 h + 64) of the stage (16-byte columns 2 h and 2 h + 1 of its row); k-step s =
+    // 0..7 uses its elements 64 h + 8 s .. + 8, i.e. block 4 h + s / 2, the same k slots
+    // for both operands.  The activation tiles of k-step s + 1 are decoded while the
+    // MFMAs of k-step s run, each weight tile right before its 4 MFMAs.  K-step 7 of
+    // stage st starts with a barrier after which stage st + 1 has landed and every wave
+    // has finished reading stage st (whose buffer then takes stage st + 4); its MFMAs
+    // run while stage st + 1's operands are read and its first activation k-step decoded.
+    constexpr int T4 = 4;
+    v16f acc2[T4][T4];
+#pragma unroll
+    for (int u = 0; u < T4; ++u)
+#pragma unroll
+      for (int i = 0; i < T4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc2[u][i][v] = 0.0f;
+    const int rho = lane & 31, h = lane >> 5;
+    const int c0 = ((2 * h) ^ tile_swz(rho & 15)) << 4;
+    const int c1 = ((2 * h + 1) ^ tile_swz(rho & 15)) << 4;
+    const int tsel = rho >> 4;   // word of a 64-row block's 4 that holds this lane's row
+    u32x4 wf[T4][2], af[T4][2];
+    f16x2 wsc[T4][2], asc[T4][2];
+    auto rd_codes = [&](const uint8_t* cur, int row0_, u32x4 (&f)[T4][2], int u) {
+      const uint8_t* rp = cur + (row0_ + 32 * u + rho) * 64;
+      f[u][0] = *reinterpret_cast<const u32x4*>(rp + c0);
+      f[u][1] = *reinterpret_cast<const u32x4*>(rp + c1);
+    };
+    // scale words of plane h for the 4 tiles of a side (two 64-row blocks, two tiles
+    // each), as two fp16 pairs per tile (blocks 4 h, 4 h + 1 and 4 h + 2, 4 h + 3)
+    auto rd_sc = [&](const uint8_t* cur, int row0_, f16x2 (&sc)[T4][2]) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const u32x4 w4 = rd_s4(cur, h, row0_ + 64 * k);
+        const uint32_t e0 = tsel ? w4.y : w4.x, e1 = tsel ? w4.w : w4.z;
+        sc[2 * k][0] = e4m3_pair_f16(e0);
+        sc[2 * k][1] = e4m3_pair_f16(e0 >> 16);
+        sc[2 * k + 1][0] = e4m3_pair_f16(e1);
+        sc[2 * k + 1][1] = e4m3_pair_f16(e1 >> 16);
+      }
+    };
+    auto dec = [&](const u32x4 (&f)[2], const f16x2 (&sc)[2], int s) {
+      return decode8_f16(dword_of_v(f[s >> 2], s & 3), f16_bcast(sc[s >> 2], (s >> 1) & 1));
+    };
+    f16x8 ad[T4];
+    sync(A3{});   // stage 0 landed
+#pragma unroll
+    for (int u = 0; u < T4; ++u) {
+      rd_codes(tsm, arow0, af, u);
+      rd_codes(tsm, wrow0, wf, u);
+    }
+    rd_sc(tsm, arow0, asc);
+    rd_sc(tsm, wrow0, wsc);
+#pragma unroll
+    for (int i = 0; i < T4; ++i) ad[i] = dec(af[i], asc[i], 0);
+    for (int64_t st = 0; st < nstages; ++st) {
+#pragma unroll
+      for (int s = 0; s < 7; ++s) {
+        f16x8 an[T4];
+#pragma unroll
+        for (int u = 0; u < T4; ++u) {
+          const f16x8 wd = dec(wf[u], wsc[u], s);
+#pragma unroll
+          for (int i = 0; i < T4; ++i)
+            acc2[u][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wd, ad[i], acc2[u][i], 0, 0, 0);
+          an[u] = dec(af[u], asc[u], s + 1);   // activation tile u of k-step s + 1
+        }
+#pragma unroll
+        for (int i = 0; i < T4; ++i) ad[i] = an[i];
+      }
+      // k-steps 0..6: per weight tile, its decode (8 VALU), then its 4 MFMAs each
+      // followed by two of the 8 VALU decoding an activation tile of the next k-step
+#pragma unroll
+      for (int g = 0; g < 7 * T4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+        for (int i = 0; i < T4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+      }
+      sync(A2{});   // stage st + 1 landed, st + 2 and st + 3 in flight
+      // operands of stage st + 1 (after the last stage: a dummy stage, unused)
+      const uint8_t* nxt = tsm + (int)((st + 1) % C::NBUF) * C::STAGE;
+#pragma unroll
+      for (int u = 0; u < T4; ++u) rd_codes(nxt, arow0, af, u);
+      f16x2 wsn[T4][2], asn[T4][2];
+      rd_sc(nxt, arow0, asn);
+      rd_sc(nxt, wrow0, wsn);
+      f16x8 an[T4];
+#pragma unroll
+      for (int u = 0; u < T4; ++u) {
+        const f16x8 wd = dec(wf[u], wsc[u], 7);
+        rd_codes(nxt, wrow0, wf, u);
+#pragma unroll
+        for (int i = 0; i < T4; ++i)
+          acc2[u][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wd, ad[i], acc2[u][i], 0, 0, 0);
+        an[u] = dec(af[u], asn[u], 0);
+#pragma unroll
+        for (int q = 0; q < C::OPS; ++q)
+          if (q * T4 / C::OPS == u) issue_part(st + C::NBUF, q);
+      }
+      big_nv_order7<C::OPS>(std::make_integer_sequence<int, T4>{});
+#pragma unroll
+      for (int u = 0; u < T4; ++u) {
+        ad[u] = an[u];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          asc[u][k] = asn[u][k];
+          wsc[u][k] = wsn[u][k];
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(tile_vmcnt(0));
+    // epilogue: lane holds, for weight tile u and activation tile i, out[m][n0 + 0..7]
+    // (accumulators 0..7) and out[m][n0 + 16 + 0..7] (8..15), m = 32 i + rho, n0 = 32 u
+    // + 8 h (the staging order above)
+    const bool vec = (p.ldo & 7) == 0 && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+#pragma unroll
+    for (int i = 0; i < T4; ++i) {
+      const int64_t m = row0 + arow0 + 32 * i + rho;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int u = 0; u < T4; ++u)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int64_t n = nt * 256 + wn * 128 + 32 * u + 16 * q + 8 * h;
+          float x[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) x[v] = acc2[u][i][8 * q + v] * alpha;
+          big_store8(p, m, n, x, vec);
+        }
+    }
+    return;
+  }
+
+
+}
+
+// Block scales in the 256 x 256 tile's stage order: word (64-row block rb, stage t,
+// plane pl, slot) at ((rb * nstages + t) * PLANES + pl) * 64 + slot holds the scale
+// bytes [t SB + 4 pl, +4) of the row staged at position 64 rb + tile_srow(slot) --
+// rows in order for the activations, in the pair order within each 256-row tile for
+// the weights; rows past the end get zero words.
+template <int FMT>
+__global__ void scale_relayout_kernel(const uint8_t* __restrict__ a_sc, int64_t M,
+                                      const uint8_t* __restrict__ w_sc, int64_t N, int64_t K,
+                                      uint8_t* __restrict__ a_t, uint8_t* __restrict__ w_t,
+                                      int64_t a_words, int64_t total_words) {
+  using C = BigCfg<FMT>;
+  const int64_t e0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e0 >= total_words) return;
+  const bool wside = e0 >= a_words;
+  const int64_t e = wside ? e0 - a_words : e0;
+  const int64_t nst = K / kTBK, KS = K / C::G;
+  const int slot = (int)(e & 63);
+  int64_t rest = e >> 6;
+  const int pl = (int)(rest % C::PLANES);
+  rest /= C::PLANES;
+  const int64_t t = rest % nst;
+  const int64_t rb = rest / nst;
+  const int64_t srow = rb * 64 + tile_srow(slot);   // staged row of this side
+  int64_t row = srow;
+  if (wside) row = (srow & ~(int64_t)255) + big_wperm<FMT>((int)(srow & 255));
+  const int64_t R = wside ? N : M;
+  const uint8_t* sc = wside ? w_sc : a_sc;
+  const uint32_t v = row < R ? *reinterpret_cast<const uint32_t*>(sc + row * KS + t * C::SB + 4 * pl) : 0u;
+  reinterpret_cast<uint32_t*>(wside ? w_t : a_t)[e] = v;
+}
+
+template <int FMT>
+hipError_t launch_big(const GemmParams& p, hipStream_t s, const char** name) {
+  using C = BigCfg<FMT>;
+  const int64_t grid = ((p.N + 255) / 256) * ((p.M + 255) / 256);
+  *name = FMT == kNV ? "big_nvfp4_256" : "big_mxfp4_256";
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (p.K % kTBK != 0 || p.K <= 0 || p.mblk_expert || p.a_gather || p.fuse_swiglu)
+    return hipErrorInvalidValue;
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&big_gemm<FMT>), C::LDS, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((big_gemm<FMT>), dim3((unsigned)grid), dim3(C::THREADS), C::LDS, s, p);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_relayout(const uint8_t* a_sc, int64_t M, const uint8_t* w_sc, int64_t N,
+                           int64_t K, uint8_t* a_t, uint8_t* w_t, hipStream_t s) {
+  using C = BigCfg<FMT>;
+  const int64_t a_words = (M + 255) / 256 * 256 * (K / C::G) / 4;
+  const int64_t total = a_words + (N + 255) / 256 * 256 * (K / C::G) / 4;
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((scale_relayout_kernel<FMT>), dim3((unsigned)grid), dim3(256), 0, s, a_sc, M,
+                     w_sc, N, K, a_t, w_t, a_words, total);
+  return hipGetLastError();
+}
+
 // NVFP4 weight-tile width (128: two workgroups per CU)
 constexpr int kNvTileN = 128;
 
 }  // namespace
 
+bool gemm_big_tile(int fmt, int64_t M, int64_t N, int64_t K) {
+  (void)fmt;
+  return M > 64 && K > 0 && K % kTBK == 0 && ((M + 255) / 256) * ((N + 255) / 256) >= 256;
+}
+
+size_t scale_relayout_bytes(int fmt, int64_t R, int64_t K) {
+  return (size_t)((R + 255) / 256 * 256) * (size_t)(K / (fmt == kNV ? 16 : 32));
+}
+
+hipError_t launch_scale_relayout(int fmt, const uint8_t* a_scales, int64_t M,
+                                 const uint8_t* w_scales, int64_t N, int64_t K, uint8_t* a_t,
+                                 uint8_t* w_t, hipStream_t s) {
+  if (K <= 0 || K % kTBK) return hipErrorInvalidValue;
+  return fmt == kNV ? launch_relayout<kNV>(a_scales, M, w_scales, N, K, a_t, w_t, s)
+                    : launch_relayout<kMX>(a_scales, M, w_scales, N, K, a_t, w_t, s);
+}
+
 hipError_t launch_gemm_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name) {
-  const int64_t ntiles256 = (p.N + 255) / 256;
-  const bool big = !p.mblk_expert && ((p.M + 255) / 256) * ntiles256 >= 256;
+  // dense problems with enough 256 x 256 tiles to give every CU one: the 4-wave tile
+  const bool big = !p.mblk_expert && !p.a_gather && !p.fuse_swiglu && gemm_big_tile(fmt, p.M, p.N, p.K);
   if (fmt == kNV) {
     if (p.fuse_swiglu) return launch_tile<kNV, 128, kNvTileN, true>(p, s, name);
-    if (big) return launch_tile<kNV, 256, 256, false>(p, s, name);
+    if (big) return launch_big<kNV>(p, s, name);
     return launch_tile<kNV, 128, kNvTileN, false>(p, s, name);
   }
   if (p.fuse_swiglu) return launch_tile<kMX, 128, 256, true>(p, s, name);
-  // dense MXFP4 with enough 256 x 256 tiles to give every CU one: the 8-wave tile
-  if (big) return launch_tile<kMX, 256, 256, false>(p, s, name);
+  if (big) return launch_big<kMX>(p, s, name);
   return launch_tile<kMX, 128, 256, false>(p, s, name);
 }
 

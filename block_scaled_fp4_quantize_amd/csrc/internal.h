@@ -81,6 +81,11 @@ struct GemmParams {
   float h_g;              // scalar multiplier when h_grp_g is null (MXFP4: unused)
   uint8_t* h_codes;       // [rows, I/2]
   uint8_t* h_scales;      // [rows, I/G]
+  // Optional block scales in the 256 x 256 tile's stage order (scale_relayout): when
+  // both are set, that kernel copies each stage's scales as contiguous 256-byte pieces
+  // instead of gathering one word from each row.
+  const uint8_t* a_scales_t;
+  const uint8_t* w_scales_t;
 };
 enum AKind : int { kA_FP4 = 0, kA_BF16 = 1 };
 // Whether a gate/up GEMM of this shape takes the fused SwiGLU + requant epilogue: on
@@ -95,6 +100,16 @@ int gemm_block_rows(int fmt, int akind, int64_t rows_per_group, int64_t H, int64
 // blocks, K % 128 == 0, lda % 8 == 0): the LDS-tiled bf16-MFMA kernel;
 // w4a16_tiled_ok says whether a GEMM qualifies.
 bool w4a16_tiled_ok(const GemmParams& p);
+// Dense fp4-activation GEMMs with at least 256 tiles of 256 x 256 run on the 4-wave
+// 256 x 256 tile kernel (K % 128 == 0).  Its block scales can first be re-laid into
+// stage order: scale_relayout_bytes(R, K) bytes per side (rows padded to 256), written
+// by launch_scale_relayout for the activations (rows in order) and the weights (rows
+// in the kernel's pair order).
+bool gemm_big_tile(int fmt, int64_t M, int64_t N, int64_t K);
+size_t scale_relayout_bytes(int fmt, int64_t R, int64_t K);
+hipError_t launch_scale_relayout(int fmt, const uint8_t* a_scales, int64_t M,
+                                 const uint8_t* w_scales, int64_t N, int64_t K, uint8_t* a_t,
+                                 uint8_t* w_t, hipStream_t s);
 hipError_t launch_gemm_w4a16_tiled(int fmt, const GemmParams& p, hipStream_t s, const char** name);
 hipError_t launch_gemm(int fmt, int akind, const GemmParams& p, hipStream_t s,
                        const char** name);

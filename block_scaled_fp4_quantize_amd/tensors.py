@@ -4,7 +4,7 @@ import torch
 
 from . import (FP4_MXFP4, FP4_NVFP4, FP4_OUT_BF16, FP4_OUT_F32, FP4_W4A4, FP4_W4A16,
                FP8_BLOCK, FP8_MX, FP8_ROWWISE, GROUP, _f8mode, _fmt, _mode,
-               fp4_gemm, fp4_gemm_workspace_size, fp4_moe_grouped_gemm, fp4_moe_topk_softmax,
+               fp4_gemm, fp4_gemm_workspace_size_mnk, fp4_moe_grouped_gemm, fp4_moe_topk_softmax,
                fp4_moe_workspace_layout, fp4_moe_workspace_size, fp4_quantize_act,
                fp4_quantize_weight, fp8_gemm, fp8_quantize_act, fp8_quantize_weight,
                make_moe_args, MX_BITS, _mxelem, mx_gemm, mx_quantize_act, mx_quantize_weight)
@@ -46,9 +46,11 @@ def gemm(fmt, mode, w_codes, w_scales, a_bf16=None, a_codes=None, a_scales=None,
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     od = FP4_OUT_F32 if out.dtype == torch.float32 else FP4_OUT_BF16
-    wsz = fp4_gemm_workspace_size(f, m, M, K, a_bf16 is not None)
+    wsz = fp4_gemm_workspace_size_mnk(f, m, M, N, K, a_bf16 is not None)
     if workspace is None and wsz:
         workspace = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    elif workspace is not None:
+        wsz = workspace.numel() * workspace.element_size()
     lda = a_bf16.stride(0) if a_bf16 is not None else 0
     st = fp4_gemm(f, m, M, N, K, a_bf16, lda, a_codes, a_scales, w_codes, w_scales,
                   float(weight_scale_2), float(input_scale), out, out.stride(0), od, flags,

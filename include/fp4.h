@@ -137,6 +137,17 @@ fp4_status fp4_gemm(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N, int64_t
 size_t fp4_gemm_workspace_size(fp4_format fmt, fp4_mode mode, int64_t M, int64_t K,
                                int has_a_bf16);
 
+/*
+ * Workspace bytes with which fp4_gemm runs a W4A4 call fastest: the above, plus, for
+ * prefill-sized problems (M > 64 and at least 256 output tiles of 256 x 256), room for
+ * both operands' block scales re-laid in the tile kernel's stage order (a small pass
+ * before the GEMM; the guide's §4.3 pre-converts scale factors to the MMA's layout).
+ * fp4_gemm uses that room when workspace_bytes reaches this size, else it reads the
+ * scales row by row: the results are bitwise the same either way.  0 for W4A16.
+ */
+size_t fp4_gemm_workspace_size_mnk(fp4_format fmt, fp4_mode mode, int64_t M, int64_t N,
+                                   int64_t K, int has_a_bf16);
+
 /* Capacity of fp4_gemm_noalloc's per-device scratch array (32 MiB). */
 #define FP4_NOALLOC_SCRATCH_BYTES (32u << 20)
 

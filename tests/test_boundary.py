@@ -145,6 +145,27 @@ def test_gemm_validation():
     assert g(NV, W44, a_bf16=A, ws=0x60000, wsb=need - 1) == F.FP4_ERR_WORKSPACE
 
 
+def test_gemm_workspace_size_mnk():
+    # the fused quantization's bytes, plus the stage-ordered block scales of both
+    # operands when the problem runs on the 256 x 256 tile (M > 64, >= 256 tiles)
+    NV, W44, W416 = F.FP4_NVFP4, F.FP4_W4A4, F.FP4_W4A16
+    assert F.fp4_gemm_workspace_size_mnk(NV, W44, 4, 256, 64, 1) == \
+        F.fp4_gemm_workspace_size(NV, W44, 4, 64, 1)
+    assert F.fp4_gemm_workspace_size_mnk(NV, W44, 4, 256, 64, 0) == 0
+    assert F.fp4_gemm_workspace_size_mnk(NV, W416, 8192, 4096, 4096, 1) == 0
+    for fmt, G in ((NV, 16), (F.FP4_MXFP4, 32)):
+        M, N, K = 8192, 4096, 4096
+        fused = F.fp4_gemm_workspace_size(fmt, W44, M, K, 1)
+        relayout = M * K // G + N * K // G
+        assert F.fp4_gemm_workspace_size_mnk(fmt, W44, M, N, K, 1) == fused + relayout
+        assert F.fp4_gemm_workspace_size_mnk(fmt, W44, M, N, K, 0) == relayout
+        # rows padded to whole 256-row tiles
+        assert F.fp4_gemm_workspace_size_mnk(fmt, W44, 8200, 4100, 1024, 0) == \
+            8448 * 1024 // G + 4352 * 1024 // G
+        # too few 256 x 256 tiles, or K not a multiple of 128: no relayout
+        assert F.fp4_gemm_workspace_size_mnk(fmt, W44, 1024, 1024, 1024, 0) == 0
+        assert F.fp4_gemm_workspace_size_mnk(fmt, W44, 8192, 4096, 4064, 0) == 0
+
 def test_topk_validation():
     t = lambda T, E, k: F.fp4_moe_topk_softmax(A, T, E, k, 1, B, C, check=False)
     assert t(4, 8, 0) == F.FP4_ERR_SHAPE

@@ -184,11 +184,10 @@ def test_raw_codes(fmt, shape):
                False, what=f"raw {fmt} M={M} N={N} K={K} ({F.fp4_last_kernel()})")
 
 
-# dense problems with at least 256 tiles of 256 x 256: the 8-wave 256-row tile, with K of
-# 1, 3, 5, 8 and 17 stages of 128 (the 256-row tile copies the block scales of 4 stages
-# at a time, so these cover a group cut short at 1, 3 and 1 stages, and whole ones),
-# ragged rows and columns; the oracle checks the first and last 300 rows and 200
-# sampled ones
+# dense problems with at least 256 tiles of 256 x 256: the 4-wave 256 x 256 tile, with K
+# of 1, 3, 5, 8 and 17 stages of 128 (fewer stages than its four stage buffers, and
+# more), ragged rows and columns; the oracle checks the first and last 300 rows and
+# 200 sampled ones
 TILED_256 = [(2300, 7324, 128), (2049, 7324, 384), (4096, 4096, 1024), (4096, 4096, 640),
              (4352, 4096, 2176)]
 
@@ -201,9 +200,36 @@ def test_tiled_256_shapes(fmt, shape):
     rows = np.unique(np.concatenate([np.arange(300), np.arange(M - 300, M),
                                      rng.choice(M, 200, replace=False)]))
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape), rows=rows)
-    assert F.fp4_last_kernel() == f"tile_{fmt}_m256"
+    assert F.fp4_last_kernel() == f"big_{fmt}_256"
     run_and_check(fmt, "w4a4", M, N, K, seed=sum(shape) + 1, out_dtype=torch.float32,
                   prequant=True, rows=rows)
+
+
+@pytest.mark.parametrize("shape", [(2300, 7324, 384), (4352, 4096, 2176)])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_big_tile_scale_paths_bitwise(fmt, shape):
+    # the 256 x 256 tile reads its block scales either from the stage-ordered copy that
+    # fp4_gemm writes into a large enough workspace, or row by row: same bits
+    M, N, K = shape
+    wc, ws, ws2, ad, av, s = problem(fmt, M, N, K, seed=M)
+    wcd, wsd = to_dev(wc), to_dev(ws)
+    ac, asc = T.quantize_act(fmt, ad, s)
+    need = F.fp4_gemm_workspace_size_mnk(fmt, "w4a4", M, N, K, 0)
+    assert need > 0
+    outs = []
+    for wsb in (torch.empty(need, dtype=torch.uint8, device=DEV),
+                torch.empty(16, dtype=torch.uint8, device=DEV)):
+        out, st = T.gemm(fmt, "w4a4", wcd, wsd, a_codes=ac, a_scales=asc, weight_scale_2=ws2,
+                         input_scale=s, out_dtype=torch.float32, workspace=wsb)
+        assert st == F.FP4_OK and F.fp4_last_kernel() == f"big_{fmt}_256"
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    # the fused path with its own workspace gives the same bits as well
+    out, st = T.gemm(fmt, "w4a4", wcd, wsd, a_bf16=ad, weight_scale_2=ws2, input_scale=s,
+                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert st == F.FP4_OK and torch.equal(out.view(torch.int32), outs[0].view(torch.int32))
 
 
 # at most 64 activation rows: the resident-activation kernel whenever the scale rows
