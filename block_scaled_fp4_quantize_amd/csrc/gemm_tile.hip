@@ -1005,30 +1005,45 @@ __global__ __launch_bounds__(256, 1) void big_gemm(GemmParams p) {
 // bytes [t SB + 4 pl, +4) of the row staged at position 64 rb + tile_srow(slot) --
 // rows in order for the activations, in the pair order within each 256-row tile for
 // the weights; rows past the end get zero words.
+// One workgroup per (64-row block of one side, 8 stages): the rows' scale bytes of
+// those stages are read whole into LDS (coalesced), then written out in stage order.
+constexpr int kRelayStages = 8;
 template <int FMT>
-__global__ void scale_relayout_kernel(const uint8_t* __restrict__ a_sc, int64_t M,
-                                      const uint8_t* __restrict__ w_sc, int64_t N, int64_t K,
-                                      uint8_t* __restrict__ a_t, uint8_t* __restrict__ w_t,
-                                      int64_t a_words, int64_t total_words) {
+__global__ __launch_bounds__(256) void scale_relayout_kernel(
+    const uint8_t* __restrict__ a_sc, int64_t M, const uint8_t* __restrict__ w_sc, int64_t N,
+    int64_t K, uint8_t* __restrict__ a_t, uint8_t* __restrict__ w_t, int64_t a_blocks) {
   using C = BigCfg<FMT>;
-  const int64_t e0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e0 >= total_words) return;
-  const bool wside = e0 >= a_words;
-  const int64_t e = wside ? e0 - a_words : e0;
+  constexpr int RB = kRelayStages * C::SB;   // bytes of a row in one workgroup's stages
+  __shared__ __attribute__((aligned(16))) uint8_t rows[64 * RB];
   const int64_t nst = K / kTBK, KS = K / C::G;
-  const int slot = (int)(e & 63);
-  int64_t rest = e >> 6;
-  const int pl = (int)(rest % C::PLANES);
-  rest /= C::PLANES;
-  const int64_t t = rest % nst;
-  const int64_t rb = rest / nst;
-  const int64_t srow = rb * 64 + tile_srow(slot);   // staged row of this side
-  int64_t row = srow;
-  if (wside) row = (srow & ~(int64_t)255) + big_wperm<FMT>((int)(srow & 255));
+  const int64_t nchunk = (nst + kRelayStages - 1) / kRelayStages;
+  const int64_t blk = (int64_t)blockIdx.x / nchunk;
+  const int64_t t0 = ((int64_t)blockIdx.x - blk * nchunk) * kRelayStages;
+  const int nt_ = (int)(nst - t0 < kRelayStages ? nst - t0 : kRelayStages);   // stages here
+  const bool wside = blk >= a_blocks;
+  const int64_t rb = wside ? blk - a_blocks : blk;
   const int64_t R = wside ? N : M;
   const uint8_t* sc = wside ? w_sc : a_sc;
-  const uint32_t v = row < R ? *reinterpret_cast<const uint32_t*>(sc + row * KS + t * C::SB + 4 * pl) : 0u;
-  reinterpret_cast<uint32_t*>(wside ? w_t : a_t)[e] = v;
+  uint8_t* out = wside ? w_t : a_t;
+  // load: words, row-major over the 64 staged rows of the block (a row's bytes of these
+  // stages are contiguous)
+  const int rwords = nt_ * C::SB / 4;
+  for (int q = threadIdx.x; q < 64 * rwords; q += 256) {
+    const int i = q / rwords, w = q - i * rwords;
+    const int64_t sr = rb * 64 + i;   // staged row
+    const int64_t row = wside ? (sr & ~(int64_t)255) + big_wperm<FMT>((int)(sr & 255)) : sr;
+    const uint32_t v = row < R ? reinterpret_cast<const uint32_t*>(sc + row * KS + t0 * C::SB)[w] : 0u;
+    reinterpret_cast<uint32_t*>(rows + i * RB)[w] = v;
+  }
+  __syncthreads();
+  // write: word slot of stage t0 + tt, plane pl holds the bytes [tt SB + 4 pl, +4) of
+  // the row staged at tile_srow(slot)
+  const int words = nt_ * C::PLANES * 64;
+  for (int e = threadIdx.x; e < words; e += 256) {
+    const int slot = e & 63, pl = (e >> 6) % C::PLANES, tt = (e >> 6) / C::PLANES;
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(rows + tile_srow(slot) * RB + tt * C::SB + 4 * pl);
+    reinterpret_cast<uint32_t*>(out)[((rb * nst + t0 + tt) * C::PLANES + pl) * 64 + slot] = v;
+  }
 }
 
 template <int FMT>
@@ -1050,13 +1065,12 @@ hipError_t launch_big(const GemmParams& p, hipStream_t s, const char** name) {
 template <int FMT>
 hipError_t launch_relayout(const uint8_t* a_sc, int64_t M, const uint8_t* w_sc, int64_t N,
                            int64_t K, uint8_t* a_t, uint8_t* w_t, hipStream_t s) {
-  using C = BigCfg<FMT>;
-  const int64_t a_words = (M + 255) / 256 * 256 * (K / C::G) / 4;
-  const int64_t total = a_words + (N + 255) / 256 * 256 * (K / C::G) / 4;
-  const int64_t grid = (total + 255) / 256;
+  const int64_t a_blocks = (M + 255) / 256 * 4, w_blocks = (N + 255) / 256 * 4;
+  const int64_t nchunk = (K / kTBK + kRelayStages - 1) / kRelayStages;
+  const int64_t grid = (a_blocks + w_blocks) * nchunk;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((scale_relayout_kernel<FMT>), dim3((unsigned)grid), dim3(256), 0, s, a_sc, M,
-                     w_sc, N, K, a_t, w_t, a_words, total);
+                     w_sc, N, K, a_t, w_t, a_blocks);
   return hipGetLastError();
 }
 
