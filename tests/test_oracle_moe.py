@@ -280,3 +280,28 @@ def test_golden_requant_through_down_projection(name):
     assert list(q[0]) == list(codes) and list(s[0]) == list(sc)
     y = Mo.expert_down(fmt, Gm.W4A4, h.reshape(1, -1), ex)[0]
     assert np.array_equal(y, a2 * deq)
+
+
+def test_requant_input_is_fp32():
+    # The intermediate h is an fp32 value when it is requantized ("vLLM on the NVIDIA DGX
+    # Spark (GB10 / sm_121): A Complete Technical Guide", §4.3: SwiGLU between the GEMMs,
+    # quantized inside the kernel).  h = 2.5 + 1e-9 rounds to 2.5 in fp32, the midpoint of
+    # the e2m1 values 2 and 3, which ties to the even code (2.0); quantized in float64 it
+    # would round up to 3.0.  MXFP4 block with amax 4: scale exponent floor(log2 4) - 2 = 0.
+    h = np.zeros((1, 32), np.float64)
+    h[0, 0] = 4.0
+    h[0, 1] = 2.5 + 1e-9
+    codes, scales = Q.quantize(Q.MXFP4, h)
+    assert scales[0, 0] == 127
+    d = Q.dequantize(Q.MXFP4, codes, scales)
+    assert d[0, 1] == 2.0 and d[0, 0] == 4.0
+    # the down projection sees the same: identity-like weights pick h's second element
+    I, H = 32, 32
+    w2 = np.zeros((H, I), np.float32)
+    w2[0, 1] = 1.0
+    w2c, w2s, _ = Q.quantize_weight(Q.MXFP4, w2)
+    w13 = np.zeros((2 * I, H), np.float32)
+    w13c, w13s, _ = Q.quantize_weight(Q.MXFP4, w13)
+    ex = Mo.Expert(w13c, w13s, w2c, w2s)
+    y = Mo.expert_down(Q.MXFP4, Gm.W4A4, h, ex)
+    assert y[0, 0] == 2.0
