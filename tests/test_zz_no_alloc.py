@@ -47,6 +47,19 @@ def test_noalloc_equals_fp4_gemm_two_calls(fmt):
         assert not torch.isnan(got).any()
 
 
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_noalloc_big_tile_relayout_two_calls(fmt):
+    # dense shapes on the 4-wave 256 x 256 tile: fp4_gemm with the plain fused workspace
+    # reads the block scales row by row, fp4_gemm_noalloc first re-lays them in stage
+    # order into the scratch array (after the quantized activations); same bits.  The
+    # second call is smaller than the first.
+    for M, N, K in ((2300, 7324, 384), (2049, 7324, 128)):
+        ref, got = _pair(fmt, M, N, K, seed=M + N + 1, out_dtype=torch.float32)
+        assert F.fp4_last_kernel() == f"big_{fmt}_256"
+        assert torch.equal(ref.view(torch.int32), got.view(torch.int32)), f"{fmt} M={M} N={N} K={K}"
+        assert not torch.isnan(got).any()
+
 def test_noalloc_prequantized_and_weight_only_need_no_scratch():
     fmt, M, N, K = "nvfp4", 12, 128, 512
     wc, ws, ws2 = weights(fmt, N, K, 5)
