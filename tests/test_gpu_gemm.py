@@ -232,6 +232,33 @@ def test_big_tile_scale_paths_bitwise(fmt, shape):
     assert st == F.FP4_OK and torch.equal(out.view(torch.int32), outs[0].view(torch.int32))
 
 
+
+@pytest.mark.parametrize("pad", [8, 3])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_big_tile_strided_output(fmt, pad):
+    # the 256 x 256 tile into a bf16 output with row stride N + pad: 16-byte stores when
+    # the stride keeps rows aligned (pad 8; N % 8 == 4 leaves a partial piece at the
+    # end of each row), element stores otherwise (pad 3); the columns past N keep their
+    # canary and the first N equal the contiguous output bit for bit
+    M, N, K = 2300, 7324, 384
+    wc, ws, ws2, ad, av, s = problem(fmt, M, N, K, seed=N + pad)
+    wcd, wsd = to_dev(wc), to_dev(ws)
+    ac, asc = T.quantize_act(fmt, ad, s)
+    ref, st = T.gemm(fmt, "w4a4", wcd, wsd, a_codes=ac, a_scales=asc, weight_scale_2=ws2,
+                     input_scale=s, out_dtype=torch.bfloat16)
+    assert st == F.FP4_OK
+    ldo = N + pad
+    canary = torch.tensor(-7.25, dtype=torch.bfloat16)
+    out = torch.full((M, ldo), float(canary), dtype=torch.bfloat16, device=DEV)
+    need = F.fp4_gemm_workspace_size_mnk(fmt, "w4a4", M, N, K, 0)
+    wsb = torch.empty(need, dtype=torch.uint8, device=DEV)
+    st = F.fp4_gemm(fmt, "w4a4", M, N, K, None, K, ac, asc, wcd, wsd, ws2, s, out, ldo,
+                    F.FP4_OUT_BF16, 0, wsb, need)
+    assert st == F.FP4_OK and F.fp4_last_kernel() == f"big_{fmt}_256"
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :N].view(torch.int16), ref.view(torch.int16))
+    assert bool((out[:, N:] == canary).all())
+
 # at most 64 activation rows: the resident-activation kernel whenever the scale rows
 # are whole 16-byte pieces and the activations fit in LDS (ring of 8, 16 or 32 K
 # steps; K = 6144 refills the ring once), otherwise the streaming kernel.  The 4 waves
