@@ -4,11 +4,11 @@
 // weighted reduction; here the work splits at the one point where every gate/up result
 // must be complete before any down projection starts).
 //
-//  1. moe_small_gateup_nv: workgroup (slot s, 32 intermediate columns).  Every
+//  1. moe_small_gateup_nv: workgroup (slot s, 16 intermediate columns).  Every
 //     workgroup routes the few slots itself (a stable counting sort by expert, the
 //     general dispatch's order), quantizes its token's hidden row under its expert's
-//     input scale into LDS (the quantization pass's arithmetic), streams the 32 gate and
-//     32 up weight rows of that expert with all of their K-steps in flight, and applies
+//     input scale into LDS (the quantization pass's arithmetic), streams the 16 gate and
+//     16 up weight rows of that expert with all of their K-steps in flight, and applies
 //     SwiGLU + requant to the one output row.  The workgroups of the first column tile
 //     also write the dispatch bookkeeping and the quantized GEMM1 input.
 //  2. moe_small_down_nv: workgroup (8 output columns), 8 waves taking the slots in
@@ -63,32 +63,33 @@ __device__ __forceinline__ float max16(float v) {
   return fmaxf(v, dpp_f<0x140>(v));   // row_mirror
 }
 
-// Gate/up: 8 waves, wave w takes weight rows of group w & 3 (gate columns nt*32 +
-// [0, 32) for groups 0-1, the matching up rows for 2-3) over K half w >> 2; K-steps of
-// 128 elements, at most SMAX per wave, all of a lane's 16-byte weight pieces in flight.
-// Every wave quantizes its own K half of the hidden row into its own LDS slice (four
-// waves share a half: the work is repeated, a workgroup barrier is not needed), so its
-// MFMA loop starts as soon as its piece of the row has arrived and decodes the weight
-// steps in the order they land.
+// Gate/up: 8 waves, wave w takes the 16 gate rows (w even) or the matching 16 up rows
+// (w odd) of columns nt*16 + [0, 16) over K quarter w >> 1; K-steps of 128 elements, at
+// most SMAX per wave, all of a lane's 16-byte weight pieces in flight.  16 columns per
+// workgroup give 2 x 8 x I / 16 workgroups for 8 slots (384 at I = 768), enough to
+// keep every CU streaming.  Every wave quantizes its own K quarter of the hidden row
+// into its own LDS slice (two waves share a quarter: the work is repeated, a workgroup
+// barrier is not needed), so its MFMA loop starts as soon as its piece of the row has
+// arrived and decodes the weight steps in the order they land.
 template <int SMAX>
 __global__ __launch_bounds__(512) void moe_small_gateup_nv(MoeSmallParams p, SmallPack pk) {
   constexpr int XR = (SMAX * 16 + 63) / 64;   // 8-element row chunks per lane
   // each wave's K half of the quantized row, decoded exactly to fp16 (its MFMA operand)
   __shared__ __attribute__((aligned(16))) _Float16 xw[8][SMAX * 128];
-  __shared__ float kp[2][4][16];   // [K half][row group][column]: the partial dot products
+  __shared__ float kp[4][2][16];   // [K quarter][gate, up][column]: the partial dot products
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = (int)(p.T * p.k);
   const int64_t H = p.H, I = p.I, E = p.E;
-  const int ntiles = (int)(I / 32);
+  const int ntiles = (int)(I / 16);
   const int s = (int)(blockIdx.x / ntiles);
   const int nt = (int)(blockIdx.x - (int64_t)s * ntiles);
   const int64_t t = s / p.k;
   const int r = lane & 15, gq = lane >> 4;
-  const int rg = wave & 3, kh = wave >> 2;
+  const int rg = wave & 1, kq = wave >> 1;   // gate (0) or up (1) rows; K quarter
   const int S = (int)(H / 128);
-  const int s0 = kh * (S / 2), s1 = kh ? S : S / 2;   // this wave's K-steps [s0, s1)
+  const int s0 = kq * S / 4, s1 = (kq + 1) * S / 4;   // this wave's K-steps [s0, s1)
   const int nq = (s1 - s0) * 16;                        // its row chunks
   // loads first, in the order they are needed: the wave's piece of the token's hidden
   // row (known from the block index), all slots' ids, this slot's expert id, that
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(512) void moe_small_gateup_nv(MoeSmallParams p, Sma
   const int ej_raw = small_ids_load(p, n, lane);
   int e = p.ids[s];
   e = (e >= 0 && e < E) ? e : -1;
-  const int64_t wn = rg < 2 ? nt * 32 + rg * 16 + r : I + nt * 32 + (rg - 2) * 16 + r;
+  const int64_t wn = rg == 0 ? nt * 16 + r : I + nt * 16 + r;
   const int ec = e >= 0 ? e : 0;   // a dropped slot's workgroup loads expert 0 and exits
   const uint8_t* wrow = p.w13_codes + ec * (2 * I) * (H / 2) + wn * (H / 2) + gq * 16;
   const uint8_t* wsrow = p.w13_scales + ec * (2 * I) * (H / 16) + wn * (H / 16) + 2 * gq;
@@ -204,25 +205,25 @@ __global__ __launch_bounds__(512) void moe_small_gateup_nv(MoeSmallParams p, Sma
   // lane (row r, gq) holds columns 4 gq .. + 3 of the group's 16 (every r alike)
   if (r == 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) kp[kh][rg][4 * gq + v] = sum[v];
+    for (int v = 0; v < 4; ++v) kp[kq][rg][4 * gq + v] = sum[v];
   }
   __syncthreads();
-  // SwiGLU + requant under g2, the arithmetic of the SwiGLU epilogues: lane c < 32 of
-  // wave 0 takes h column nt * 32 + c; a 16-column block is a row of 16 lanes, a code
+  // SwiGLU + requant under g2, the arithmetic of the SwiGLU epilogues: lane c < 16 of
+  // wave 0 takes h column nt * 16 + c; the 16-column block is a row of 16 lanes, a code
   // byte a lane pair
   if (wave == 0) {
-    const int c = lane & 15, b = (lane >> 4) & 1;
-    const float g = (kp[0][b][c] + kp[1][b][c]) * alpha13;
-    const float u = (kp[0][2 + b][c] + kp[1][2 + b][c]) * alpha13;
+    const int c = lane & 15;
+    const float g = ((kp[0][0][c] + kp[1][0][c]) + (kp[2][0][c] + kp[3][0][c])) * alpha13;
+    const float u = ((kp[0][1][c] + kp[1][1][c]) + (kp[2][1][c] + kp[3][1][c])) * alpha13;
     const float h = swiglu1(g, u);
     const float amax = max16(fabsf(h));
     float rq;
     const uint32_t sc = q_nv_scale(amax, g2, &rq);
     const float h1 = lane_xor1(h);
-    if (lane < 32) {
+    if (lane < 16) {
       if ((lane & 1) == 0)
-        p.h_codes[(int64_t)pos * (I / 2) + nt * 16 + lane / 2] = (uint8_t)q_nv_pack2(h, h1, rq);
-      if (c == 0) p.h_scales[(int64_t)pos * (I / 16) + nt * 2 + b] = (uint8_t)sc;
+        p.h_codes[(int64_t)pos * (I / 2) + nt * 8 + lane / 2] = (uint8_t)q_nv_pack2(h, h1, rq);
+      if (c == 0) p.h_scales[(int64_t)pos * (I / 16) + nt] = (uint8_t)sc;
     }
   }
 }
@@ -367,10 +368,10 @@ hipError_t launch_moe_small(const MoeSmallParams& p, const float* scal_host, hip
   for (int i = 0; i < kSmallPack; ++i) pk.v[i] = i < 4 * p.E ? scal_host[i] : 0.0f;
   const int64_t n = p.T * p.k;
   *name = "moe_small_gateup_nvfp4";
-  // K-steps per wave, the smallest instance that covers them: half of H / 128 for
-  // gate/up, I / 128 for down (steps past them are masked, not skipped)
-  const dim3 g1((unsigned)(n * (p.I / 32)));
-  const int64_t s1 = p.H / 256 + (p.H % 256 ? 1 : 0);
+  // K-steps per wave, the smallest instance that covers them: a quarter of H / 128
+  // (rounded up) for gate/up, I / 128 for down (steps past them are masked, not skipped)
+  const dim3 g1((unsigned)(n * (p.I / 16)));
+  const int64_t s1 = (p.H / 128 + 3) / 4;
   if (s1 <= 4)
     hipLaunchKernelGGL(moe_small_gateup_nv<4>, g1, dim3(512), 0, s, p, pk);
   else if (s1 <= 8)
